@@ -1,0 +1,227 @@
+"""Planted mistakes in the oracle must each break at least one pin.
+
+Every mutant replaces one step function of the oracle (on the CPU, for the
+duration of one test) with a plausible bug: a dropped term, a wrong sign, a
+wrong index or a transposed operand.  If the pin suite still passed, that
+step would be unpinned.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.decode_ref as ref
+from oracle_pins import ALL_PINS
+
+
+def _scores_noscale(q, keys, scale):
+    return keys @ q
+
+
+def _scores_negated(q, keys, scale):
+    return -scale * (keys @ q)
+
+
+def _attend_nomax(q, keys, values, scale):
+    n = keys.shape[0]
+    if n == 0:
+        return np.zeros(values.shape[1]), -np.inf
+    s = ref.scores(q, keys, scale)
+    p = np.exp(s)
+    return (p @ values) / np.sum(p), np.log(np.sum(p))
+
+
+def _attend_log2(q, keys, values, scale):
+    n = keys.shape[0]
+    if n == 0:
+        return np.zeros(values.shape[1]), -np.inf
+    s = ref.scores(q, keys, scale)
+    m = np.max(s)
+    p = np.exp(s - m)
+    return (p @ values) / np.sum(p), m + np.log2(np.sum(p))
+
+
+def _attend_lse_nom(q, keys, values, scale):
+    n = keys.shape[0]
+    if n == 0:
+        return np.zeros(values.shape[1]), -np.inf
+    s = ref.scores(q, keys, scale)
+    m = np.max(s)
+    p = np.exp(s - m)
+    return (p @ values) / np.sum(p), np.log(np.sum(p))
+
+
+def _attend_mean_norm(q, keys, values, scale):
+    n = keys.shape[0]
+    if n == 0:
+        return np.zeros(values.shape[1]), -np.inf
+    s = ref.scores(q, keys, scale)
+    m = np.max(s)
+    p = np.exp(s - m)
+    return (p @ values) / n, m + np.log(np.sum(p))
+
+
+def _attend_drop_last(q, keys, values, scale):
+    return ref.__dict__["_orig_attend"](q, keys[:-1], values[:-1], scale) if keys.shape[0] > 1 \
+        else ref.__dict__["_orig_attend"](q, keys, values, scale)
+
+
+def _token_locations_swapped(bt_row, ctx, bs):
+    i = np.arange(ctx, dtype=np.int64)
+    return np.asarray(bt_row, dtype=np.int64)[i % bs], i // bs
+
+
+def _token_locations_reversed_slot(bt_row, ctx, bs):
+    i = np.arange(ctx, dtype=np.int64)
+    return np.asarray(bt_row, dtype=np.int64)[i // bs], (bs - 1 - i % bs)
+
+
+def _token_locations_off_by_one(bt_row, ctx, bs):
+    i = np.arange(1, ctx + 1, dtype=np.int64) if ctx else np.arange(0, dtype=np.int64)
+    i = np.minimum(i, len(bt_row) * bs - 1)
+    return np.asarray(bt_row, dtype=np.int64)[i // bs], i % bs
+
+
+def _gather_kv_vtrans(k_pool, v_pool, pages, slots):
+    k = k_pool[pages, :, slots, :]
+    bs = v_pool.shape[3]
+    dv = v_pool.shape[2]
+    # reads V as if stored [bs][Dv] inside the (page, head) tile
+    flat = v_pool.reshape(v_pool.shape[0], v_pool.shape[1], -1)
+    idx = slots[:, None] * dv + np.arange(dv)[None, :]
+    v = np.stack([flat[p, :, ix] for p, ix in zip(pages, idx)]) if len(pages) else \
+        np.zeros((0, v_pool.shape[1], dv))
+    return k, v
+
+
+def _gather_kv_khead_swapped(k_pool, v_pool, pages, slots):
+    k, v = ref.__dict__["_orig_gather_kv"](k_pool, v_pool, pages, slots)
+    return k[:, ::-1, :], v
+
+
+def _kv_head_mod(h, hq, hkv):
+    return h % hkv
+
+
+def _latent_kv_tail(c, dv):
+    return c, c[:, c.shape[1] - dv:]
+
+
+def _latent_kv_truncated_keys(c, dv):
+    return c[:, :dv], c[:, :dv]
+
+
+def _bf16_shift15(bits):
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)
+    return u.view(np.float32).astype(np.float64)
+
+
+def _bf16_as_fp16(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def _merge_unnormalised(o_parts, lse_parts):
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    big = np.max(lse_parts)
+    if not np.isfinite(big):
+        return np.zeros(o_parts.shape[1]), -np.inf
+    w = np.exp(lse_parts - big)
+    return w @ o_parts, big + np.log(np.sum(w))
+
+
+def _merge_plain_mean(o_parts, lse_parts):
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    keep = np.isfinite(lse_parts)
+    if not keep.any():
+        return np.zeros(o_parts.shape[1]), -np.inf
+    big = np.max(lse_parts)
+    return o_parts[keep].mean(axis=0), big + np.log(np.sum(np.exp(lse_parts - big)))
+
+
+def _chunk_alpha_flipped(q, keys, values, scale, bs, tok0):
+    n = keys.shape[0]
+    if n == 0:
+        return np.zeros(values.shape[1]), -np.inf
+    m, l, acc, start = -np.inf, 0.0, np.zeros(values.shape[1]), 0
+    while start < n:
+        end = min(n, start + bs - ((tok0 + start) % bs))
+        s = ref.scores(q, keys[start:end], scale)
+        m_new = max(m, float(np.max(s)))
+        alpha = np.exp(m_new - m) if np.isfinite(m) else 0.0
+        p = np.exp(s - m_new)
+        l = alpha * l + np.sum(p)
+        acc = alpha * acc + p @ values[start:end]
+        m, start = m_new, end
+    return acc / l, m + np.log(l)
+
+
+def _chunk_l_not_rescaled(q, keys, values, scale, bs, tok0):
+    n = keys.shape[0]
+    if n == 0:
+        return np.zeros(values.shape[1]), -np.inf
+    m, l, acc, start = -np.inf, 0.0, np.zeros(values.shape[1]), 0
+    while start < n:
+        end = min(n, start + bs - ((tok0 + start) % bs))
+        s = ref.scores(q, keys[start:end], scale)
+        m_new = max(m, float(np.max(s)))
+        alpha = np.exp(m - m_new) if np.isfinite(m) else 0.0
+        p = np.exp(s - m_new)
+        l = l + np.sum(p)
+        acc = alpha * acc + p @ values[start:end]
+        m, start = m_new, end
+    return acc / l, m + np.log(l)
+
+
+def _split_ranges_overlap(num_pages, c, ns):
+    return [(min(num_pages, max(0, s * c - 1)), min(num_pages, (s + 1) * c)) for s in range(ns)]
+
+
+def _split_ranges_gap(num_pages, c, ns):
+    return [(min(num_pages, s * c + (1 if s else 0)), min(num_pages, (s + 1) * c)) for s in range(ns)]
+
+
+MUTANTS = {
+    "scores_noscale": ("scores", _scores_noscale),
+    "scores_negated": ("scores", _scores_negated),
+    "attend_nomax": ("attend", _attend_nomax),
+    "attend_log2": ("attend", _attend_log2),
+    "attend_lse_without_max": ("attend", _attend_lse_nom),
+    "attend_divide_by_count": ("attend", _attend_mean_norm),
+    "attend_drops_last_token": ("attend", _attend_drop_last),
+    "token_page_slot_swapped": ("token_locations", _token_locations_swapped),
+    "token_slot_reversed": ("token_locations", _token_locations_reversed_slot),
+    "token_off_by_one": ("token_locations", _token_locations_off_by_one),
+    "v_read_transposed": ("gather_kv", _gather_kv_vtrans),
+    "k_heads_reversed": ("gather_kv", _gather_kv_khead_swapped),
+    "gqa_head_modulo": ("kv_head_of", _kv_head_mod),
+    "mla_values_from_tail": ("latent_kv", _latent_kv_tail),
+    "mla_keys_truncated": ("latent_kv", _latent_kv_truncated_keys),
+    "bf16_shift_15": ("bf16_bits_to_f64", _bf16_shift15),
+    "bf16_read_as_fp16": ("bf16_bits_to_f64", _bf16_as_fp16),
+    "merge_unnormalised": ("merge_partials", _merge_unnormalised),
+    "merge_plain_mean": ("merge_partials", _merge_plain_mean),
+    "chunk_alpha_flipped": ("chunk_partial", _chunk_alpha_flipped),
+    "chunk_l_not_rescaled": ("chunk_partial", _chunk_l_not_rescaled),
+    "split_ranges_overlap": ("split_page_ranges", _split_ranges_overlap),
+    "split_ranges_gap": ("split_page_ranges", _split_ranges_gap),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setitem(ref.__dict__, "_orig_attend", ref.attend)
+    monkeypatch.setitem(ref.__dict__, "_orig_gather_kv", ref.gather_kv)
+    monkeypatch.setattr(ref, attr, fn)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(ref)
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"mutant {name} passed every pin"

@@ -1,0 +1,291 @@
+"""Seeded synthetic inputs for paged decode attention.
+
+This module only draws and lays out inputs: context lengths, page
+assignments, the query and the paged key/value (or latent) cache.  It holds
+none of the attention arithmetic, so that the CPU oracle and the HIP path can
+both be fed from it without sharing any of the method.
+
+Every value is drawn as float32 N(0, 1) and, for bf16 workloads, rounded to
+bfloat16 with round-to-nearest-even; bf16 arrays are carried as their uint16
+bit patterns.  Draws come in fixed chunks of ``CHUNK`` values, chunk ``i``
+from the ``i``-th child of ``numpy.random.SeedSequence(seed)``; the result is
+therefore independent of how many threads fill it.
+
+Pool layouts (physical page ``p``):
+
+* MHA/GQA key pool    ``k[num_blocks][Hkv][block_size][D]``
+* MHA/GQA value pool  ``v[num_blocks][Hkv][D][block_size]``
+* MLA latent pool     ``c[num_blocks][block_size][Dqk]`` (V = first Dv dims)
+
+Only the pages a workload uses are materialised on the host ("compact"
+arrays, row ``i`` holding physical page ``page_ids[i]``); a device pool of
+``num_blocks`` pages is filled from them by scattering rows to ``page_ids``.
+"""
+
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+CHUNK = 1 << 22
+BF16_NAN_BITS = 0x7FC0
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); return uint16 bits.
+
+    Inputs are finite draws, so the NaN/overflow corners of the rounding are
+    not needed here.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+class _Draw:
+    """Chunked, thread-count independent N(0,1) stream for one tensor."""
+
+    def __init__(self, seed_seq: np.random.SeedSequence):
+        self.seq = seed_seq
+
+    def normal(self, n: int, dtype: str) -> np.ndarray:
+        """n values in the workload dtype (float32, or bf16 bits as uint16)."""
+        nchunks = max(1, (n + CHUNK - 1) // CHUNK)
+        children = self.seq.spawn(nchunks)
+        out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
+
+        def fill(i: int) -> None:
+            lo, hi = i * CHUNK, min(n, (i + 1) * CHUNK)
+            if hi <= lo:
+                return
+            vals = np.random.default_rng(children[i]).standard_normal(hi - lo, dtype=np.float32)
+            out[lo:hi] = vals if dtype == "f32" else f32_to_bf16_bits(vals)
+
+        if nchunks == 1:
+            fill(0)
+        else:
+            with ThreadPoolExecutor(_threads()) as ex:
+                list(ex.map(fill, range(nchunks)))
+        return out
+
+
+@dataclass
+class PagedDecodeInputs:
+    """One decode step's inputs, with the KV pages held compactly on the host."""
+
+    name: str
+    kind: str                 # "mha" (MHA/GQA) or "mla"
+    dtype: str                # "f32" or "bf16"
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int         # 1 for MLA
+    head_dim: int             # Dqk
+    head_dim_v: int           # Dv
+    block_size: int
+    num_blocks: int           # physical pages in the device pool
+    scale: float
+    context_lens: np.ndarray  # int32 [B]
+    block_table: np.ndarray   # int32 [B][max_blocks_per_seq], physical ids
+    page_ids: np.ndarray      # int32 [n_used]: physical id of compact row i
+    q: np.ndarray             # [B][Hq][Dqk] float32 or uint16 bf16 bits
+    k_pages: np.ndarray | None = None   # [n_used][Hkv][bs][D]
+    v_pages: np.ndarray | None = None   # [n_used][Hkv][D][bs]
+    c_pages: np.ndarray | None = None   # [n_used][bs][Dqk] (MLA latent)
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.batch else 0
+
+    @property
+    def esize(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def compact_block_table(self) -> np.ndarray:
+        """The block table with physical ids replaced by compact row indices.
+
+        Entries that point at no used page become -1.
+        """
+        lut = np.full(self.num_blocks, -1, dtype=np.int64)
+        lut[self.page_ids] = np.arange(len(self.page_ids))
+        bt = self.block_table.astype(np.int64)
+        out = np.where(bt >= 0, lut[np.clip(bt, 0, self.num_blocks - 1)], -1)
+        return out.astype(np.int32)
+
+    def kv_bytes_read(self) -> int:
+        """Bytes of K and V the step must read: every context token's rows."""
+        toks = int(self.context_lens.astype(np.int64).sum())
+        if self.kind == "mla":
+            return toks * self.head_dim * self.esize
+        return toks * self.num_kv_heads * (self.head_dim + self.head_dim_v) * self.esize
+
+
+def _assign_pages(rng: np.random.Generator, n_pages: np.ndarray, num_blocks: int,
+                  max_blocks: int) -> tuple[np.ndarray, np.ndarray]:
+    """Give each sequence its pages from a seeded permutation of the pool.
+
+    Returns (block_table [B][max_blocks] with -1 padding, page_ids in logical
+    order: sequence-major, then logical page).
+    """
+    total = int(n_pages.sum())
+    if total > num_blocks:
+        raise ValueError(f"pool of {num_blocks} pages cannot hold {total}")
+    perm = rng.permutation(num_blocks)[:total].astype(np.int32)
+    bt = np.full((len(n_pages), max_blocks), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(n_pages.tolist()):
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    return bt, perm
+
+
+def make_paged_inputs(*, name: str = "custom", kind: str = "mha", dtype: str = "bf16",
+                      batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                      head_dim_v: int | None = None, block_size: int,
+                      context_lens, num_blocks: int | None = None,
+                      max_blocks_per_seq: int | None = None, scale: float | None = None,
+                      seed: int = 0, poison: bool = True, values: bool = True,
+                      meta: dict | None = None) -> PagedDecodeInputs:
+    """Draw a paged decode workload.
+
+    ``context_lens`` is an int sequence (or a callable ``rng -> array`` drawn
+    first from the workload's generator).  Pages are assigned from a seeded
+    permutation of a pool of ``num_blocks`` pages.  With ``poison`` the slots
+    past each context's end in its last page are NaN; the device pool's
+    unassigned pages are to be NaN-filled by the caller as well.  With
+    ``values=False`` only the shapes, lengths and tables are drawn.
+    """
+    if kind not in ("mha", "mla"):
+        raise ValueError(kind)
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(dtype)
+    if kind == "mla":
+        num_kv_heads = 1
+    head_dim_v = head_dim if head_dim_v is None else head_dim_v
+    root = np.random.SeedSequence(seed)
+    ctl_seq, page_seq, q_seq, k_seq, v_seq = root.spawn(5)
+    rng_ctx = np.random.default_rng(ctl_seq)
+    if callable(context_lens):
+        ctx = np.asarray(context_lens(rng_ctx), dtype=np.int64)
+    else:
+        ctx = np.asarray(context_lens, dtype=np.int64)
+    ctx = ctx.reshape(batch).astype(np.int32)
+    n_pages = (ctx.astype(np.int64) + block_size - 1) // block_size
+    need = int(n_pages.max()) if batch else 0
+    max_blocks = max(1, need) if max_blocks_per_seq is None else max_blocks_per_seq
+    if max_blocks < need:
+        raise ValueError("max_blocks_per_seq too small for the context lengths")
+    total = int(n_pages.sum())
+    nb = max(1, total) if num_blocks is None else num_blocks
+    bt, page_ids = _assign_pages(np.random.default_rng(page_seq), n_pages, nb, max_blocks)
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+
+    dq = head_dim
+    q = _Draw(q_seq).normal(batch * num_q_heads * dq, dtype).reshape(batch, num_q_heads, dq)
+    inp = PagedDecodeInputs(name=name, kind=kind, dtype=dtype, batch=batch,
+                            num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                            head_dim=head_dim, head_dim_v=head_dim_v, block_size=block_size,
+                            num_blocks=nb, scale=float(scale), context_lens=ctx,
+                            block_table=bt, page_ids=page_ids, q=q, meta=dict(meta or {}))
+    if not values:
+        return inp
+
+    nan = np.float32("nan") if dtype == "f32" else np.uint16(BF16_NAN_BITS)
+    # Tail mask in logical order: [n_used][bs], True where the slot is past ctx.
+    tail = np.zeros((total, block_size), dtype=bool)
+    off = 0
+    for b in range(batch):
+        n = int(n_pages[b])
+        if n:
+            used = int(ctx[b]) - (n - 1) * block_size
+            tail[off + n - 1, used:] = True
+        off += n
+
+    if kind == "mla":
+        c = _Draw(k_seq).normal(total * block_size * dq, dtype).reshape(total, block_size, dq)
+        if poison:
+            c[tail] = nan
+        inp.c_pages = c
+        return inp
+
+    hkv, dv = num_kv_heads, head_dim_v
+    # Drawn token-major ([page][slot][head][dim], logical order), then laid out.
+    k = _Draw(k_seq).normal(total * block_size * hkv * dq, dtype).reshape(total, block_size, hkv, dq)
+    if poison:
+        k[tail] = nan
+    inp.k_pages = np.ascontiguousarray(k.transpose(0, 2, 1, 3))   # [n][Hkv][bs][D]
+    del k
+    v = _Draw(v_seq).normal(total * block_size * hkv * dv, dtype).reshape(total, block_size, hkv, dv)
+    if poison:
+        v[tail] = nan
+    inp.v_pages = np.ascontiguousarray(v.transpose(0, 2, 3, 1))   # [n][Hkv][Dv][bs]
+    return inp
+
+
+# ---------------------------------------------------------------------------
+# The five benchmark workloads (shapes, dtypes, length mixes and pools).
+# ---------------------------------------------------------------------------
+
+def _uniform_ctx(lo, hi, n):
+    return lambda rng: rng.integers(lo, hi, n, endpoint=True)
+
+
+def _loguniform_ctx(lo, hi, n):
+    return lambda rng: np.rint(np.exp(rng.uniform(math.log(lo), math.log(hi), n)))
+
+
+CONFIGS = {
+    "tiny_mha_f32": dict(
+        kind="mha", dtype="f32", batch=1, num_q_heads=8, num_kv_heads=8, head_dim=64,
+        block_size=16, context_lens=[512], num_blocks=32, scale=1.0 / 8.0, seed=1,
+        meta=dict(num_splits=[1, 4],
+                  desc="tiny MHA fp32: B1, 8 heads, D64, ctx 512, bs16, 32 permuted pages")),
+    "llama_mha_bf16": dict(
+        kind="mha", dtype="bf16", batch=16, num_q_heads=32, num_kv_heads=32, head_dim=128,
+        block_size=16, context_lens=_uniform_ctx(1024, 4096, 16), num_blocks=65536,
+        max_blocks_per_seq=256, scale=1.0 / math.sqrt(128), seed=2,
+        meta=dict(desc="Llama-style MHA bf16: B16, 32 heads, D128, ctx U[1024,4096], bs16, 65536-page pool")),
+    "long_gqa_bf16": dict(
+        kind="mha", dtype="bf16", batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        block_size=16, context_lens=[131072], num_blocks=8192, scale=1.0 / math.sqrt(128), seed=3,
+        meta=dict(desc="long-context GQA bf16: B1, 32 q / 8 kv heads, D128, ctx 131072, bs16")),
+    "ragged_gqa_bf16": dict(
+        kind="mha", dtype="bf16", batch=64, num_q_heads=64, num_kv_heads=8, head_dim=128,
+        block_size=16, context_lens=_loguniform_ctx(128, 32768, 64), num_blocks=65536,
+        max_blocks_per_seq=2048, scale=1.0 / math.sqrt(128), seed=4,
+        meta=dict(desc="ragged GQA bf16: 64 seqs, ctx log-U[128,32768], 64 q / 8 kv heads, D128, bs16")),
+    "mla_bf16": dict(
+        kind="mla", dtype="bf16", batch=32, num_q_heads=128, num_kv_heads=1, head_dim=576,
+        head_dim_v=512, block_size=64, context_lens=[8192] * 32, num_blocks=4096,
+        scale=1.0 / math.sqrt(192), seed=5,
+        meta=dict(desc="MLA latent bf16: B32, 128 heads, latent 576 (V = first 512), ctx 8192, bs64")),
+}
+
+CONFIG_ORDER = ["tiny_mha_f32", "llama_mha_bf16", "long_gqa_bf16", "ragged_gqa_bf16", "mla_bf16"]
+
+
+def make_config(name: str, *, poison: bool = True, values: bool = True, seed: int | None = None,
+                **overrides) -> PagedDecodeInputs:
+    """Draw one of the five named workloads (optionally with fields overridden)."""
+    spec = dict(CONFIGS[name])
+    spec.update(overrides)
+    if seed is not None:
+        spec["seed"] = seed
+    return make_paged_inputs(name=name, poison=poison, values=values, **spec)
