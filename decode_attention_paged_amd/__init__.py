@@ -1,0 +1,204 @@
+"""Paged split-KV decode attention for MI355X (gfx950).
+
+A thin binding over libpa_decode.so: every step of the computation runs in
+the library's HIP kernels; this module only checks tensors, sizes the
+workspace (a torch allocation) and passes pointers and the current stream.
+
+Layouts (see include/pa_decode.h):
+    q            [B][Hq][D]                 float32 or bfloat16
+    k_cache      [num_blocks][Hkv][bs][D]
+    v_cache      [num_blocks][Hkv][D][bs]
+    kv_cache     [num_blocks][bs][Dqk]      (MLA latent; values = first Dv entries)
+    block_table  [B][max_blocks_per_seq]    int32
+    context_lens [B]                        int32
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import PaError, PaShape  # noqa: F401
+
+__all__ = [
+    "decode", "decode_mla", "decode_partial", "decode_mla_partial", "reduce",
+    "choose_num_splits", "workspace_size", "make_shape", "PaError", "library_path",
+]
+
+_DTYPES = {torch.float32: _lib.PA_F32, torch.bfloat16: _lib.PA_BF16}
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype=None, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def make_shape(*, batch, num_q_heads, num_kv_heads, head_dim, head_dim_v, block_size,
+               max_blocks_per_seq, num_blocks, max_context_len, scale, dtype) -> PaShape:
+    code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return PaShape(batch, num_q_heads, num_kv_heads, head_dim, head_dim_v, block_size,
+                   max_blocks_per_seq, num_blocks, int(max_context_len), float(scale), code)
+
+
+def _mha_shape(q, k_cache, v_cache, block_table, context_lens, max_context_len, scale):
+    _need(q, "q", ndim=3)
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    _need(k_cache, "k_cache", q.dtype, 4, dev)
+    _need(v_cache, "v_cache", q.dtype, 4, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    B, Hq, D = q.shape
+    nb, Hkv, bs, Dk = k_cache.shape
+    if Dk != D:
+        raise ValueError("k_cache head dim differs from q")
+    if tuple(v_cache.shape[:2]) != (nb, Hkv) or v_cache.shape[3] != bs:
+        raise ValueError("v_cache must be [num_blocks][Hkv][Dv][bs]")
+    if block_table.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_table / context_lens batch differs from q")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if B else 0
+    if scale is None:
+        scale = D ** -0.5
+    return make_shape(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                      head_dim_v=v_cache.shape[2], block_size=bs,
+                      max_blocks_per_seq=block_table.shape[1], num_blocks=nb,
+                      max_context_len=max_context_len, scale=scale, dtype=q.dtype)
+
+
+def _mla_shape(q, kv_cache, block_table, context_lens, max_context_len, scale, head_dim_v):
+    _need(q, "q", ndim=3)
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    _need(kv_cache, "kv_cache", q.dtype, 3, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    B, Hq, D = q.shape
+    nb, bs, Dc = kv_cache.shape
+    if Dc != D:
+        raise ValueError("kv_cache width differs from q")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if B else 0
+    return make_shape(batch=B, num_q_heads=Hq, num_kv_heads=1, head_dim=D, head_dim_v=head_dim_v,
+                      block_size=bs, max_blocks_per_seq=block_table.shape[1], num_blocks=nb,
+                      max_context_len=max_context_len, scale=scale, dtype=q.dtype)
+
+
+def choose_num_splits(shape: PaShape, num_cus: int = 0, mla: bool = False) -> int:
+    s = _lib.load().pa_choose_num_splits(ctypes.byref(shape), int(num_cus), int(mla))
+    if s <= 0:
+        raise PaError(_lib.PA_ERR_INVALID, "pa_choose_num_splits")
+    return s
+
+
+def workspace_size(shape: PaShape, num_splits: int = 0, mla: bool = False) -> int:
+    return int(_lib.load().pa_decode_workspace_size(ctypes.byref(shape), int(num_splits), int(mla)))
+
+
+def _outputs(shape, q, out, lse, workspace, num_splits, mla):
+    B, Hq, Dv = shape.batch, shape.num_q_heads, shape.head_dim_v
+    if out is None:
+        out = torch.empty((B, Hq, Dv), dtype=q.dtype, device=q.device)
+    else:
+        _need(out, "out", q.dtype, 3, q.device)
+        if tuple(out.shape) != (B, Hq, Dv):
+            raise ValueError("out must be [B][Hq][Dv]")
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    elif lse is not False:
+        _need(lse, "lse", torch.float32, 2, q.device)
+    need = workspace_size(shape, num_splits, mla)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    return out, (None if lse is False else lse), workspace
+
+
+def decode(q, k_cache, v_cache, block_table, context_lens, *, max_context_len=None, scale=None,
+           num_splits=0, out=None, lse=None, workspace=None, stream=None):
+    """Decode attention over a paged K/V cache (MHA/GQA).  Returns (out, lse).
+
+    num_splits <= 0 lets the library choose.  Pass lse=False to skip it.
+    """
+    shape = _mha_shape(q, k_cache, v_cache, block_table, context_lens, max_context_len, scale)
+    out, lse, ws = _outputs(shape, q, out, lse, workspace, num_splits, False)
+    st = _lib.load().pa_decode(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(block_table), _ptr(context_lens), int(num_splits), _ptr(out),
+                               _ptr(lse), _ptr(ws), _nbytes(ws),
+                               _stream(stream))
+    _lib.check(st, "pa_decode")
+    return out, lse
+
+
+def decode_mla(q, kv_cache, block_table, context_lens, *, max_context_len=None, scale=None,
+               head_dim_v=512, num_splits=0, out=None, lse=None, workspace=None, stream=None):
+    """MLA latent decode: keys = latent rows, values = their first head_dim_v entries."""
+    if scale is None:
+        raise ValueError("MLA needs an explicit scale")
+    shape = _mla_shape(q, kv_cache, block_table, context_lens, max_context_len, scale, head_dim_v)
+    out, lse, ws = _outputs(shape, q, out, lse, workspace, num_splits, True)
+    st = _lib.load().pa_decode_mla(ctypes.byref(shape), _ptr(q), _ptr(kv_cache), _ptr(block_table),
+                                   _ptr(context_lens), int(num_splits), _ptr(out), _ptr(lse),
+                                   _ptr(ws), _nbytes(ws), _stream(stream))
+    _lib.check(st, "pa_decode_mla")
+    return out, lse
+
+
+def decode_partial(shape: PaShape, q, k_cache, v_cache, block_table, context_lens, num_splits,
+                   out, lse, workspace, stream=None):
+    """Only the per-split partial step (writes out/lse directly when S == 1)."""
+    st = _lib.load().pa_decode_partial(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(block_table), _ptr(context_lens), int(num_splits),
+                                       _ptr(out), _ptr(lse), _ptr(workspace),
+                                       _nbytes(workspace),
+                                       _stream(stream))
+    _lib.check(st, "pa_decode_partial")
+
+
+def decode_mla_partial(shape: PaShape, q, kv_cache, block_table, context_lens, num_splits, out,
+                       lse, workspace, stream=None):
+    st = _lib.load().pa_decode_mla_partial(ctypes.byref(shape), _ptr(q), _ptr(kv_cache),
+                                           _ptr(block_table), _ptr(context_lens), int(num_splits),
+                                           _ptr(out), _ptr(lse), _ptr(workspace),
+                                           _nbytes(workspace),
+                                           _stream(stream))
+    _lib.check(st, "pa_decode_mla_partial")
+
+
+def reduce(shape: PaShape, context_lens, num_splits, workspace, out, lse, mla=False, stream=None):
+    """Only the log-sum-exp weighted merge of the split partials."""
+    st = _lib.load().pa_reduce(ctypes.byref(shape), _ptr(context_lens), int(num_splits), int(mla),
+                               _ptr(workspace), _nbytes(workspace),
+                               _ptr(out), _ptr(lse), _stream(stream))
+    _lib.check(st, "pa_reduce")

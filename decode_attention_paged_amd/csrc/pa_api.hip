@@ -1,0 +1,287 @@
+// C ABI of libpa_decode: argument checks, the split plan, dispatch.
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+#include <mutex>
+
+#include "../../include/pa_decode.h"
+#include "pa_launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxDevices = 64;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+enum class Kernel { None, MhaValu, GqaMfma, MlaMfma };
+
+// Which partial kernel serves this shape (host-only, no HIP calls).
+Kernel pick_kernel(const pa_shape& s, bool mla) {
+  const bool bf16 = s.dtype == PA_BF16;
+  if (mla) {
+    return pa::mla_mfma_supported(bf16, s.head_dim, s.head_dim_v, s.block_size, s.num_q_heads)
+               ? Kernel::MlaMfma
+               : Kernel::None;
+  }
+  if (s.head_dim_v != s.head_dim) return Kernel::None;
+  const int G = s.num_q_heads / s.num_kv_heads;
+  if (pa::gqa_mfma_supported(bf16, s.head_dim, s.head_dim_v, s.block_size, G)) return Kernel::GqaMfma;
+  if (pa::mha_valu_supported(bf16, s.head_dim, s.block_size)) return Kernel::MhaValu;
+  return Kernel::None;
+}
+
+// Shape checks that need no pointers (host-only).
+pa_status check_shape(const pa_shape* s, bool mla) {
+  if (!s) return PA_ERR_INVALID;
+  if (s->batch < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1 || s->head_dim < 1 ||
+      s->head_dim_v < 1 || s->block_size < 1 || s->max_blocks_per_seq < 1 || s->num_blocks < 1 ||
+      s->max_context_len < 0)
+    return PA_ERR_INVALID;
+  if (s->num_q_heads % s->num_kv_heads != 0) return PA_ERR_INVALID;
+  if ((int64_t)s->max_context_len > (int64_t)s->max_blocks_per_seq * s->block_size)
+    return PA_ERR_INVALID;
+  if (s->dtype != PA_F32 && s->dtype != PA_BF16) return PA_ERR_INVALID;
+  if (!std::isfinite(s->scale)) return PA_ERR_INVALID;
+  if (mla && (s->num_kv_heads != 1 || s->head_dim_v > s->head_dim)) return PA_ERR_INVALID;
+  if (pick_kernel(*s, mla) == Kernel::None) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+int max_pages(const pa_shape& s) { return (s.max_context_len + s.block_size - 1) / s.block_size; }
+
+// Number of compute units of the current device, cached per device.
+int device_cus() {
+  static std::mutex mu;
+  static int cache[kMaxDevices] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    std::lock_guard<std::mutex> lk(mu);
+    if (cache[dev] > 0) return cache[dev];
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < kMaxDevices && cus > 0) {
+    std::lock_guard<std::mutex> lk(mu);
+    cache[dev] = cus;
+  }
+  return cus;
+}
+
+// Split plan (host only): prefer many small splits so that ragged batches
+// balance over the CUs, but keep each split long enough that its float32
+// partial (written once, read once by the reduction) stays a few percent of
+// the KV bytes it summarises, and cap the grid.
+int heuristic_splits(const pa_shape& s, int cus, bool mla) {
+  const int P = max_pages(s);
+  if (P <= 1) return 1;
+  const Kernel k = pick_kernel(s, mla);
+  const int esz = s.dtype == PA_BF16 ? 2 : 4;
+  if (k == Kernel::MlaMfma) {
+    // one workgroup per (sequence, split) holds every head: fill the CUs once
+    const int units = s.batch;
+    int S = (cus + units - 1) / units;
+    return S < 1 ? 1 : (S > P ? P : S);
+  }
+  int units, heads_per_wg;
+  if (k == Kernel::GqaMfma) {
+    units = s.batch * s.num_kv_heads;
+    heads_per_wg = s.num_q_heads / s.num_kv_heads;
+  } else {
+    units = s.batch * s.num_q_heads;
+    heads_per_wg = 1;
+  }
+  const double page_bytes = (double)s.block_size * (s.head_dim + s.head_dim_v) * esz;
+  const double part_bytes = 2.0 * heads_per_wg * (s.head_dim_v + 1) * 4.0;
+  int c_min = (int)std::ceil(part_bytes / (0.03 * page_bytes));
+  if (c_min < 1) c_min = 1;
+  const long max_wgs = 64L * (cus > 0 ? cus : 256);
+  int c = c_min;
+  if ((long)units * ((P + c - 1) / c) > max_wgs) {
+    c = (int)(((long)P * units + max_wgs - 1) / max_wgs);
+  }
+  int S = (P + c - 1) / c;
+  return S < 1 ? 1 : (S > P ? P : S);
+}
+
+// Resolve num_splits (<= 0: heuristic), clamp to [1, P].  0 on failure.
+int resolve_splits(const pa_shape& s, int32_t num_splits, bool mla) {
+  const int P = max_pages(s);
+  int S = num_splits;
+  if (S <= 0) {
+    const int cus = device_cus();
+    if (cus <= 0) return 0;
+    S = heuristic_splits(s, cus, mla);
+  }
+  if (S > P) S = P;
+  if (S < 1) S = 1;
+  return S;
+}
+
+size_t workspace_bytes_for(const pa_shape& s, int S) {
+  if (S <= 1) return 0;
+  const size_t rows = (size_t)s.batch * s.num_q_heads * S;
+  return align_up(rows * s.head_dim_v * sizeof(float)) + align_up(rows * sizeof(float));
+}
+
+pa::Params make_params(const pa_shape& s, int S, const void* q, const void* k, const void* v,
+                       const int32_t* bt, const int32_t* ctx, void* out, float* lse, void* ws) {
+  pa::Params p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.block_table = bt;
+  p.context_lens = ctx;
+  p.out = out;
+  p.lse = lse;
+  p.B = s.batch;
+  p.Hq = s.num_q_heads;
+  p.Hkv = s.num_kv_heads;
+  p.D = s.head_dim;
+  p.Dv = s.head_dim_v;
+  p.bs = s.block_size;
+  p.maxb = s.max_blocks_per_seq;
+  p.nblocks = s.num_blocks;
+  p.max_ctx = s.max_context_len;
+  p.S = S;
+  const int P = max_pages(s);
+  p.c = P > 0 ? (P + S - 1) / S : 1;
+  p.scale_log2 = s.scale * 1.4426950408889634f;
+  p.final_write = S == 1 ? 1 : 0;
+  if (S > 1) {
+    const size_t rows = (size_t)s.batch * s.num_q_heads * S;
+    p.o_part = static_cast<float*>(ws);
+    p.lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                          align_up(rows * s.head_dim_v * sizeof(float)));
+  }
+  return p;
+}
+
+pa_status run_partial(const pa_shape* shape, const void* q, const void* k, const void* v,
+                      const int32_t* bt, const int32_t* ctx, int32_t num_splits, void* out,
+                      float* lse, void* ws, size_t ws_bytes, void* stream, bool mla, int* S_out) {
+  const pa_status st = check_shape(shape, mla);
+  if (st != PA_OK) return st;
+  if (!q || !k || (!mla && !v) || !bt || !ctx || !out) return PA_ERR_INVALID;
+  // workspace check for an explicit split count needs no device query
+  if (num_splits > 0) {
+    const int S = num_splits > max_pages(*shape) ? (max_pages(*shape) > 0 ? max_pages(*shape) : 1)
+                                                 : num_splits;
+    if (S > 1 && (!ws || ws_bytes < workspace_bytes_for(*shape, S))) return PA_ERR_WORKSPACE;
+  }
+  const int S = resolve_splits(*shape, num_splits, mla);
+  if (S < 1) return PA_ERR_HIP;
+  if (S > 1 && (!ws || ws_bytes < workspace_bytes_for(*shape, S))) return PA_ERR_WORKSPACE;
+  const pa::Params p = make_params(*shape, S, q, k, mla ? k : v, bt, ctx, out, lse, ws);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (pick_kernel(*shape, mla)) {
+    case Kernel::MhaValu: e = pa::launch_mha_valu(p, shape->dtype == PA_BF16, hs); break;
+    case Kernel::GqaMfma: e = pa::launch_gqa_mfma(p, hs); break;
+    case Kernel::MlaMfma: e = pa::launch_mla_mfma(p, hs); break;
+    default: return PA_ERR_UNSUPPORTED;
+  }
+  if (e != hipSuccess) return PA_ERR_HIP;
+  if (S_out) *S_out = S;
+  return PA_OK;
+}
+
+pa_status run_reduce(const pa_shape* shape, const int32_t* ctx, int S, const void* ws, void* out,
+                     float* lse, void* stream) {
+  if (S <= 1) return PA_OK;
+  const pa::Params p = make_params(*shape, S, nullptr, nullptr, nullptr, nullptr, ctx, out, lse,
+                                   const_cast<void*>(ws));
+  const hipError_t e = pa::launch_reduce(p, shape->dtype == PA_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int32_t status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported dtype/head_dim/block_size combination";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t pa_version(void) { return 100; }
+
+int32_t pa_choose_num_splits(const pa_shape* shape, int32_t num_cus, int32_t mla) {
+  if (check_shape(shape, mla != 0) != PA_OK) return 0;
+  int cus = num_cus;
+  if (cus <= 0) cus = device_cus();
+  if (cus <= 0) return 0;
+  return heuristic_splits(*shape, cus, mla != 0);
+}
+
+size_t pa_decode_workspace_size(const pa_shape* shape, int32_t num_splits, int32_t mla) {
+  if (check_shape(shape, mla != 0) != PA_OK) return 0;
+  const int S = resolve_splits(*shape, num_splits, mla != 0);
+  if (S < 1) return 0;
+  return workspace_bytes_for(*shape, S);
+}
+
+pa_status pa_decode_partial(const pa_shape* shape, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            const int32_t* context_lens, int32_t num_splits, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return run_partial(shape, q, k_cache, v_cache, block_table, context_lens, num_splits, out, lse,
+                     workspace, workspace_bytes, stream, false, nullptr);
+}
+
+pa_status pa_decode_mla_partial(const pa_shape* shape, const void* q, const void* kv_cache,
+                                const int32_t* block_table, const int32_t* context_lens,
+                                int32_t num_splits, void* out, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return run_partial(shape, q, kv_cache, nullptr, block_table, context_lens, num_splits, out, lse,
+                     workspace, workspace_bytes, stream, true, nullptr);
+}
+
+pa_status pa_reduce(const pa_shape* shape, const int32_t* context_lens, int32_t num_splits,
+                    int32_t mla, const void* workspace, size_t workspace_bytes, void* out,
+                    float* lse, void* stream) {
+  const pa_status st = check_shape(shape, mla != 0);
+  if (st != PA_OK) return st;
+  if (!context_lens || !out) return PA_ERR_INVALID;
+  if (num_splits > 0) {
+    const int P = max_pages(*shape);
+    const int S = num_splits > P ? (P > 0 ? P : 1) : num_splits;
+    if (S <= 1) return PA_OK;
+    if (!workspace || workspace_bytes < workspace_bytes_for(*shape, S)) return PA_ERR_WORKSPACE;
+  }
+  const int S = resolve_splits(*shape, num_splits, mla != 0);
+  if (S < 1) return PA_ERR_HIP;
+  if (S <= 1) return PA_OK;
+  if (!workspace || workspace_bytes < workspace_bytes_for(*shape, S)) return PA_ERR_WORKSPACE;
+  return run_reduce(shape, context_lens, S, workspace, out, lse, stream);
+}
+
+pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_table, const int32_t* context_lens, int32_t num_splits,
+                    void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  int S = 0;
+  const pa_status st = run_partial(shape, q, k_cache, v_cache, block_table, context_lens, num_splits,
+                                   out, lse, workspace, workspace_bytes, stream, false, &S);
+  if (st != PA_OK) return st;
+  return run_reduce(shape, context_lens, S, workspace, out, lse, stream);
+}
+
+pa_status pa_decode_mla(const pa_shape* shape, const void* q, const void* kv_cache,
+                        const int32_t* block_table, const int32_t* context_lens, int32_t num_splits,
+                        void* out, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  int S = 0;
+  const pa_status st = run_partial(shape, q, kv_cache, nullptr, block_table, context_lens,
+                                   num_splits, out, lse, workspace, workspace_bytes, stream, true, &S);
+  if (st != PA_OK) return st;
+  return run_reduce(shape, context_lens, S, workspace, out, lse, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,242 @@
+// Split-KV partial kernel for grouped-query decode on the matrix cores.
+//
+// When G = Hq / Hkv query heads share one KV head, each K/V tile is a real
+// dense contraction with G columns, so the scores S^T = K Q^T and the value
+// product O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16 (heads padded to
+// 16 columns).  One workgroup handles one (split, KV head, sequence): the
+// tile of a page is read from HBM once for all G heads.  Its NW waves take
+// pairs of pages round-robin (a pair is 32 tokens, the MFMA contraction
+// depth of the value product) and merge their running states in LDS at the
+// end, which yields the split's (o_s, lse_s) of Flash-Decoding's second step
+// (page 4).
+//
+// Operand layouts (MFMA 16x16x32 bf16: A[i][k] in lane i + 16*(k/8), element
+// k%8; B[k][j] in lane j + 16*(k/8); D[i][j] in lane j + 16*(i/4), reg i%4):
+//   K is [bs][D] per (page, head): lane (quad, n) loads 16 bytes of one token
+//   row, so K is the A operand as stored.  Row n of score chain c is the
+//   token (n/8 selects the page of the pair) ((n/4)%2)*8 + 4c + n%4; with this
+//   assignment the 8 scores a lane receives (both chains) are tokens
+//   (quad%2)*8 + 0..7 of page quad/2, exactly the 8 contraction entries its
+//   B operand of the value product needs.  So P^T comes from the lane's own
+//   registers, without shuffles.
+//   V is stored [D][bs]: 16 contiguous bytes are 8 consecutive tokens of one
+//   dim, i.e. the A operand of O^T = V^T P^T as stored.
+//   Both outputs put head n in lane column n, so the running max, the
+//   rescale factor and the accumulator of a head live in the same lanes.
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+namespace {
+
+constexpr int kD = 128;                 // head dim
+constexpr int kBS = 16;                 // tokens per page
+constexpr int kRowB = kD * 2;           // bytes per K row
+constexpr int kTile = kBS * kRowB;      // bytes per (page, head) tile, K and V alike
+constexpr int kOPad = kD + 4;           // LDS row stride of the merge buffer (floats)
+
+struct PairTile {
+  u32x4 k[2][4];   // [chain][k-step]
+  u32x4 v[8];      // [dim block]
+};
+
+__device__ __forceinline__ void load_pair(PairTile& t, const char* ka, const char* kb_,
+                                          const char* va, const char* vb, int koff, int voff,
+                                          bool ksel, bool vsel) {
+  const char* kp = (ksel ? kb_ : ka) + koff;
+  const char* vp = (vsel ? vb : va) + voff;
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) t.k[c][kb] = ld128(kp + c * 4 * kRowB + kb * 64);
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) t.v[nb] = ld128(vp + nb * 16 * 32);
+}
+
+__device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <bool PARTIAL>
+__device__ __forceinline__ void consume_pair(PairTile& t, const u32x4 (&qf)[4], f32x4 (&acc)[8],
+                                             float& m, float& l, float scale_log2, int tok0,
+                                             int ctx) {
+  // tok0: logical index of this lane's first score token; the lane's tokens
+  // are tok0 .. tok0+7 (tok0 < 0 marks a page missing from the pair).
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    s0 = mfma(t.k[0][kb], qf[kb], s0);
+    s1 = mfma(t.k[1][kb], qf[kb], s1);
+  }
+  float sc[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sc[r] = s0[r] * scale_log2;
+    sc[4 + r] = s1[r] * scale_log2;
+  }
+  if constexpr (PARTIAL) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sc[j] = (tok0 >= 0 && tok0 + j < ctx) ? sc[j] : kNegInf;
+  }
+  float mx = sc[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sc[j]);
+  mx = max_xor32(max_xor16(mx));
+  const float mn = fmaxf(m, mx);
+  const float alpha = fast_exp2(m - mn);
+  m = mn;
+  float pr[8];
+  float ls = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    pr[j] = fast_exp2(sc[j] - mn);
+    ls += pr[j];
+  }
+  l = fmaf(l, alpha, ls);
+  u32x4 pb;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) pb[e] = pack_bf16(pr[2 * e], pr[2 * e + 1]);
+  if constexpr (PARTIAL) {
+    // tokens past the context may hold anything (NaN): zero them in V
+    u32x4 keep;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool v0 = tok0 >= 0 && tok0 + 2 * e < ctx;
+      const bool v1 = tok0 >= 0 && tok0 + 2 * e + 1 < ctx;
+      keep[e] = (v0 ? 0x0000ffffu : 0u) | (v1 ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t.v[nb][e] &= keep[e];
+  }
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    f32x4 a = acc[nb];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] *= alpha;
+    acc[nb] = mfma(t.v[nb], pb, a);
+  }
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
+  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int quad = lane >> 4, n = lane & 15;
+  const int G = p.Hq / p.Hkv;
+  const int ctx = clampi(p.context_lens[b], 0, p.max_ctx);
+  const int pages = (ctx + kBS - 1) / kBS;
+  const int nsplit = splits_of(pages, p.c);
+  if (s >= (nsplit > 0 ? nsplit : 1)) return;
+  const int p0 = s * p.c;
+  const int p1 = min(pages, p0 + p.c);
+
+  // Q^T as the B operand of the score MFMA: column n = head kvh*G + n
+  u32x4 qf[4];
+  if (n < G) {
+    const char* qr = static_cast<const char*>(p.q) + ((size_t)b * p.Hq + kvh * G + n) * kRowB;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) qf[kb] = ld128(qr + kb * 64 + quad * 16);
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) qf[kb] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const int* bt = p.block_table + (size_t)b * p.maxb;
+  const size_t pstride = (size_t)p.Hkv * kTile;   // bytes per page, K and V pools alike
+  const char* kbase = static_cast<const char*>(p.k) + (size_t)kvh * kTile;
+  const char* vbase = static_cast<const char*>(p.v) + (size_t)kvh * kTile;
+  const bool ksel = (n >> 3) != 0;
+  const int koff = (((n >> 2) & 1) * 8 + (n & 3)) * kRowB + quad * 16;
+  const bool vsel = (quad >> 1) != 0;
+  const int voff = n * 32 + (quad & 1) * 16;
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf, l = 0.f;
+
+  const int npairs = (p1 - p0 + 1) >> 1;
+  int k = w;
+  PairTile cur, nxt;
+  auto issue = [&](PairTile& t, int kk) {
+    const int pa_ = p0 + 2 * kk;
+    const bool hasb = pa_ + 1 < p1;
+    const int ida = clampi(bt[pa_], 0, p.nblocks - 1);
+    const int idb = hasb ? clampi(bt[pa_ + 1], 0, p.nblocks - 1) : ida;
+    load_pair(t, kbase + ida * pstride, kbase + idb * pstride, vbase + ida * pstride,
+              vbase + idb * pstride, koff, voff, ksel, vsel);
+  };
+  if (k < npairs) issue(cur, k);
+  for (; k < npairs; k += NW) {
+    if (k + NW < npairs) issue(nxt, k + NW);
+    const int pa_ = p0 + 2 * k;
+    const bool hasb = pa_ + 1 < p1;
+    const bool partial = !hasb || (pa_ + 2) * kBS > ctx;
+    const int mypage = vsel ? pa_ + 1 : pa_;
+    const int tok0 = (vsel && !hasb) ? -1 : mypage * kBS + (quad & 1) * 8;
+    if (partial)
+      consume_pair<true>(cur, qf, acc, m, l, p.scale_log2, tok0, ctx);
+    else
+      consume_pair<false>(cur, qf, acc, m, l, p.scale_log2, tok0, ctx);
+    cur = nxt;
+  }
+  const float ltot = sum_xor32(sum_xor16(l));
+
+  // ---- merge the NW wave states per head and write the split result
+  __shared__ float sm_m[NW][16], sm_l[NW][16];
+  __shared__ float sm_o[NW][16][kOPad];
+  if (quad == 0) {
+    sm_m[w][n] = m;
+    sm_l[w][n] = ltot;
+  }
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm_o[w][n][nb * 16 + quad * 4 + r] = acc[nb][r];
+  __syncthreads();
+
+  for (int idx = threadIdx.x; idx < G * kD; idx += NW * 64) {
+    const int hn = idx / kD, d = idx % kD;
+    float M = kNegInf;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) M = fmaxf(M, sm_m[i][hn]);
+    const bool empty = (M == kNegInf);
+    float L = 0.f, o = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const float f = empty ? 0.f : fast_exp2(sm_m[i][hn] - M);
+      L = fmaf(f, sm_l[i][hn], L);
+      o = fmaf(f, sm_o[i][hn][d], o);
+    }
+    o = empty ? 0.f : o / L;
+    const size_t row = (size_t)b * p.Hq + kvh * G + hn;
+    if (p.final_write) {
+      static_cast<uint16_t*>(p.out)[row * kD + d] = to_bf16(o);
+      if (d == 0 && p.lse) p.lse[row] = empty ? kNegInf : (M + fast_log2(L)) * kLn2;
+    } else {
+      p.o_part[(row * p.S + s) * kD + d] = o;
+      if (d == 0) p.lse_part[row * p.S + s] = empty ? kNegInf : (M + fast_log2(L)) * kLn2;
+    }
+  }
+}
+
+constexpr int kGqaWaves = 4;
+
+}  // namespace
+
+bool gqa_mfma_supported(bool bf16, int D, int Dv, int bs, int G) {
+  return bf16 && D == kD && Dv == kD && bs == kBS && G >= 2 && G <= 16;
+}
+
+hipError_t launch_gqa_mfma(const Params& p, hipStream_t st) {
+  dim3 grid(p.S, p.Hkv, p.B);
+  hipLaunchKernelGGL(gqa_mfma_partial<kGqaWaves>, grid, dim3(kGqaWaves * 64), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,39 @@
+// Kernel parameter block and launch entry points (internal to libpa_decode).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Everything a partial or reduce kernel needs, passed by value as the kernel
+// argument.  Pointers are device pointers owned by the caller.
+struct Params {
+  const void* q;             // [B][Hq][Dqk]
+  const void* k;             // MHA/GQA: [nb][Hkv][bs][D]; MLA: latent [nb][bs][Dqk]
+  const void* v;             // MHA/GQA: [nb][Hkv][Dv][bs]; MLA: unused (aliases k)
+  const int32_t* block_table;  // [B][maxb]
+  const int32_t* context_lens; // [B]
+  void* out;                 // [B][Hq][Dv] dtype
+  float* lse;                // [B][Hq] or nullptr
+  float* o_part;             // [B][Hq][S][Dv] (S > 1)
+  float* lse_part;           // [B][Hq][S]     (S > 1)
+  int32_t B, Hq, Hkv, D, Dv, bs, maxb, nblocks, max_ctx;
+  int32_t S;                 // splits in the grid
+  int32_t c;                 // pages per split
+  float scale_log2;          // scale * log2(e)
+  int32_t final_write;       // 1: S == 1, write out/lse directly
+};
+
+// Each returns hipSuccess or the launch error.  Shapes are validated by the caller.
+hipError_t launch_mha_valu(const Params& p, bool bf16, hipStream_t st);
+hipError_t launch_gqa_mfma(const Params& p, hipStream_t st);
+hipError_t launch_mla_mfma(const Params& p, hipStream_t st);
+hipError_t launch_reduce(const Params& p, bool bf16, hipStream_t st);
+
+// Which kernels exist (host-side predicates used by validation and dispatch).
+bool mha_valu_supported(bool bf16, int D, int bs);
+bool gqa_mfma_supported(bool bf16, int D, int Dv, int bs, int G);
+bool mla_mfma_supported(bool bf16, int Dqk, int Dv, int bs, int Hq);
+
+}  // namespace pa

@@ -1,0 +1,302 @@
+// Split-KV partial kernel for plain multi-head decode, on the vector ALUs.
+//
+// One workgroup per (split, query head, sequence); its NW waves take the
+// split's pages round-robin and each keeps its own running (max, sum, acc)
+// state, merged in LDS at the end (the per-chunk step of Flash-Decoding,
+// page 4: attention of the query with each chunk, recording its
+// log-sum-exp).  A single query row per KV head gives no operand reuse, so
+// the dot products run on the VALU (v_dot2_f32_bf16 for bf16) rather than
+// on MFMA.
+//
+// Lane mapping for one (page, head) tile:
+//   K rows are D*esize bytes; LPR lanes cover a row with 16-byte loads and a
+//   wave loads RPI = 64/LPR rows per instruction.  The score of token
+//   i*RPI + r ends up in every lane of row group r after a DPP reduction.
+//   V is stored [D][bs]: lane l reads 16 contiguous bytes = TPC tokens of
+//   dim j*64 + l, so all lanes of one load share the same tokens and the
+//   token weights can be wave-uniform scalars (v_readlane into SGPRs).
+//   Each lane therefore owns whole output dims; no cross-lane sum of the
+//   accumulator is needed.
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+namespace {
+
+template <bool BF16, int D, int BS>
+struct MhaCfg {
+  static constexpr int ES = BF16 ? 2 : 4;
+  static constexpr int ROWB = D * ES;      // bytes per K row
+  static constexpr int LPR = ROWB / 16;    // lanes per K row
+  static constexpr int RPI = 64 / LPR;     // K rows per load instruction
+  static constexpr int KI = BS / RPI;      // K loads per page
+  static constexpr int TPC = 16 / ES;      // tokens per 16-byte V chunk
+  static constexpr int CPD = BS / TPC;     // V chunks per dim
+  static constexpr int DPL = D / 64;       // output dims per lane
+  static constexpr int VI = DPL * CPD;     // V loads per page
+  static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row width");
+  static_assert(BS % RPI == 0 && BS % TPC == 0 && D % 64 == 0, "tile shape");
+};
+
+// Sum over the LPR lanes of one K row.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+  if constexpr (LPR == 8) {
+    return group_sum<8>(x);
+  } else if constexpr (LPR == 16) {
+    return group_sum<16>(x);
+  } else {
+    return sum_xor16(group_sum<16>(x));
+  }
+}
+
+// Max / sum across the RPI row groups of a wave.
+template <int LPR>
+__device__ __forceinline__ float across_rows_max(float x) {
+  if constexpr (LPR == 8) x = fmaxf(x, dpp<kDppRowRor8>(x));
+  if constexpr (LPR <= 16) x = max_xor16(x);
+  return max_xor32(x);
+}
+template <int LPR>
+__device__ __forceinline__ float across_rows_sum(float x) {
+  if constexpr (LPR == 8) x += dpp<kDppRowRor8>(x);
+  if constexpr (LPR <= 16) x = sum_xor16(x);
+  return sum_xor32(x);
+}
+
+template <bool BF16, int D, int BS>
+struct MhaTile {
+  u32x4 k[MhaCfg<BF16, D, BS>::KI];
+  u32x4 v[MhaCfg<BF16, D, BS>::VI];
+};
+
+template <bool BF16, int D, int BS>
+__device__ __forceinline__ void load_tile(MhaTile<BF16, D, BS>& t, const char* kp, const char* vp,
+                                          int lane) {
+  using C = MhaCfg<BF16, D, BS>;
+  const char* kl = kp + (lane / C::LPR) * C::ROWB + (lane % C::LPR) * 16;
+#pragma unroll
+  for (int i = 0; i < C::KI; ++i) t.k[i] = ld128(kl + i * C::RPI * C::ROWB);
+#pragma unroll
+  for (int j = 0; j < C::DPL; ++j)
+#pragma unroll
+    for (int h = 0; h < C::CPD; ++h)
+      t.v[j * C::CPD + h] = ld128(vp + (size_t)(j * 64 + lane) * BS * C::ES + h * 16);
+}
+
+// Running state of one wave: max (log2 domain, wave-uniform), this lane's
+// row-group share of the sum, and the lane's output dims.
+template <int DPL>
+struct MhaState {
+  float m;
+  float l;
+  float acc[DPL];
+};
+
+template <bool BF16, int D, int BS, bool PARTIAL>
+__device__ __forceinline__ void consume_tile(const MhaTile<BF16, D, BS>& t, MhaState<D / 64>& st,
+                                             const u32x4& qv, const float (&qf)[4], float scale_log2,
+                                             int lane, int nvalid) {
+  using C = MhaCfg<BF16, D, BS>;
+  const int row = lane / C::LPR;
+  float sc[C::KI];
+#pragma unroll
+  for (int i = 0; i < C::KI; ++i) {
+    float d = 0.f;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d = dot2_bf16(qv[e], t.k[i][e], d);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d = fmaf(qf[e], as_f32(t.k[i][e]), d);
+    }
+    d = row_sum<C::LPR>(d) * scale_log2;
+    if constexpr (PARTIAL) d = (i * C::RPI + row < nvalid) ? d : kNegInf;
+    sc[i] = d;
+  }
+  float mx = sc[0];
+#pragma unroll
+  for (int i = 1; i < C::KI; ++i) mx = fmaxf(mx, sc[i]);
+  mx = across_rows_max<C::LPR>(mx);
+  const float mn = fmaxf(st.m, mx);          // finite: the tile has a valid token
+  const float alpha = fast_exp2(st.m - mn);  // 0 on the first tile (m = -inf)
+  st.m = mn;
+  float pr[C::KI];
+  float lsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < C::KI; ++i) {
+    pr[i] = fast_exp2(sc[i] - mn);
+    lsum += pr[i];
+  }
+  st.l = fmaf(st.l, alpha, lsum);
+  // token weights as wave-uniform scalars: token i*RPI + r lives in row group r
+  float ps[BS];
+#pragma unroll
+  for (int t2 = 0; t2 < BS; ++t2) ps[t2] = readlane(pr[t2 / C::RPI], (t2 % C::RPI) * C::LPR);
+#pragma unroll
+  for (int j = 0; j < C::DPL; ++j) {
+    float a = st.acc[j] * alpha;
+#pragma unroll
+    for (int h = 0; h < C::CPD; ++h) {
+      const u32x4 vv = t.v[j * C::CPD + h];
+      if constexpr (BF16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t0 = h * 8 + 2 * e;
+          float v0 = bf16lo(vv[e]), v1 = bf16hi(vv[e]);
+          if constexpr (PARTIAL) {
+            v0 = (t0 < nvalid) ? v0 : 0.f;
+            v1 = (t0 + 1 < nvalid) ? v1 : 0.f;
+          }
+          a = fmaf(ps[t0], v0, a);
+          a = fmaf(ps[t0 + 1], v1, a);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t0 = h * 4 + e;
+          float v0 = as_f32(vv[e]);
+          if constexpr (PARTIAL) v0 = (t0 < nvalid) ? v0 : 0.f;
+          a = fmaf(ps[t0], v0, a);
+        }
+      }
+    }
+    st.acc[j] = a;
+  }
+}
+
+template <bool BF16, int D, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) void mha_valu_partial(Params p) {
+  using C = MhaCfg<BF16, D, BS>;
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int ctx = clampi(p.context_lens[b], 0, p.max_ctx);
+  const int pages = (ctx + BS - 1) / BS;
+  const int nsplit = splits_of(pages, p.c);
+  if (s >= (nsplit > 0 ? nsplit : 1)) return;
+  const int g = h / (p.Hq / p.Hkv);
+  const int p0 = s * p.c;
+  const int p1 = min(pages, p0 + p.c);
+
+  // this lane's 16 bytes of the query row
+  const char* qrow = static_cast<const char*>(p.q) + ((size_t)b * p.Hq + h) * C::ROWB;
+  const u32x4 qv = ld128(qrow + (lane % C::LPR) * 16);
+  float qf[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) qf[e] = as_f32(qv[e]);
+
+  const int* bt = p.block_table + (size_t)b * p.maxb;
+  const size_t kstride = (size_t)p.Hkv * BS * C::ROWB;      // bytes per K page
+  const size_t vstride = (size_t)p.Hkv * D * BS * C::ES;    // bytes per V page
+  const char* kbase = static_cast<const char*>(p.k) + (size_t)g * BS * C::ROWB;
+  const char* vbase = static_cast<const char*>(p.v) + (size_t)g * D * BS * C::ES;
+
+  MhaState<C::DPL> st;
+  st.m = kNegInf;
+  st.l = 0.f;
+#pragma unroll
+  for (int j = 0; j < C::DPL; ++j) st.acc[j] = 0.f;
+
+  int pg = p0 + w;
+  MhaTile<BF16, D, BS> cur, nxt;
+  if (pg < p1) {
+    const int id = clampi(bt[pg], 0, p.nblocks - 1);
+    load_tile(cur, kbase + id * kstride, vbase + id * vstride, lane);
+  }
+  for (; pg < p1; pg += NW) {
+    const int pn = pg + NW;
+    if (pn < p1) {
+      const int id = clampi(bt[pn], 0, p.nblocks - 1);
+      load_tile(nxt, kbase + id * kstride, vbase + id * vstride, lane);
+    }
+    const int nvalid = ctx - pg * BS;
+    if (nvalid >= BS)
+      consume_tile<BF16, D, BS, false>(cur, st, qv, qf, p.scale_log2, lane, BS);
+    else
+      consume_tile<BF16, D, BS, true>(cur, st, qv, qf, p.scale_log2, lane, nvalid);
+    cur = nxt;
+  }
+  const float ltot = across_rows_sum<C::LPR>(st.l);
+
+  // ---- merge the NW wave states and write the split result
+  __shared__ float sm_m[NW], sm_l[NW];
+  __shared__ float sm_acc[NW][D];
+  if (lane == 0) {
+    sm_m[w] = st.m;
+    sm_l[w] = ltot;
+  }
+#pragma unroll
+  for (int j = 0; j < C::DPL; ++j) sm_acc[w][j * 64 + lane] = st.acc[j];
+  __syncthreads();
+
+  float M = kNegInf;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) M = fmaxf(M, sm_m[i]);
+  float f[NW];
+  float L = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    f[i] = (M == kNegInf) ? 0.f : fast_exp2(sm_m[i] - M);
+    L = fmaf(f[i], sm_l[i], L);
+  }
+  const bool empty = (M == kNegInf);
+  const float inv = empty ? 0.f : 1.f / L;
+  const float lse = empty ? kNegInf : (M + fast_log2(L)) * kLn2;
+  const size_t row = (size_t)b * p.Hq + h;
+  for (int d = threadIdx.x; d < D; d += NW * 64) {
+    float o = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) o = fmaf(f[i], sm_acc[i][d], o);
+    o *= inv;
+    if (p.final_write) {
+      if constexpr (BF16)
+        static_cast<uint16_t*>(p.out)[row * D + d] = to_bf16(o);
+      else
+        static_cast<float*>(p.out)[row * D + d] = o;
+    } else {
+      p.o_part[(row * p.S + s) * D + d] = o;
+    }
+  }
+  if (threadIdx.x == 0) {
+    if (p.final_write) {
+      if (p.lse) p.lse[row] = lse;
+    } else {
+      p.lse_part[row * p.S + s] = lse;
+    }
+  }
+}
+
+constexpr int kMhaWaves = 4;
+
+template <bool BF16, int D, int BS>
+hipError_t launch_one(const Params& p, hipStream_t st) {
+  dim3 grid(p.S, p.Hq, p.B);
+  hipLaunchKernelGGL((mha_valu_partial<BF16, D, BS, kMhaWaves>), grid, dim3(kMhaWaves * 64), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool mha_valu_supported(bool bf16, int D, int bs) {
+  (void)bf16;
+  return (D == 64 || D == 128) && (bs == 16 || bs == 32);
+}
+
+hipError_t launch_mha_valu(const Params& p, bool bf16, hipStream_t st) {
+  const int D = p.D, bs = p.bs;
+  if (bf16) {
+    if (D == 128 && bs == 16) return launch_one<true, 128, 16>(p, st);
+    if (D == 128 && bs == 32) return launch_one<true, 128, 32>(p, st);
+    if (D == 64 && bs == 16) return launch_one<true, 64, 16>(p, st);
+    if (D == 64 && bs == 32) return launch_one<true, 64, 32>(p, st);
+  } else {
+    if (D == 128 && bs == 16) return launch_one<false, 128, 16>(p, st);
+    if (D == 128 && bs == 32) return launch_one<false, 128, 32>(p, st);
+    if (D == 64 && bs == 16) return launch_one<false, 64, 16>(p, st);
+    if (D == 64 && bs == 32) return launch_one<false, 64, 32>(p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

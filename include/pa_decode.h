@@ -1,0 +1,171 @@
+/*
+ * pa_decode.h - single-token decode attention over a paged KV cache, split-KV.
+ *
+ * C ABI of libpa_decode.so (gfx950 / MI355X).  Plain pointers and sizes only.
+ *
+ * What is computed (the definition every entry point reaches, up to rounding):
+ *   For sequence b < batch, query head h < num_q_heads and logical token
+ *   i < context_lens[b]:
+ *       page  = block_table[b * max_blocks_per_seq + i / block_size]
+ *       slot  = i % block_size,        g = h / (num_q_heads / num_kv_heads)
+ *       s_i   = scale * <q[b][h][:], k_i>
+ *       out[b][h][:] = sum_i exp(s_i - m) v_i / sum_i exp(s_i - m),  m = max_i s_i
+ *       lse[b][h]    = m + ln(sum_i exp(s_i - m))          (natural log)
+ *   This is scaled dot-product softmax attention of one query row per head
+ *   (page 1, "Transformer introduction": each query scored against every key,
+ *   scores re-weighting the values; page 2: multi-head attention as h
+ *   self-attentions), over KV memory managed in fixed pages as PagedAttention
+ *   does (page 1, vLLM README snippets).  It is evaluated with Flash-Decoding's
+ *   three steps (page 4, "Flash Decoding mainly has three steps"): the pages of
+ *   a sequence are cut into contiguous splits, each split's attention is
+ *   computed in parallel with its log-sum-exp, and the split results are
+ *   rescaled and reduced into the exact output.
+ *
+ * Memory layouts (all row-major, contiguous, device memory):
+ *   q            [batch][num_q_heads][head_dim]                    dtype
+ *   k_cache      [num_blocks][num_kv_heads][block_size][head_dim]  dtype
+ *   v_cache      [num_blocks][num_kv_heads][head_dim_v][block_size] dtype
+ *   kv_cache     [num_blocks][block_size][head_dim]  (MLA latent)  dtype
+ *                keys are whole rows, values the first head_dim_v entries
+ *   block_table  [batch][max_blocks_per_seq]                        int32
+ *   context_lens [batch]                                            int32
+ *   out          [batch][num_q_heads][head_dim_v]                   dtype
+ *   lse          [batch][num_q_heads]                               float32
+ *   dtype PA_F32 = float32, PA_BF16 = bfloat16 (accumulation is float32;
+ *   bf16 outputs are rounded to nearest even).
+ *
+ * Splits: with S = num_splits and P = ceil(max_context_len / block_size),
+ *   every split covers c = ceil(P / S) pages; sequence b uses
+ *   ceil(ceil(context_lens[b] / block_size) / c) splits (ragged batches
+ *   therefore use fewer splits for shorter sequences).  num_splits <= 0 asks
+ *   for pa_choose_num_splits().  S larger than P is legal (empty splits).
+ *
+ * Ownership and execution: every pointer is caller-owned device memory; the
+ *   library allocates nothing and keeps no state beyond a per-device cache of
+ *   the compute-unit count.  `stream` is a hipStream_t (NULL = default stream).
+ *   Calls are asynchronous on `stream`; outputs are valid once it completes.
+ *   Calls are thread-safe and reentrant; concurrent calls must not share a
+ *   workspace.
+ *
+ * Errors: a status is returned, nothing is thrown.  Arguments are checked on
+ *   the host before any HIP call; on failure nothing is launched.  Device-side
+ *   context_lens are clamped to [0, max_context_len] and block ids to
+ *   [0, num_blocks), so malformed tables cannot read outside the pools.
+ */
+#ifndef PA_DECODE_H
+#define PA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID = 1,     /* NULL required pointer, non-positive size, inconsistent shape */
+  PA_ERR_UNSUPPORTED = 2, /* well-formed but no kernel for this dtype/head_dim/block_size */
+  PA_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than pa_decode_workspace_size() */
+  PA_ERR_HIP = 4          /* the HIP runtime reported an error (device query or launch) */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+typedef struct pa_shape {
+  int32_t batch;              /* B >= 1 */
+  int32_t num_q_heads;        /* Hq >= 1 */
+  int32_t num_kv_heads;       /* Hkv >= 1, divides Hq; must be 1 for MLA */
+  int32_t head_dim;           /* Dqk: width of q and k (MLA: latent width) */
+  int32_t head_dim_v;         /* Dv: width of v and out (MHA/GQA: == head_dim) */
+  int32_t block_size;         /* tokens per page */
+  int32_t max_blocks_per_seq; /* row length of block_table */
+  int32_t num_blocks;         /* pages in the pool */
+  int32_t max_context_len;    /* host-side upper bound of context_lens; sizes the grid */
+  float scale;                /* score scale, e.g. 1/sqrt(head_dim) */
+  int32_t dtype;              /* pa_dtype of q, caches and out */
+} pa_shape;
+
+/* Human-readable name of a status code.  Never NULL. */
+const char* pa_status_string(int32_t status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t pa_version(void);
+
+/*
+ * Split-count heuristic (the split control that Flash-Decoding adds when
+ * batch x heads alone cannot fill the GPU; page 4, the TRT-LLM
+ * multi_block_mode / vLLM PagedAttention V2 snippet).  Picks S so that the
+ * partial kernel launches enough workgroups for `num_cus` compute units
+ * while each split keeps enough pages to amortise its partial write.
+ * num_cus <= 0 queries the current HIP device.  Returns S >= 1, or 0 if the
+ * shape is invalid (or the device query failed).  `mla` != 0 selects the
+ * latent kernel's work unit.  Host only.
+ */
+int32_t pa_choose_num_splits(const pa_shape* shape, int32_t num_cus, int32_t mla);
+
+/*
+ * Bytes of workspace a call with this shape and split count needs: float32
+ * partials o[batch][num_q_heads][S][head_dim_v] and lse[batch][num_q_heads][S],
+ * each 256-byte aligned.  0 when S resolves to 1 (the partial kernel then
+ * writes out/lse directly).  num_splits <= 0 resolves through the heuristic
+ * (which may query the device).  Returns 0 on an invalid shape.  Host only.
+ */
+size_t pa_decode_workspace_size(const pa_shape* shape, int32_t num_splits, int32_t mla);
+
+/*
+ * Paged split-KV decode attention, MHA and GQA (num_q_heads a multiple of
+ * num_kv_heads).  Runs the per-split partial kernel and, when S > 1, the
+ * log-sum-exp weighted reduction.  `lse` may be NULL.  `workspace` may be
+ * NULL only when S resolves to 1.
+ * Supported: PA_F32 with head_dim 64 or 128; PA_BF16 with head_dim 64 or 128;
+ * head_dim_v == head_dim; block_size 16 or 32.
+ */
+pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* block_table,
+                    const int32_t* context_lens, int32_t num_splits, void* out,
+                    float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * MLA latent decode: every query head attends to one shared latent row per
+ * token (page 2/3: MLA compresses the KV cache into a latent vector and
+ * caches only it).  Keys are whole latent rows (head_dim wide), values their
+ * first head_dim_v entries, read from the same memory.  num_kv_heads must be 1.
+ * Supported: PA_BF16, head_dim 576, head_dim_v 512, block_size 64,
+ * num_q_heads a multiple of 16.
+ */
+pa_status pa_decode_mla(const pa_shape* shape, const void* q, const void* kv_cache,
+                        const int32_t* block_table, const int32_t* context_lens,
+                        int32_t num_splits, void* out, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * The two steps of pa_decode / pa_decode_mla, exposed separately so a caller
+ * can time them, or gather partials computed elsewhere (for example other
+ * devices' page ranges) before reducing.  The partial step writes the split
+ * partials into `workspace` (or, when S resolves to 1, out/lse directly).
+ * pa_reduce merges them: M = max_s lse_s, w_s = exp(lse_s - M),
+ * out = sum_s w_s o_s / sum_s w_s, lse = M + ln(sum_s w_s) (page 4, step
+ * three: rescale the split results by their log-sum-exp and reduce).
+ * pa_reduce with S == 1 does nothing and returns PA_OK.
+ */
+pa_status pa_decode_partial(const pa_shape* shape, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            const int32_t* context_lens, int32_t num_splits, void* out,
+                            float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+pa_status pa_decode_mla_partial(const pa_shape* shape, const void* q, const void* kv_cache,
+                                const int32_t* block_table, const int32_t* context_lens,
+                                int32_t num_splits, void* out, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+pa_status pa_reduce(const pa_shape* shape, const int32_t* context_lens, int32_t num_splits,
+                    int32_t mla, const void* workspace, size_t workspace_bytes, void* out,
+                    float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_DECODE_H */

@@ -1,0 +1,163 @@
+"""The C ABI on the host: the library loads, exports every declared entry point,
+and rejects bad arguments before touching the GPU.
+
+No call here reaches a kernel launch: every call either fails validation or
+is a host-only query with an explicit CU count / split count.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from decode_attention_paged_amd import _lib
+from decode_attention_paged_amd._lib import PaShape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa_decode.h")
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails before any use
+NULL = ctypes.c_void_p(0)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libpa_decode.so not built")
+    return _lib.load()
+
+
+def shape(**kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=8, head_dim=128, head_dim_v=128,
+                block_size=16, max_blocks_per_seq=8, num_blocks=64, max_context_len=100,
+                scale=128 ** -0.5, dtype=_lib.PA_BF16)
+    base.update(kw)
+    return PaShape(**base)
+
+
+def decode(lib, s, *, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, ctx=FAKE, splits=1, out=FAKE, ws=NULL,
+           ws_bytes=0):
+    return lib.pa_decode(ctypes.byref(s) if s is not None else None, q, k, v, bt, ctx, splits, out,
+                         NULL, ws, ws_bytes, NULL)
+
+
+def test_header_and_binding_agree():
+    assert header_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert _lib.status_string(code)
+    assert _lib.status_string(99) == "unknown status"
+    assert lib.pa_version() >= 100
+
+
+def test_shape_struct_size_matches_header():
+    # 10 int32 fields + one float, no padding
+    assert ctypes.sizeof(PaShape) == 11 * 4
+
+
+@pytest.mark.parametrize("field,value", [
+    ("batch", 0), ("num_q_heads", 0), ("num_kv_heads", 0), ("head_dim", -1), ("block_size", 0),
+    ("max_blocks_per_seq", 0), ("num_blocks", 0), ("max_context_len", -5), ("dtype", 7),
+    ("num_kv_heads", 3),            # 8 % 3 != 0
+    ("max_context_len", 8 * 16 + 1),  # longer than the block table allows
+    ("scale", math.inf),
+])
+def test_invalid_shapes(lib, field, value):
+    assert decode(lib, shape(**{field: value})) == _lib.PA_ERR_INVALID
+
+
+def test_null_shape_and_pointers(lib):
+    assert decode(lib, None) == _lib.PA_ERR_INVALID
+    s = shape()
+    for kw in ("q", "k", "v", "bt", "ctx", "out"):
+        assert decode(lib, s, **{kw: NULL}) == _lib.PA_ERR_INVALID, kw
+
+
+@pytest.mark.parametrize("kw", [
+    dict(head_dim=96, head_dim_v=96),                   # no kernel for D = 96
+    dict(head_dim=128, head_dim_v=64),                  # Dv != D for MHA
+    dict(block_size=8, max_context_len=50),             # no kernel for bs = 8
+])
+def test_unsupported(lib, kw):
+    assert decode(lib, shape(**kw)) == _lib.PA_ERR_UNSUPPORTED
+
+
+def test_workspace_checks(lib):
+    s = shape()
+    assert decode(lib, s, splits=4) == _lib.PA_ERR_WORKSPACE
+    need = lib.pa_decode_workspace_size(ctypes.byref(s), 4, 0)
+    rows = 2 * 8 * 4
+    assert need == (-(-rows * 128 * 4 // 256) * 256) + (-(-rows * 4 // 256) * 256)
+    assert decode(lib, s, splits=4, ws=FAKE, ws_bytes=need - 1) == _lib.PA_ERR_WORKSPACE
+    # one split needs no workspace
+    assert lib.pa_decode_workspace_size(ctypes.byref(s), 1, 0) == 0
+
+
+def test_mla_checks(lib):
+    s = shape(num_q_heads=128, num_kv_heads=1, head_dim=576, head_dim_v=512, block_size=64,
+              max_context_len=300, max_blocks_per_seq=8)
+    mla = lambda sh, **kw: lib.pa_decode_mla(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, 1,
+                                             kw.get("out", FAKE), NULL, NULL, 0, NULL)
+    assert mla(shape(num_q_heads=128, num_kv_heads=2, head_dim=576, head_dim_v=512,
+                     block_size=64, max_context_len=300, max_blocks_per_seq=8)) == _lib.PA_ERR_INVALID
+    assert mla(shape(num_q_heads=120, num_kv_heads=1, head_dim=576, head_dim_v=512,
+                     block_size=64, max_context_len=300, max_blocks_per_seq=8)) == _lib.PA_ERR_UNSUPPORTED
+    assert mla(s, out=NULL) == _lib.PA_ERR_INVALID
+    assert lib.pa_decode_mla(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 3, FAKE, NULL, NULL, 0,
+                             NULL) == _lib.PA_ERR_WORKSPACE
+
+
+def test_reduce_checks(lib):
+    s = shape()
+    assert lib.pa_reduce(ctypes.byref(s), NULL, 4, 0, FAKE, 1 << 20, FAKE, NULL, NULL) == _lib.PA_ERR_INVALID
+    assert lib.pa_reduce(ctypes.byref(s), FAKE, 4, 0, NULL, 0, FAKE, NULL, NULL) == _lib.PA_ERR_WORKSPACE
+    # a single split has nothing to reduce
+    assert lib.pa_reduce(ctypes.byref(s), FAKE, 1, 0, NULL, 0, FAKE, NULL, NULL) == _lib.PA_OK
+
+
+def _splits(lib, mla=False, **kw):
+    s = shape(**kw)
+    return lib.pa_choose_num_splits(ctypes.byref(s), 256, int(mla))
+
+
+def test_split_heuristic_fills_the_gpu(lib):
+    # long context, 8 KV heads, one sequence: must split
+    S = _splits(lib, batch=1, num_q_heads=32, num_kv_heads=8, max_context_len=131072,
+                max_blocks_per_seq=8192, num_blocks=8192)
+    assert 64 <= S <= 8192
+    assert S * 8 >= 256                        # at least one workgroup per CU
+    # Llama-style MHA batch of 16 x 32 heads, contexts up to 4096
+    S2 = _splits(lib, batch=16, num_q_heads=32, num_kv_heads=32, max_context_len=4096,
+                 max_blocks_per_seq=256, num_blocks=65536)
+    assert 2 <= S2 <= 256
+    # ragged GQA batch of 64 up to 30011 tokens
+    S3 = _splits(lib, batch=64, num_q_heads=64, num_kv_heads=8, max_context_len=30011,
+                 max_blocks_per_seq=2048, num_blocks=65536)
+    assert S3 * 64 * 8 <= 64 * 256 and S3 >= 8
+    # MLA: 32 sequences of 8192 tokens, 64-token pages
+    S4 = _splits(lib, mla=True, batch=32, num_q_heads=128, num_kv_heads=1, head_dim=576,
+                 head_dim_v=512, block_size=64, max_context_len=8192, max_blocks_per_seq=128,
+                 num_blocks=4096)
+    assert S4 * 32 >= 256 and S4 <= 128
+    # a single page never splits
+    assert _splits(lib, max_context_len=16) == 1
+    assert _splits(lib, max_context_len=0) == 1
+
+
+def test_split_heuristic_invalid_shape(lib):
+    s = shape(batch=0)
+    assert lib.pa_choose_num_splits(ctypes.byref(s), 256, 0) == 0

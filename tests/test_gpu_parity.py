@@ -1,0 +1,329 @@
+"""HIP path vs the float64 oracle, element by element, on seeded inputs.
+
+Tolerances (written here, from the required bars):
+  float32 inputs: max |out - ref| <= 1e-5, max |lse - ref| <= 1e-5
+  bf16 inputs:    max |out - ref| <= 2e-2 and ||out - ref||_2 / ||ref||_2 <= 1e-2;
+                  max |lse - ref| <= 1e-3
+Unused pool pages and the slots past each context are NaN, so any read of
+memory the method must not read shows up as NaN in the output.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import decode_attention_paged_amd as pa
+from workloads import make_config, make_paged_inputs
+from workloads.device import from_device, to_device
+
+pytestmark = pytest.mark.gpu
+
+TOL = {
+    "f32": dict(max_abs=1e-5, rel_l2=None, lse=1e-5),
+    "bf16": dict(max_abs=2e-2, rel_l2=1e-2, lse=1e-3),
+}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run(inp, t=None, num_splits=0, poison=True):
+    if t is None:
+        t = to_device(inp, "cuda", poison)
+    if inp.kind == "mla":
+        out, lse = pa.decode_mla(t["q"], t["kv_cache"], t["block_table"], t["context_lens"],
+                                 max_context_len=inp.max_context_len, scale=inp.scale,
+                                 head_dim_v=inp.head_dim_v, num_splits=num_splits)
+    else:
+        out, lse = pa.decode(t["q"], t["k_cache"], t["v_cache"], t["block_table"],
+                             t["context_lens"], max_context_len=inp.max_context_len,
+                             scale=inp.scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def compare(inp, out, lse, ref_out, ref_lse, what=""):
+    o = from_device(out)
+    l = lse.detach().cpu().numpy().astype(np.float64)
+    sel = ~np.isnan(ref_lse)           # sampled rows only (others are NaN in the reference)
+    tol = TOL[inp.dtype]
+    ro, rl = ref_out[sel], ref_lse[sel]
+    go, gl = o[sel], l[sel]
+    assert np.isfinite(go).all(), f"{what}: non-finite outputs"
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(gl), fin), f"{what}: lse finiteness differs"
+    assert np.array_equal(gl[~fin], rl[~fin])
+    err = np.abs(go - ro)
+    max_abs = float(err.max()) if err.size else 0.0
+    denom = float(np.linalg.norm(ro))
+    rel = float(np.linalg.norm(go - ro) / denom) if denom > 0 else float(np.linalg.norm(go))
+    lerr = float(np.abs(gl[fin] - rl[fin]).max()) if fin.any() else 0.0
+    say(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} lse_err={lerr:.3e} rows={int(sel.sum())}")
+    assert max_abs <= tol["max_abs"], f"{what}: max abs {max_abs}"
+    if tol["rel_l2"] is not None:
+        assert rel <= tol["rel_l2"], f"{what}: rel l2 {rel}"
+    assert lerr <= tol["lse"], f"{what}: lse err {lerr}"
+
+
+# ----------------------------------------------------------------------------------------------
+# The tiny fp32 workload, both required split counts
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("num_splits", [1, 4, 0])
+def test_tiny_mha_f32(num_splits):
+    inp = make_config("tiny_mha_f32")
+    say(f"tiny_mha_f32 S={num_splits}")
+    ref_out, ref_lse = oracle.decode_inputs(inp)
+    out, lse = run(inp, num_splits=num_splits)
+    compare(inp, out, lse, ref_out, ref_lse, f"tiny S={num_splits}")
+
+
+# ----------------------------------------------------------------------------------------------
+# Small shapes, every output compared: several tiles, ragged tails, many split counts
+# ----------------------------------------------------------------------------------------------
+
+SMALL = {
+    "mha_bf16_d128": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=4, num_kv_heads=4,
+                          head_dim=128, block_size=16, context_lens=[1, 37, 300], num_blocks=64),
+    "mha_bf16_d64": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=3, num_kv_heads=3,
+                         head_dim=64, block_size=16, context_lens=[129, 16], num_blocks=40),
+    "mha_bf16_bs32": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=2, num_kv_heads=2,
+                          head_dim=128, block_size=32, context_lens=[100, 31], num_blocks=20),
+    "mha_f32_d128": dict(kind="mha", dtype="f32", batch=2, num_q_heads=2, num_kv_heads=2,
+                         head_dim=128, block_size=16, context_lens=[77, 160], num_blocks=30),
+    "mha_f32_d64_bs32": dict(kind="mha", dtype="f32", batch=2, num_q_heads=4, num_kv_heads=4,
+                             head_dim=64, block_size=32, context_lens=[65, 3], num_blocks=10),
+    "gqa_f32_g4": dict(kind="mha", dtype="f32", batch=2, num_q_heads=8, num_kv_heads=2,
+                       head_dim=64, block_size=16, context_lens=[50, 200], num_blocks=30),
+    "gqa_bf16_g4": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=8, num_kv_heads=2,
+                        head_dim=128, block_size=16, context_lens=[17, 333], num_blocks=40),
+    "gqa_bf16_g8": dict(kind="mha", dtype="bf16", batch=4, num_q_heads=16, num_kv_heads=2,
+                        head_dim=128, block_size=16, context_lens=[1, 16, 1000, 47], num_blocks=90),
+    "gqa_bf16_g16": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=16, num_kv_heads=1,
+                         head_dim=128, block_size=16, context_lens=[15, 515], num_blocks=40),
+    "gqa_bf16_g2": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=6, num_kv_heads=3,
+                        head_dim=128, block_size=16, context_lens=[33, 95], num_blocks=20),
+    "mla_bf16_h16": dict(kind="mla", dtype="bf16", batch=2, num_q_heads=16, num_kv_heads=1,
+                         head_dim=576, head_dim_v=512, block_size=64, context_lens=[1, 700],
+                         num_blocks=20, scale=192 ** -0.5),
+    "mla_bf16_h128": dict(kind="mla", dtype="bf16", batch=2, num_q_heads=128, num_kv_heads=1,
+                          head_dim=576, head_dim_v=512, block_size=64, context_lens=[65, 300],
+                          num_blocks=12, scale=192 ** -0.5),
+    "mla_bf16_h64": dict(kind="mla", dtype="bf16", batch=1, num_q_heads=64, num_kv_heads=1,
+                         head_dim=576, head_dim_v=512, block_size=64, context_lens=[129],
+                         num_blocks=5, scale=192 ** -0.5),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_shapes(name):
+    inp = make_paged_inputs(name=name, seed=100 + sorted(SMALL).index(name), **SMALL[name])
+    ref_out, ref_lse = oracle.decode_inputs(inp)
+    t = to_device(inp, "cuda", poison=True)
+    P = -(-inp.max_context_len // inp.block_size)
+    for S in [0, 1, 2, 3, 7, P + 5]:
+        say(f"{name} S={S}")
+        out, lse = run(inp, t, num_splits=S)
+        compare(inp, out, lse, ref_out, ref_lse, f"{name} S={S}")
+
+
+# ----------------------------------------------------------------------------------------------
+# Full-size workloads in the launch configuration the benchmark times (heuristic split count):
+# sampled (sequence, head) rows against the oracle, every output finite.
+# ----------------------------------------------------------------------------------------------
+
+def sample_pairs(inp, n, seed):
+    rng = np.random.default_rng(seed)
+    pairs = {(int(rng.integers(inp.batch)), int(rng.integers(inp.num_q_heads))) for _ in range(n)}
+    # always include the longest and the shortest sequence
+    for b in (int(np.argmax(inp.context_lens)), int(np.argmin(inp.context_lens))):
+        pairs.add((b, 0))
+        pairs.add((b, inp.num_q_heads - 1))
+    return sorted(pairs)
+
+
+@pytest.mark.parametrize("name", ["llama_mha_bf16", "long_gqa_bf16", "ragged_gqa_bf16", "mla_bf16"])
+def test_full_size_sampled(name):
+    say(f"full {name}: drawing inputs")
+    inp = make_config(name)
+    pairs = sample_pairs(inp, 24, 7)
+    ref_out, ref_lse = oracle.decode_inputs(inp, heads=pairs)
+    t = to_device(inp, "cuda", poison=True)
+    say(f"full {name}: running")
+    out, lse = run(inp, t, num_splits=0)
+    assert torch.isfinite(out.float()).all().item(), "non-finite output"
+    compare(inp, out, lse, ref_out, ref_lse, f"{name} sampled")
+    del t
+
+
+# ----------------------------------------------------------------------------------------------
+# Properties that hold at any size
+# ----------------------------------------------------------------------------------------------
+
+PROP = dict(kind="mha", dtype="bf16", batch=3, num_q_heads=16, num_kv_heads=2, head_dim=128,
+            block_size=16, context_lens=[70, 1, 260], num_blocks=60)
+PROP_MHA = dict(PROP, num_kv_heads=16)
+PROP_MLA = dict(kind="mla", dtype="bf16", batch=2, num_q_heads=32, num_kv_heads=1, head_dim=576,
+                head_dim_v=512, block_size=64, context_lens=[200, 1], num_blocks=10,
+                scale=192 ** -0.5)
+
+
+def _permuted(t, inp, seed):
+    """Same logical KV with physical pages relabelled by a permutation."""
+    perm = torch.from_numpy(np.random.default_rng(seed).permutation(inp.num_blocks)).cuda()
+    u = dict(t)
+    for key in ("k_cache", "v_cache", "kv_cache"):
+        if key in t:
+            pool = torch.empty_like(t[key])
+            pool[perm] = t[key]
+            u[key] = pool
+    bt = t["block_table"].long()
+    u["block_table"] = torch.where(bt >= 0, perm[bt.clamp(min=0)], bt).to(torch.int32)
+    return u
+
+
+@pytest.mark.parametrize("spec", [PROP, PROP_MHA, PROP_MLA], ids=["gqa", "mha", "mla"])
+@pytest.mark.parametrize("S", [0, 1, 5])
+def test_page_permutation_bitwise(spec, S):
+    inp = make_paged_inputs(seed=11, **spec)
+    t = to_device(inp, "cuda")
+    o1, l1 = run(inp, t, num_splits=S)
+    o2, l2 = run(inp, _permuted(t, inp, 3), num_splits=S)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("spec", [PROP, PROP_MHA, PROP_MLA], ids=["gqa", "mha", "mla"])
+def test_determinism_and_batch_independence(spec):
+    inp = make_paged_inputs(seed=12, **spec)
+    t = to_device(inp, "cuda")
+    o1, l1 = run(inp, t, num_splits=4)
+    o2, l2 = run(inp, t, num_splits=4)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "run-to-run difference"
+    # each sequence alone (same max_context_len so the split plan is the same)
+    for b in range(inp.batch):
+        u = {k: v for k, v in t.items()}
+        u["q"] = t["q"][b:b + 1].contiguous()
+        u["block_table"] = t["block_table"][b:b + 1].contiguous()
+        u["context_lens"] = t["context_lens"][b:b + 1].contiguous()
+        one = make_paged_inputs(seed=12, values=False, **spec)
+        one.batch = 1
+        one.context_lens = inp.context_lens[b:b + 1]
+        one.block_table = inp.block_table[b:b + 1]
+        ob, lb = run(_with_max(one, inp.max_context_len), u, num_splits=4)
+        assert torch.equal(ob[0], o1[b]) and torch.equal(lb[0], l1[b]), f"sequence {b}"
+
+
+class _with_max:
+    """Workload view that keeps a given max_context_len (same split plan)."""
+
+    def __init__(self, inp, max_ctx):
+        self._inp = inp
+        self.max_context_len = max_ctx
+
+    def __getattr__(self, k):
+        return getattr(self._inp, k)
+
+
+@pytest.mark.parametrize("spec", [PROP, PROP_MHA, PROP_MLA], ids=["gqa", "mha", "mla"])
+def test_context_one_returns_v0_exactly(spec):
+    s = dict(spec, context_lens=[1] * spec["batch"])
+    inp = make_paged_inputs(seed=13, **s)
+    out, lse = run(inp, num_splits=0)
+    o = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    for b in range(inp.batch):
+        row = inp.compact_block_table()[b, 0]
+        for h in range(inp.num_q_heads):
+            if inp.kind == "mla":
+                v0 = inp.c_pages[row, 0, :inp.head_dim_v]
+            else:
+                g = h // (inp.num_q_heads // inp.num_kv_heads)
+                v0 = inp.v_pages[row, g, :, 0]
+            assert np.array_equal(o[b, h], v0), (b, h)
+    ref_out, ref_lse = oracle.decode_inputs(inp)
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() <= 1e-3
+
+
+@pytest.mark.parametrize("spec", [PROP, PROP_MHA, PROP_MLA], ids=["gqa", "mha", "mla"])
+def test_identical_keys_give_mean_of_values(spec):
+    """Equal keys weight every token equally: out is the mean of the values.
+
+    For the latent variant keys and values are the same rows, so equal keys
+    mean equal rows and the output is that row's value part.
+    """
+    inp = make_paged_inputs(seed=14, **spec)
+    b = 2 if inp.batch > 2 else 0
+    bt = inp.compact_block_table()
+    n = int(inp.context_lens[b])
+    if inp.kind == "mla":
+        inp.c_pages[:] = inp.c_pages[bt[b, 0], 0, :][None, None, :]
+        want = np.broadcast_to(oracle.as_f64(inp.c_pages[0, 0, :inp.head_dim_v], "bf16"),
+                               (inp.num_q_heads, inp.head_dim_v))
+    else:
+        inp.k_pages[:] = inp.k_pages[bt[b, 0], :, 0, :][None, :, None, :]
+        pages = bt[b, :-(-n // inp.block_size)]
+        vals = oracle.as_f64(inp.v_pages[pages], "bf16")            # [p][Hkv][D][bs]
+        vals = vals.transpose(0, 3, 1, 2).reshape(-1, inp.num_kv_heads, inp.head_dim)[:n]
+        mean = vals.mean(axis=0)
+        G = inp.num_q_heads // inp.num_kv_heads
+        want = np.stack([mean[h // G] for h in range(inp.num_q_heads)])
+    ref_out, ref_lse = oracle.decode_inputs(inp)
+    out, lse = run(inp, num_splits=3)
+    compare(inp, out, lse, ref_out, ref_lse, "identical keys")
+    assert np.abs(from_device(out)[b] - want).max() <= 2e-2
+
+
+@pytest.mark.parametrize("spec", [PROP, PROP_MHA, PROP_MLA], ids=["gqa", "mha", "mla"])
+def test_empty_context(spec):
+    s = dict(spec, context_lens=[0] + list(spec["context_lens"][1:]))
+    inp = make_paged_inputs(seed=15, **s)
+    ref_out, ref_lse = oracle.decode_inputs(inp)
+    for S in (1, 4):
+        out, lse = run(inp, num_splits=S)
+        assert (out[0].float() == 0).all().item()
+        assert torch.isinf(lse[0]).all().item() and (lse[0] < 0).all().item()
+        compare(inp, out, lse, ref_out, ref_lse, f"empty ctx S={S}")
+
+
+@pytest.mark.parametrize("spec", [PROP, PROP_MLA], ids=["gqa", "mla"])
+def test_partial_then_reduce_equals_decode(spec):
+    inp = make_paged_inputs(seed=16, **spec)
+    t = to_device(inp, "cuda")
+    S = 3
+    o1, l1 = run(inp, t, num_splits=S)
+    mla = inp.kind == "mla"
+    shape = pa.make_shape(batch=inp.batch, num_q_heads=inp.num_q_heads,
+                          num_kv_heads=inp.num_kv_heads, head_dim=inp.head_dim,
+                          head_dim_v=inp.head_dim_v, block_size=inp.block_size,
+                          max_blocks_per_seq=inp.max_blocks_per_seq, num_blocks=inp.num_blocks,
+                          max_context_len=inp.max_context_len, scale=inp.scale,
+                          dtype=torch.bfloat16)
+    ws = torch.empty(pa.workspace_size(shape, S, mla), dtype=torch.uint8, device="cuda")
+    o2 = torch.empty_like(o1)
+    l2 = torch.empty_like(l1)
+    if mla:
+        pa.decode_mla_partial(shape, t["q"], t["kv_cache"], t["block_table"], t["context_lens"],
+                              S, o2, l2, ws)
+    else:
+        pa.decode_partial(shape, t["q"], t["k_cache"], t["v_cache"], t["block_table"],
+                          t["context_lens"], S, o2, l2, ws)
+    pa.reduce(shape, t["context_lens"], S, ws, o2, l2, mla=mla)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_bf16_output_rounding_is_nearest_even():
+    """A one-token context copies v0; with S = 1 and S > 1 alike the bits survive."""
+    inp = make_paged_inputs(seed=17, **dict(PROP_MHA, context_lens=[1, 1, 1]))
+    for S in (1, 2):
+        out, _ = run(inp, num_splits=S)
+        o = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        bt = inp.compact_block_table()
+        for b in range(3):
+            assert np.array_equal(o[b, :, :], inp.v_pages[bt[b, 0], :, :, 0])
