@@ -1,0 +1,365 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--only]
+
+One step = one decode-attention call over a batch: the split-KV partial
+kernel and the log-sum-exp reduction (pa_decode_partial + pa_reduce, which is
+exactly what pa_decode launches).  Inputs are seeded synthetic workloads that
+are already resident in HBM when the timed region starts.  The partial
+kernel, the dominant one, is also timed on its own with HIP events on the
+stream it is launched on; its algorithmic KV-read bytes per launch divided by
+that average duration give the achieved HBM bandwidth reported against the
+8 TB/s MI355X peak.
+
+Prints ONE JSON line on stdout.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attn tokens/s + achieved KV-read HBM GB/s (% of MI355X peak), 1 GPU"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+DEFAULT_CONFIG = "llama_mha_bf16"
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "decode_attention_paged_amd", "csrc")
+
+KERNEL_OF = {"mha": "pa_mha.hip", "gqa": "pa_gqa.hip", "mla": "pa_mla.hip"}
+
+
+def kernel_family(inp) -> str:
+    if inp.kind == "mla":
+        return "mla"
+    if inp.dtype == "bf16" and inp.num_q_heads != inp.num_kv_heads and inp.head_dim == 128 \
+            and inp.block_size == 16 and inp.num_q_heads // inp.num_kv_heads <= 16:
+        return "gqa"
+    return "mha"
+
+
+def kernel_source_hash(family: str) -> str:
+    h = hashlib.sha256()
+    for f in (KERNEL_OF[family], "pa_device.h", "pa_launch.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, family: str):
+    """HBM bytes per launch from the committed counter summary, if still current.
+
+    The summary (profiles/pmc_<workload>.md) holds lines
+    `kernel_source_sha256: <hash>` and `hbm_bytes_per_launch: <bytes>`; the
+    figure is used only when the hash matches today's kernel sources.
+    """
+    path = os.path.join(PROFILES, f"pmc_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    mh = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    mb = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not mh or not mb or mh.group(1) != kernel_source_hash(family):
+        return None
+    return float(mb.group(1))
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--only", action="store_true",
+                    help="time only --config (no other workloads, no CPU baseline)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration under rocprofv3)")
+    return ap.parse_args()
+
+
+class Case:
+    """One workload on the device with prebound library calls."""
+
+    def __init__(self, name: str):
+        import torch
+
+        import decode_attention_paged_amd as pa
+        from decode_attention_paged_amd import _lib
+        from workloads import make_config
+        from workloads.device import to_device, torch_dtype
+
+        self.name = name
+        self.inp = inp = make_config(name, poison=False)
+        self.t = to_device(inp, "cuda", poison=False)
+        self.mla = inp.kind == "mla"
+        self.family = kernel_family(inp)
+        self.shape = pa.make_shape(
+            batch=inp.batch, num_q_heads=inp.num_q_heads, num_kv_heads=inp.num_kv_heads,
+            head_dim=inp.head_dim, head_dim_v=inp.head_dim_v, block_size=inp.block_size,
+            max_blocks_per_seq=inp.max_blocks_per_seq, num_blocks=inp.num_blocks,
+            max_context_len=inp.max_context_len, scale=inp.scale, dtype=torch_dtype(inp.dtype))
+        self.S = pa.choose_num_splits(self.shape, 0, self.mla)
+        nbytes = pa.workspace_size(self.shape, self.S, self.mla)
+        # zero-filled: the fused reduction's arrival counters start at 0
+        self.ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+        self.out = torch.empty((inp.batch, inp.num_q_heads, inp.head_dim_v),
+                               dtype=torch_dtype(inp.dtype), device="cuda")
+        self.lse = torch.empty((inp.batch, inp.num_q_heads), dtype=torch.float32, device="cuda")
+        lib = _lib.load()
+        P = ctypes.c_void_p
+        stream = P(torch.cuda.current_stream().cuda_stream)
+        sh = ctypes.byref(self.shape)
+        t = self.t
+        ws, wsb = P(self.ws.data_ptr()), self.ws.numel()
+        out, lse = P(self.out.data_ptr()), P(self.lse.data_ptr())
+        bt, ctx = P(t["block_table"].data_ptr()), P(t["context_lens"].data_ptr())
+        q = P(t["q"].data_ptr())
+        # MHA/GQA: pa_decode is one launch (the last workgroup of each unit
+        # merges the splits).  MLA: pa_decode_mla launches the partial kernel
+        # and the reduction; they are called here one by one so that each can
+        # be timed.
+        self.fused = not self.mla
+        if self.mla:
+            kv = P(t["kv_cache"].data_ptr())
+            self._partial = (lib.pa_decode_mla_partial,
+                             (sh, q, kv, bt, ctx, self.S, out, lse, ws, wsb, stream))
+            self._reduce = (lib.pa_reduce,
+                            (sh, ctx, self.S, int(self.mla), ws, wsb, out, lse, stream))
+        else:
+            k, v = P(t["k_cache"].data_ptr()), P(t["v_cache"].data_ptr())
+            self._partial = (lib.pa_decode,
+                             (sh, q, k, v, bt, ctx, self.S, out, lse, ws, wsb, stream))
+            self._reduce = None
+        self.kv_bytes = inp.kv_bytes_read()
+        self.tokens = int(inp.context_lens.astype("int64").sum())
+
+    def partial(self):
+        fn, args = self._partial
+        st = fn(*args)
+        if st != 0:
+            raise RuntimeError(f"partial step failed with status {st}")
+
+    def reduce(self):
+        if self._reduce is None:
+            return
+        fn, args = self._reduce
+        st = fn(*args)
+        if st != 0:
+            raise RuntimeError(f"reduce step failed with status {st}")
+
+    def step(self):
+        self.partial()
+        self.reduce()
+
+    def flops(self) -> float:
+        i = self.inp
+        toks = self.tokens
+        return 2.0 * toks * i.num_q_heads * (i.head_dim + i.head_dim_v)
+
+    def time(self, steps: int, warmup: int):
+        """Time `steps` whole steps; partial and reduce timed with events."""
+        import torch
+
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e0, e1, e2 in evs:
+            e0.record()
+            self.partial()
+            e1.record()
+            self.reduce()
+            e2.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        part = [a.elapsed_time(b) for a, b, _ in evs]
+        red = [b.elapsed_time(c) for _, b, c in evs]
+        part.sort()
+        return dict(
+            ms_per_step=wall * 1e3 / steps,
+            partial_ms=sum(part) / len(part),
+            partial_ms_median=part[len(part) // 2],
+            reduce_ms=sum(red) / len(red),
+        )
+
+    def summary(self, r):
+        frac = (self.kv_bytes / (r["partial_ms"] * 1e-3) / 1e9) / PEAK_HBM_GBS
+        d = dict(
+            workload=self.inp.meta.get("desc", self.name),
+            num_splits=self.S,
+            kernel=self.family,
+            ms_per_step=round(r["ms_per_step"], 5),
+            tokens_per_s=round(self.inp.batch / (r["ms_per_step"] * 1e-3), 1),
+            partial_ms=round(r["partial_ms"], 5),
+            reduce_ms=round(r["reduce_ms"], 5),
+            kv_bytes=self.kv_bytes,
+            kv_gbps_partial=round(self.kv_bytes / (r["partial_ms"] * 1e-3) / 1e9, 1),
+            kv_gbps_step=round(self.kv_bytes / (r["ms_per_step"] * 1e-3) / 1e9, 1),
+            frac_of_peak_partial=round(frac, 4),
+        )
+        if self.mla:
+            d["mfma_tflops_partial"] = round(self.flops() / (r["partial_ms"] * 1e-3) / 1e12, 1)
+            d["mfma_frac_of_bf16_peak"] = round(d["mfma_tflops_partial"] / PEAK_BF16_TFLOPS, 4)
+        return d
+
+    def free(self):
+        import torch
+
+        self.t.clear()
+        del self.ws, self.out, self.lse
+        torch.cuda.empty_cache()
+
+
+def cpu_baseline(inp, min_s: float = 10.0, max_s: float = 30.0):
+    """The float64 oracle, as it stands, on a bounded sample of the workload.
+
+    Sequences of the batch are decoded one at a time (all heads), cycling
+    through the batch until at least `min_s` seconds of CPU work are done.
+    """
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    bt = inp.compact_block_table()
+    done, toks = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        b = done % inp.batch
+        one_q = inp.q[b:b + 1]
+        if inp.kind == "mla":
+            oracle.paged_decode_mla(one_q, inp.c_pages, bt[b:b + 1], inp.context_lens[b:b + 1],
+                                    inp.scale, dv=inp.head_dim_v, dtype=inp.dtype)
+        else:
+            oracle.paged_decode(one_q, inp.k_pages, inp.v_pages, bt[b:b + 1],
+                                inp.context_lens[b:b + 1], inp.scale, dtype=inp.dtype)
+        done += 1
+        toks += int(inp.context_lens[b])
+        el = time.perf_counter() - t0
+        if el >= min_s or el >= max_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    bytes_per_tok = inp.kv_bytes_read() / max(1, int(inp.context_lens.sum()))
+    return {
+        "value": round(done / dt, 3),
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} sequence decodes (cycling the batch of {inp.batch}; all "
+                  f"{inp.num_q_heads} heads; {toks} context tokens) in {dt:.1f} s, float64 NumPy",
+        "kv_gbps": round(toks * bytes_per_tok / dt / 1e9, 4),
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from workloads import CONFIG_ORDER
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    main_case = Case(args.config)
+    r = main_case.time(args.steps, args.warmup)
+    main_sum = main_case.summary(r)
+    inp = main_case.inp
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    traffic = load_traffic(args.config, main_case.family)
+    achieved = main_case.kv_bytes / (r["partial_ms"] * 1e-3) / 1e9
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": PEAK_HBM_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / PEAK_HBM_GBS, 4),
+        "traffic": traffic,
+        "kernel": (f"{main_case.family} split-KV kernel with fused reduction" if main_case.fused
+                   else f"{main_case.family} partial kernel"),
+        "algorithmic_bytes_per_launch": main_case.kv_bytes,
+        "avg_launch_ms": round(r["partial_ms"], 5),
+    }
+    main_case.free()
+
+    per_config = {}
+    if not args.only:
+        for name in CONFIG_ORDER:
+            if name == args.config:
+                per_config[name] = main_sum
+                continue
+            c = Case(name)
+            rr = c.time(max(20, args.steps // 4), max(5, args.warmup // 2))
+            per_config[name] = c.summary(rr)
+            c.free()
+            del c
+
+    cpu = None
+    if not args.only and not args.no_cpu:
+        cpu = cpu_baseline(inp)
+
+    line = {
+        "metric": METRIC,
+        "value": round(inp.batch / (r["ms_per_step"] * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, shuffled page tables; see workloads/)",
+        "config": {
+            "workload": f"{args.config}: {inp.meta.get('desc', '')}",
+            "batch": inp.batch,
+            "num_q_heads": inp.num_q_heads,
+            "num_kv_heads": inp.num_kv_heads,
+            "head_dim": inp.head_dim,
+            "block_size": inp.block_size,
+            "context_tokens": main_case.tokens,
+            "num_splits": main_case.S,
+            "parallelism": "single GPU",
+        },
+        "kv_gbps_step": main_sum["kv_gbps_step"],
+        "kv_frac_of_peak_step": round(main_sum["kv_gbps_step"] / PEAK_HBM_GBS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_config": per_config,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

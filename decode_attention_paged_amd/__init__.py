@@ -24,7 +24,8 @@ from ._lib import PaError, PaShape  # noqa: F401
 
 __all__ = [
     "decode", "decode_mla", "decode_partial", "decode_mla_partial", "reduce",
-    "choose_num_splits", "workspace_size", "make_shape", "PaError", "library_path",
+    "choose_num_splits", "workspace_size", "workspace_init", "make_shape", "PaError",
+    "library_path",
 ]
 
 _DTYPES = {torch.float32: _lib.PA_F32, torch.bfloat16: _lib.PA_BF16}
@@ -141,7 +142,8 @@ def _outputs(shape, q, out, lse, workspace, num_splits, mla):
         _need(lse, "lse", torch.float32, 2, q.device)
     need = workspace_size(shape, num_splits, mla)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        # zero-filled: the fused reduction's arrival counters must start at 0
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     return out, (None if lse is False else lse), workspace
 
 
@@ -173,6 +175,13 @@ def decode_mla(q, kv_cache, block_table, context_lens, *, max_context_len=None, 
                                    _ptr(ws), _nbytes(ws), _stream(stream))
     _lib.check(st, "pa_decode_mla")
     return out, lse
+
+
+def workspace_init(shape: PaShape, workspace, num_splits: int = 0, mla: bool = False, stream=None):
+    """Zero the workspace's arrival counters (needed once per new workspace)."""
+    st = _lib.load().pa_workspace_init(ctypes.byref(shape), int(num_splits), int(mla),
+                                       _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _lib.check(st, "pa_workspace_init")
 
 
 def decode_partial(shape: PaShape, q, k_cache, v_cache, block_table, context_lens, num_splits,

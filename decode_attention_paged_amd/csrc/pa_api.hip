@@ -11,6 +11,9 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxDevices = 64;
+constexpr int kMaxSplits = 65535;          // grid y limit
+constexpr double kSplitBytesValu = 128.0 * 1024.0;   // KV bytes per workgroup, VALU kernel
+constexpr double kSplitBytesMfma = 1024.0 * 1024.0;  // KV bytes per workgroup, MFMA kernel
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -34,6 +37,7 @@ Kernel pick_kernel(const pa_shape& s, bool mla) {
 // Shape checks that need no pointers (host-only).
 pa_status check_shape(const pa_shape* s, bool mla) {
   if (!s) return PA_ERR_INVALID;
+  if (s->batch > 65535) return PA_ERR_UNSUPPORTED;   // grid z limit
   if (s->batch < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1 || s->head_dim < 1 ||
       s->head_dim_v < 1 || s->block_size < 1 || s->max_blocks_per_seq < 1 || s->num_blocks < 1 ||
       s->max_context_len < 0)
@@ -69,40 +73,54 @@ int device_cus() {
   return cus;
 }
 
-// Split plan (host only): prefer many small splits so that ragged batches
-// balance over the CUs, but keep each split long enough that its float32
-// partial (written once, read once by the reduction) stays a few percent of
-// the KV bytes it summarises, and cap the grid.
+// Split plan (host only).  Each split is a fixed number of pages c, so
+// ragged batches use fewer splits for shorter sequences (see header).  Chosen
+// from measurements on MI355X (bf16, 128-dim heads, 16-token pages):
+//  * a split should carry a fixed amount of KV per workgroup: ~128 KiB for
+//    the VALU kernel (one head per workgroup, 4 workgroups per CU), ~1 MiB for
+//    the MFMA kernel (a whole head group, 2 workgroups per CU).  Longer splits
+//    leave a long tail on ragged batches; shorter ones pay each workgroup's
+//    fixed prologue/epilogue more often;
+//  * the grid must still hold at least one workgroup per CU if every sequence
+//    were as long as the longest;
+//  * each split's float32 partial (written, then read by the merge) should
+//    stay a few percent of the KV bytes it summarises.
 int heuristic_splits(const pa_shape& s, int cus, bool mla) {
   const int P = max_pages(s);
   if (P <= 1) return 1;
+  if (cus <= 0) cus = 256;
   const Kernel k = pick_kernel(s, mla);
   const int esz = s.dtype == PA_BF16 ? 2 : 4;
+  long S;
   if (k == Kernel::MlaMfma) {
     // one workgroup per (sequence, split) holds every head: fill the CUs once
-    const int units = s.batch;
-    int S = (cus + units - 1) / units;
-    return S < 1 ? 1 : (S > P ? P : S);
-  }
-  int units, heads_per_wg;
-  if (k == Kernel::GqaMfma) {
-    units = s.batch * s.num_kv_heads;
-    heads_per_wg = s.num_q_heads / s.num_kv_heads;
+    S = (cus + s.batch - 1) / s.batch;
   } else {
-    units = s.batch * s.num_q_heads;
-    heads_per_wg = 1;
+    long units;
+    int heads_per_wg;
+    double target_bytes;
+    if (k == Kernel::GqaMfma) {
+      units = (long)s.batch * s.num_kv_heads;
+      heads_per_wg = s.num_q_heads / s.num_kv_heads;
+      target_bytes = kSplitBytesMfma;
+    } else {
+      units = (long)s.batch * s.num_q_heads;
+      heads_per_wg = 1;
+      target_bytes = kSplitBytesValu;
+    }
+    const double page_bytes = (double)s.block_size * (s.head_dim + s.head_dim_v) * esz;
+    const double part_bytes = 2.0 * heads_per_wg * (s.head_dim_v + 1) * 4.0;
+    int c_min = (int)std::ceil(part_bytes / (0.03 * page_bytes));
+    if (c_min < 1) c_min = 1;
+    int c = (int)(target_bytes / page_bytes);
+    if (c < c_min) c = c_min;
+    S = (P + c - 1) / c;
+    const long s_fill = (cus + units - 1) / units;
+    if (S < s_fill) S = s_fill;
   }
-  const double page_bytes = (double)s.block_size * (s.head_dim + s.head_dim_v) * esz;
-  const double part_bytes = 2.0 * heads_per_wg * (s.head_dim_v + 1) * 4.0;
-  int c_min = (int)std::ceil(part_bytes / (0.03 * page_bytes));
-  if (c_min < 1) c_min = 1;
-  const long max_wgs = 64L * (cus > 0 ? cus : 256);
-  int c = c_min;
-  if ((long)units * ((P + c - 1) / c) > max_wgs) {
-    c = (int)(((long)P * units + max_wgs - 1) / max_wgs);
-  }
-  int S = (P + c - 1) / c;
-  return S < 1 ? 1 : (S > P ? P : S);
+  if (S > P) S = P;
+  if (S > kMaxSplits) S = kMaxSplits;
+  return S < 1 ? 1 : (int)S;
 }
 
 // Resolve num_splits (<= 0: heuristic), clamp to [1, P].  0 on failure.
@@ -115,14 +133,22 @@ int resolve_splits(const pa_shape& s, int32_t num_splits, bool mla) {
     S = heuristic_splits(s, cus, mla);
   }
   if (S > P) S = P;
+  if (S > kMaxSplits) S = kMaxSplits;
   if (S < 1) S = 1;
   return S;
 }
 
+// Workspace layout (S > 1): o_part f32 [B][Hq][S][Dv] | lse_part f32 [B][Hq][S]
+// | counters i32 [B][Hq], each 256-byte aligned.
+size_t ws_lse_offset(const pa_shape& s, int S) {
+  return align_up((size_t)s.batch * s.num_q_heads * S * s.head_dim_v * sizeof(float));
+}
+size_t ws_counter_offset(const pa_shape& s, int S) {
+  return ws_lse_offset(s, S) + align_up((size_t)s.batch * s.num_q_heads * S * sizeof(float));
+}
 size_t workspace_bytes_for(const pa_shape& s, int S) {
   if (S <= 1) return 0;
-  const size_t rows = (size_t)s.batch * s.num_q_heads * S;
-  return align_up(rows * s.head_dim_v * sizeof(float)) + align_up(rows * sizeof(float));
+  return ws_counter_offset(s, S) + align_up((size_t)s.batch * s.num_q_heads * sizeof(int32_t));
 }
 
 pa::Params make_params(const pa_shape& s, int S, const void* q, const void* k, const void* v,
@@ -150,33 +176,37 @@ pa::Params make_params(const pa_shape& s, int S, const void* q, const void* k, c
   p.scale_log2 = s.scale * 1.4426950408889634f;
   p.final_write = S == 1 ? 1 : 0;
   if (S > 1) {
-    const size_t rows = (size_t)s.batch * s.num_q_heads * S;
     p.o_part = static_cast<float*>(ws);
-    p.lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                          align_up(rows * s.head_dim_v * sizeof(float)));
+    p.lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) + ws_lse_offset(s, S));
+    p.counters = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + ws_counter_offset(s, S));
   }
   return p;
 }
 
+// Launch the partial kernel.  With `fused` (and a kernel that supports it)
+// the last workgroup of every (sequence, head unit) also merges the splits,
+// so no reduction launch is needed; *needs_reduce tells the caller.
 pa_status run_partial(const pa_shape* shape, const void* q, const void* k, const void* v,
                       const int32_t* bt, const int32_t* ctx, int32_t num_splits, void* out,
-                      float* lse, void* ws, size_t ws_bytes, void* stream, bool mla, int* S_out) {
+                      float* lse, void* ws, size_t ws_bytes, void* stream, bool mla, bool fused,
+                      int* S_out, bool* needs_reduce) {
   const pa_status st = check_shape(shape, mla);
   if (st != PA_OK) return st;
   if (!q || !k || (!mla && !v) || !bt || !ctx || !out) return PA_ERR_INVALID;
   // workspace check for an explicit split count needs no device query
   if (num_splits > 0) {
-    const int S = num_splits > max_pages(*shape) ? (max_pages(*shape) > 0 ? max_pages(*shape) : 1)
-                                                 : num_splits;
+    const int S = resolve_splits(*shape, num_splits, mla);
     if (S > 1 && (!ws || ws_bytes < workspace_bytes_for(*shape, S))) return PA_ERR_WORKSPACE;
   }
   const int S = resolve_splits(*shape, num_splits, mla);
   if (S < 1) return PA_ERR_HIP;
   if (S > 1 && (!ws || ws_bytes < workspace_bytes_for(*shape, S))) return PA_ERR_WORKSPACE;
-  const pa::Params p = make_params(*shape, S, q, k, mla ? k : v, bt, ctx, out, lse, ws);
+  pa::Params p = make_params(*shape, S, q, k, mla ? k : v, bt, ctx, out, lse, ws);
+  const Kernel kern = pick_kernel(*shape, mla);
+  p.fused = (fused && S > 1 && kern != Kernel::MlaMfma) ? 1 : 0;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e;
-  switch (pick_kernel(*shape, mla)) {
+  switch (kern) {
     case Kernel::MhaValu: e = pa::launch_mha_valu(p, shape->dtype == PA_BF16, hs); break;
     case Kernel::GqaMfma: e = pa::launch_gqa_mfma(p, hs); break;
     case Kernel::MlaMfma: e = pa::launch_mla_mfma(p, hs); break;
@@ -184,6 +214,7 @@ pa_status run_partial(const pa_shape* shape, const void* q, const void* k, const
   }
   if (e != hipSuccess) return PA_ERR_HIP;
   if (S_out) *S_out = S;
+  if (needs_reduce) *needs_reduce = S > 1 && !p.fused;
   return PA_OK;
 }
 
@@ -228,12 +259,31 @@ size_t pa_decode_workspace_size(const pa_shape* shape, int32_t num_splits, int32
   return workspace_bytes_for(*shape, S);
 }
 
+pa_status pa_workspace_init(const pa_shape* shape, int32_t num_splits, int32_t mla,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  const pa_status st = check_shape(shape, mla != 0);
+  if (st != PA_OK) return st;
+  if (num_splits > 0) {
+    const int S = resolve_splits(*shape, num_splits, mla != 0);
+    if (S <= 1) return PA_OK;
+    if (!workspace || workspace_bytes < workspace_bytes_for(*shape, S)) return PA_ERR_WORKSPACE;
+  }
+  const int S = resolve_splits(*shape, num_splits, mla != 0);
+  if (S < 1) return PA_ERR_HIP;
+  if (S <= 1) return PA_OK;
+  if (!workspace || workspace_bytes < workspace_bytes_for(*shape, S)) return PA_ERR_WORKSPACE;
+  int32_t* cnt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ws_counter_offset(*shape, S));
+  const size_t n = (size_t)shape->batch * shape->num_q_heads;
+  return pa::launch_zero_i32(cnt, n, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK
+                                                                                    : PA_ERR_HIP;
+}
+
 pa_status pa_decode_partial(const pa_shape* shape, const void* q, const void* k_cache,
                             const void* v_cache, const int32_t* block_table,
                             const int32_t* context_lens, int32_t num_splits, void* out, float* lse,
                             void* workspace, size_t workspace_bytes, void* stream) {
   return run_partial(shape, q, k_cache, v_cache, block_table, context_lens, num_splits, out, lse,
-                     workspace, workspace_bytes, stream, false, nullptr);
+                     workspace, workspace_bytes, stream, false, false, nullptr, nullptr);
 }
 
 pa_status pa_decode_mla_partial(const pa_shape* shape, const void* q, const void* kv_cache,
@@ -241,7 +291,7 @@ pa_status pa_decode_mla_partial(const pa_shape* shape, const void* q, const void
                                 int32_t num_splits, void* out, float* lse, void* workspace,
                                 size_t workspace_bytes, void* stream) {
   return run_partial(shape, q, kv_cache, nullptr, block_table, context_lens, num_splits, out, lse,
-                     workspace, workspace_bytes, stream, true, nullptr);
+                     workspace, workspace_bytes, stream, true, false, nullptr, nullptr);
 }
 
 pa_status pa_reduce(const pa_shape* shape, const int32_t* context_lens, int32_t num_splits,
@@ -251,8 +301,7 @@ pa_status pa_reduce(const pa_shape* shape, const int32_t* context_lens, int32_t 
   if (st != PA_OK) return st;
   if (!context_lens || !out) return PA_ERR_INVALID;
   if (num_splits > 0) {
-    const int P = max_pages(*shape);
-    const int S = num_splits > P ? (P > 0 ? P : 1) : num_splits;
+    const int S = resolve_splits(*shape, num_splits, mla != 0);
     if (S <= 1) return PA_OK;
     if (!workspace || workspace_bytes < workspace_bytes_for(*shape, S)) return PA_ERR_WORKSPACE;
   }
@@ -267,10 +316,12 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache, c
                     const int32_t* block_table, const int32_t* context_lens, int32_t num_splits,
                     void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   int S = 0;
+  bool reduce = false;
   const pa_status st = run_partial(shape, q, k_cache, v_cache, block_table, context_lens, num_splits,
-                                   out, lse, workspace, workspace_bytes, stream, false, &S);
+                                   out, lse, workspace, workspace_bytes, stream, false, true, &S,
+                                   &reduce);
   if (st != PA_OK) return st;
-  return run_reduce(shape, context_lens, S, workspace, out, lse, stream);
+  return reduce ? run_reduce(shape, context_lens, S, workspace, out, lse, stream) : PA_OK;
 }
 
 pa_status pa_decode_mla(const pa_shape* shape, const void* q, const void* kv_cache,
@@ -278,10 +329,12 @@ pa_status pa_decode_mla(const pa_shape* shape, const void* q, const void* kv_cac
                         void* out, float* lse, void* workspace, size_t workspace_bytes,
                         void* stream) {
   int S = 0;
+  bool reduce = false;
   const pa_status st = run_partial(shape, q, kv_cache, nullptr, block_table, context_lens,
-                                   num_splits, out, lse, workspace, workspace_bytes, stream, true, &S);
+                                   num_splits, out, lse, workspace, workspace_bytes, stream, true,
+                                   true, &S, &reduce);
   if (st != PA_OK) return st;
-  return run_reduce(shape, context_lens, S, workspace, out, lse, stream);
+  return reduce ? run_reduce(shape, context_lens, S, workspace, out, lse, stream) : PA_OK;
 }
 
 }  // extern "C"

@@ -25,6 +25,7 @@
 //   rescale factor and the accumulator of a head live in the same lanes.
 #include "pa_device.h"
 #include "pa_launch.h"
+#include "pa_merge.h"
 
 namespace pa {
 namespace {
@@ -48,9 +49,9 @@ __device__ __forceinline__ void load_pair(PairTile& t, const char* ka, const cha
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) t.k[c][kb] = ld128(kp + c * 4 * kRowB + kb * 64);
+    for (int kb = 0; kb < 4; ++kb) t.k[c][kb] = ld128_stream(kp + c * 4 * kRowB + kb * 64);
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) t.v[nb] = ld128(vp + nb * 16 * 32);
+  for (int nb = 0; nb < 8; ++nb) t.v[nb] = ld128_stream(vp + nb * 16 * 32);
 }
 
 __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
@@ -123,7 +124,8 @@ __device__ __forceinline__ void consume_pair(PairTile& t, const u32x4 (&qf)[4], 
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
-  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int kvh = blockIdx.x, b = blockIdx.z;
+  const int s = split_of_block(blockIdx.y, b, p.S);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int quad = lane >> 4, n = lane & 15;
@@ -200,6 +202,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
     for (int r = 0; r < 4; ++r) sm_o[w][n][nb * 16 + quad * 4 + r] = acc[nb][r];
   __syncthreads();
 
+  const bool direct = split_is_direct(p, nsplit);
   for (int idx = threadIdx.x; idx < G * kD; idx += NW * 64) {
     const int hn = idx / kD, d = idx % kD;
     float M = kNegInf;
@@ -214,13 +217,22 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
       o = fmaf(f, sm_o[i][hn][d], o);
     }
     o = empty ? 0.f : o / L;
+    const float lse = empty ? kNegInf : (M + fast_log2(L)) * kLn2;
     const size_t row = (size_t)b * p.Hq + kvh * G + hn;
-    if (p.final_write) {
-      static_cast<uint16_t*>(p.out)[row * kD + d] = to_bf16(o);
-      if (d == 0 && p.lse) p.lse[row] = empty ? kNegInf : (M + fast_log2(L)) * kLn2;
+    if (direct) {
+      store_out<true>(p, row, d, o);
+      if (d == 0 && p.lse) p.lse[row] = lse;
     } else {
-      p.o_part[(row * p.S + s) * kD + d] = o;
-      if (d == 0) p.lse_part[row * p.S + s] = empty ? kNegInf : (M + fast_log2(L)) * kLn2;
+      store_coherent(p.o_part + (row * p.S + s) * kD + d, o);
+      if (d == 0) store_coherent(p.lse_part + row * p.S + s, lse);
+    }
+  }
+  if (!direct && p.fused) {
+    __shared__ int sm_flag;
+    const int unit = b * p.Hkv + kvh;
+    if (arrive_last(p, unit, nsplit, &sm_flag)) {
+      merge_unit<true, NW * 64>(p, b, kvh * G, G, nsplit, &sm_o[0][0][0]);
+      reset_counter(p, unit);
     }
   }
 }
@@ -234,7 +246,7 @@ bool gqa_mfma_supported(bool bf16, int D, int Dv, int bs, int G) {
 }
 
 hipError_t launch_gqa_mfma(const Params& p, hipStream_t st) {
-  dim3 grid(p.S, p.Hkv, p.B);
+  dim3 grid(p.Hkv, p.S, p.B);
   hipLaunchKernelGGL(gqa_mfma_partial<kGqaWaves>, grid, dim3(kGqaWaves * 64), 0, st, p);
   return hipGetLastError();
 }

@@ -18,11 +18,13 @@ struct Params {
   float* lse;                // [B][Hq] or nullptr
   float* o_part;             // [B][Hq][S][Dv] (S > 1)
   float* lse_part;           // [B][Hq][S]     (S > 1)
+  int32_t* counters;         // [B][Hq] arrival counters of the fused reduction (S > 1)
   int32_t B, Hq, Hkv, D, Dv, bs, maxb, nblocks, max_ctx;
   int32_t S;                 // splits in the grid
   int32_t c;                 // pages per split
   float scale_log2;          // scale * log2(e)
   int32_t final_write;       // 1: S == 1, write out/lse directly
+  int32_t fused;             // 1: the last workgroup of a unit merges the splits
 };
 
 // Each returns hipSuccess or the launch error.  Shapes are validated by the caller.
@@ -30,6 +32,7 @@ hipError_t launch_mha_valu(const Params& p, bool bf16, hipStream_t st);
 hipError_t launch_gqa_mfma(const Params& p, hipStream_t st);
 hipError_t launch_mla_mfma(const Params& p, hipStream_t st);
 hipError_t launch_reduce(const Params& p, bool bf16, hipStream_t st);
+hipError_t launch_zero_i32(int32_t* dst, size_t n, hipStream_t st);
 
 // Which kernels exist (host-side predicates used by validation and dispatch).
 bool mha_valu_supported(bool bf16, int D, int bs);

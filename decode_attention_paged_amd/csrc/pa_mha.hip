@@ -19,6 +19,7 @@
 //   accumulator is needed.
 #include "pa_device.h"
 #include "pa_launch.h"
+#include "pa_merge.h"
 
 namespace pa {
 namespace {
@@ -76,12 +77,12 @@ __device__ __forceinline__ void load_tile(MhaTile<BF16, D, BS>& t, const char* k
   using C = MhaCfg<BF16, D, BS>;
   const char* kl = kp + (lane / C::LPR) * C::ROWB + (lane % C::LPR) * 16;
 #pragma unroll
-  for (int i = 0; i < C::KI; ++i) t.k[i] = ld128(kl + i * C::RPI * C::ROWB);
+  for (int i = 0; i < C::KI; ++i) t.k[i] = ld128_stream(kl + i * C::RPI * C::ROWB);
 #pragma unroll
   for (int j = 0; j < C::DPL; ++j)
 #pragma unroll
     for (int h = 0; h < C::CPD; ++h)
-      t.v[j * C::CPD + h] = ld128(vp + (size_t)(j * 64 + lane) * BS * C::ES + h * 16);
+      t.v[j * C::CPD + h] = ld128_stream(vp + (size_t)(j * 64 + lane) * BS * C::ES + h * 16);
 }
 
 // Running state of one wave: max (log2 domain, wave-uniform), this lane's
@@ -168,7 +169,9 @@ __device__ __forceinline__ void consume_tile(const MhaTile<BF16, D, BS>& t, MhaS
 template <bool BF16, int D, int BS, int NW>
 __global__ __launch_bounds__(NW * 64) void mha_valu_partial(Params p) {
   using C = MhaCfg<BF16, D, BS>;
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // head fastest: consecutive workgroups land on different XCDs with equal work
+  const int h = blockIdx.x, b = blockIdx.z;
+  const int s = split_of_block(blockIdx.y, b, p.S);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int ctx = clampi(p.context_lens[b], 0, p.max_ctx);
@@ -244,25 +247,31 @@ __global__ __launch_bounds__(NW * 64) void mha_valu_partial(Params p) {
   const float inv = empty ? 0.f : 1.f / L;
   const float lse = empty ? kNegInf : (M + fast_log2(L)) * kLn2;
   const size_t row = (size_t)b * p.Hq + h;
+  const bool direct = split_is_direct(p, nsplit);
   for (int d = threadIdx.x; d < D; d += NW * 64) {
     float o = 0.f;
 #pragma unroll
     for (int i = 0; i < NW; ++i) o = fmaf(f[i], sm_acc[i][d], o);
     o *= inv;
-    if (p.final_write) {
-      if constexpr (BF16)
-        static_cast<uint16_t*>(p.out)[row * D + d] = to_bf16(o);
-      else
-        static_cast<float*>(p.out)[row * D + d] = o;
-    } else {
-      p.o_part[(row * p.S + s) * D + d] = o;
-    }
+    if (direct)
+      store_out<BF16>(p, row, d, o);
+    else
+      store_coherent(p.o_part + (row * p.S + s) * D + d, o);
   }
   if (threadIdx.x == 0) {
-    if (p.final_write) {
+    if (direct) {
       if (p.lse) p.lse[row] = lse;
     } else {
-      p.lse_part[row * p.S + s] = lse;
+      store_coherent(p.lse_part + row * p.S + s, lse);
+    }
+  }
+  if (!direct && p.fused) {
+    __shared__ int sm_flag;
+    __shared__ __attribute__((aligned(16))) float scratch[NW * 64 * 4];
+    const int unit = b * p.Hq + h;
+    if (arrive_last(p, unit, nsplit, &sm_flag)) {
+      merge_unit<BF16, NW * 64>(p, b, h, 1, nsplit, scratch);
+      reset_counter(p, unit);
     }
   }
 }
@@ -271,7 +280,7 @@ constexpr int kMhaWaves = 4;
 
 template <bool BF16, int D, int BS>
 hipError_t launch_one(const Params& p, hipStream_t st) {
-  dim3 grid(p.S, p.Hq, p.B);
+  dim3 grid(p.Hq, p.S, p.B);
   hipLaunchKernelGGL((mha_valu_partial<BF16, D, BS, kMhaWaves>), grid, dim3(kMhaWaves * 64), 0, st, p);
   return hipGetLastError();
 }

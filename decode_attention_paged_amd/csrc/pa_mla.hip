@@ -52,7 +52,8 @@ __global__ __launch_bounds__(NW * 64) void mla_mfma_partial(Params p) {
   __shared__ __attribute__((aligned(16))) char tile_g[kBS * kLdsRow];
   lds_char* tile = (lds_char*)tile_g;
 
-  const int s = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;
+  const int hb = blockIdx.x, b = blockIdx.z;
+  const int s = split_of_block(blockIdx.y, b, p.S);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int quad = lane >> 4, n = lane & 15;
   const int h0 = (hb * NW + w) * 16;
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(NW * 64) void mla_mfma_partial(Params p) {
     for (int c = threadIdx.x; c < kChunks; c += NW * 64) {
       const int tok = c / kChunksPerRow, cc = c % kChunksPerRow;
       u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (tok < nvalid) v = ld128(src + (size_t)c * 16);
+      if (tok < nvalid) v = ld128_stream(src + (size_t)c * 16);
       *(__attribute__((address_space(3))) u32x4*)(tile + tok * kLdsRow + cc * 16) = v;
     }
     __syncthreads();
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(NW * 64) void mla_mfma_partial(Params p) {
 
 template <int NW>
 hipError_t launch_nw(const Params& p, hipStream_t st) {
-  dim3 grid(p.S, p.Hq / (16 * NW), p.B);
+  dim3 grid(p.Hq / (16 * NW), p.S, p.B);
   hipLaunchKernelGGL(mla_mfma_partial<NW>, grid, dim3(NW * 64), 0, st, p);
   return hipGetLastError();
 }

@@ -81,7 +81,19 @@ __global__ __launch_bounds__(kRedWaves * 64) void split_reduce(Params p) {
   }
 }
 
+__global__ void zero_i32(int32_t* dst, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_zero_i32(int32_t* dst, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(zero_i32, dim3(blocks), dim3(256), 0, st, dst, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_reduce(const Params& p, bool bf16, hipStream_t st) {
   dim3 grid(p.Hq, p.B, (p.Dv + 63) / 64);

@@ -106,18 +106,34 @@ int32_t pa_choose_num_splits(const pa_shape* shape, int32_t num_cus, int32_t mla
 
 /*
  * Bytes of workspace a call with this shape and split count needs: float32
- * partials o[batch][num_q_heads][S][head_dim_v] and lse[batch][num_q_heads][S],
- * each 256-byte aligned.  0 when S resolves to 1 (the partial kernel then
- * writes out/lse directly).  num_splits <= 0 resolves through the heuristic
- * (which may query the device).  Returns 0 on an invalid shape.  Host only.
+ * partials o[batch][num_q_heads][S][head_dim_v], float32 lse[batch][num_q_heads][S]
+ * and int32 arrival counters [batch][num_q_heads], each 256-byte aligned.  0 when
+ * S resolves to 1 (the partial kernel then writes out/lse directly).
+ * num_splits <= 0 resolves through the heuristic (which may query the device).
+ * Returns 0 on an invalid shape.  Host only.
+ *
+ * The counters must be zero when a pa_decode / pa_decode_mla call starts:
+ * zero-fill a new workspace (pa_workspace_init, or any memset to 0) once; every
+ * call that completes leaves them zero again.  A workspace that a faulted or
+ * aborted call may have left dirty must be re-initialised.
  */
 size_t pa_decode_workspace_size(const pa_shape* shape, int32_t num_splits, int32_t mla);
 
 /*
+ * Zero the counter region of `workspace` for this shape and split count, on
+ * `stream` (a fill kernel, safe to capture in a graph).  PA_OK when S resolves
+ * to 1 (no workspace needed).  Errors as for pa_decode.
+ */
+pa_status pa_workspace_init(const pa_shape* shape, int32_t num_splits, int32_t mla,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Paged split-KV decode attention, MHA and GQA (num_q_heads a multiple of
- * num_kv_heads).  Runs the per-split partial kernel and, when S > 1, the
- * log-sum-exp weighted reduction.  `lse` may be NULL.  `workspace` may be
- * NULL only when S resolves to 1.
+ * num_kv_heads).  One kernel launch: each workgroup computes one split's
+ * partial; the last workgroup of each (sequence, head unit) to finish merges
+ * that unit's splits with the log-sum-exp weights (a sequence that needs a
+ * single split is written directly).  `lse` may be NULL.  `workspace` may be
+ * NULL only when S resolves to 1; its counters must be zero (see above).
  * Supported: PA_F32 with head_dim 64 or 128; PA_BF16 with head_dim 64 or 128;
  * head_dim_v == head_dim; block_size 16 or 32.
  */
@@ -140,10 +156,11 @@ pa_status pa_decode_mla(const pa_shape* shape, const void* q, const void* kv_cac
                         size_t workspace_bytes, void* stream);
 
 /*
- * The two steps of pa_decode / pa_decode_mla, exposed separately so a caller
- * can time them, or gather partials computed elsewhere (for example other
- * devices' page ranges) before reducing.  The partial step writes the split
- * partials into `workspace` (or, when S resolves to 1, out/lse directly).
+ * The two steps of the split-KV method as separate launches, so a caller can
+ * time them, or gather partials computed elsewhere (for example other
+ * devices' page ranges) before reducing.  The partial step writes every split
+ * partial into `workspace` (or, when S resolves to 1, out/lse directly) and
+ * does not touch the counters.
  * pa_reduce merges them: M = max_s lse_s, w_s = exp(lse_s - M),
  * out = sum_s w_s o_s / sum_s w_s, lse = M + ln(sum_s w_s) (page 4, step
  * three: rescale the split results by their log-sum-exp and reduce).

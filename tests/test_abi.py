@@ -101,10 +101,22 @@ def test_workspace_checks(lib):
     assert decode(lib, s, splits=4) == _lib.PA_ERR_WORKSPACE
     need = lib.pa_decode_workspace_size(ctypes.byref(s), 4, 0)
     rows = 2 * 8 * 4
-    assert need == (-(-rows * 128 * 4 // 256) * 256) + (-(-rows * 4 // 256) * 256)
+    up = lambda x: -(-x // 256) * 256
+    # o partials | lse partials | one arrival counter per (sequence, head)
+    assert need == up(rows * 128 * 4) + up(rows * 4) + up(2 * 8 * 4)
     assert decode(lib, s, splits=4, ws=FAKE, ws_bytes=need - 1) == _lib.PA_ERR_WORKSPACE
     # one split needs no workspace
     assert lib.pa_decode_workspace_size(ctypes.byref(s), 1, 0) == 0
+
+
+def test_workspace_init_checks(lib):
+    s = shape()
+    init = lambda sh, ws, n, splits=4: lib.pa_workspace_init(ctypes.byref(sh), splits, 0, ws, n, NULL)
+    need = lib.pa_decode_workspace_size(ctypes.byref(s), 4, 0)
+    assert init(s, NULL, 0) == _lib.PA_ERR_WORKSPACE
+    assert init(s, FAKE, need - 1) == _lib.PA_ERR_WORKSPACE
+    assert init(shape(batch=0), FAKE, need) == _lib.PA_ERR_INVALID
+    assert init(s, NULL, 0, splits=1) == _lib.PA_OK     # one split: nothing to initialise
 
 
 def test_mla_checks(lib):
