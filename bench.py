@@ -167,34 +167,43 @@ class Case:
         toks = self.tokens
         return 2.0 * toks * i.num_q_heads * (i.head_dim + i.head_dim_v)
 
+    def _loop(self, fn, steps: int):
+        """Average ms per call of `fn` over `steps` back-to-back calls.
+
+        HIP events on the launch stream bracket the whole loop; nothing else is
+        enqueued between the calls, so for a single-launch `fn` this is that
+        kernel's average launch duration.  Also returns host wall time.
+        """
+        import torch
+
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
+
     def time(self, steps: int, warmup: int):
-        """Time `steps` whole steps; partial and reduce timed with events."""
+        """Time `steps` whole steps (the timed region), then each kernel alone."""
         import torch
 
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-                torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for e0, e1, e2 in evs:
-            e0.record()
-            self.partial()
-            e1.record()
-            self.reduce()
-            e2.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        part = [a.elapsed_time(b) for a, b, _ in evs]
-        red = [b.elapsed_time(c) for _, b, c in evs]
-        part.sort()
-        return dict(
-            ms_per_step=wall * 1e3 / steps,
-            partial_ms=sum(part) / len(part),
-            partial_ms_median=part[len(part) // 2],
-            reduce_ms=sum(red) / len(red),
-        )
+        ev_ms, wall_ms = self._loop(self.step, steps)
+        r = dict(ms_per_step=wall_ms, ev_ms_per_step=ev_ms)
+        if self.fused:
+            r["partial_ms"] = ev_ms          # one launch per step
+            r["reduce_ms"] = 0.0
+        else:
+            r["partial_ms"], _ = self._loop(self.partial, steps)
+            r["reduce_ms"], _ = self._loop(self.reduce, steps)
+        return r
 
     def summary(self, r):
         frac = (self.kv_bytes / (r["partial_ms"] * 1e-3) / 1e9) / PEAK_HBM_GBS
@@ -203,6 +212,7 @@ class Case:
             num_splits=self.S,
             kernel=self.family,
             ms_per_step=round(r["ms_per_step"], 5),
+            ev_ms_per_step=round(r["ev_ms_per_step"], 5),
             tokens_per_s=round(self.inp.batch / (r["ms_per_step"] * 1e-3), 1),
             partial_ms=round(r["partial_ms"], 5),
             reduce_ms=round(r["reduce_ms"], 5),
