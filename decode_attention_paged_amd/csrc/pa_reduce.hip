@@ -4,10 +4,12 @@
 //   M = max_s lse_s,  w_s = exp(lse_s - M),
 //   out = sum_s w_s o_s / sum_s w_s,  lse = M + ln(sum_s w_s).
 //
-// One workgroup per (query head, sequence, block of 64 output dims); its four
-// waves each sum a quarter of the splits for the same 64 dims and the
-// quarters are added in LDS.  Only the splits the sequence actually used are
-// read (ragged batches use fewer splits for shorter sequences).
+// One wave per (sequence, query head) row, four rows per workgroup.  The
+// row's split weights come from its lse values (uniform across the wave);
+// each lane owns float4 columns of the output and sums the splits it needs
+// with 16-byte loads, several splits in flight at once.  Only the splits the
+// sequence actually used are read (ragged batches use fewer splits for
+// shorter sequences).
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -16,69 +18,76 @@ namespace {
 
 constexpr int kRedWaves = 4;
 
-__device__ __forceinline__ float block_max(float x, float* red) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+__device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  if (lane == 0) red[w] = x;
-  __syncthreads();
-  float r = red[0];
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
-  for (int i = 1; i < kRedWaves; ++i) r = fmaxf(r, red[i]);
-  __syncthreads();
-  return r;
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
 }
 
 template <bool BF16>
 __global__ __launch_bounds__(kRedWaves * 64) void split_reduce(Params p) {
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int d = blockIdx.z * 64 + lane;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kRedWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (row >= p.B * p.Hq) return;
+  const int b = row / p.Hq;
   const int ctx = clampi(p.context_lens[b], 0, p.max_ctx);
   const int pages = (ctx + p.bs - 1) / p.bs;
   int nsp = splits_of(pages, p.c);
   nsp = nsp > 0 ? nsp : 1;
-  const size_t row = (size_t)b * p.Hq + h;
-  const float* lp = p.lse_part + row * p.S;
-  const float* op = p.o_part + row * p.S * p.Dv;
+  const float* lp = p.lse_part + (size_t)row * p.S;
+  const float* op = p.o_part + (size_t)row * p.S * p.Dv;
 
-  __shared__ float red[kRedWaves];
-  __shared__ float part[kRedWaves][64];
-  __shared__ float lsum[kRedWaves];
-
-  float mx = kNegInf;
-  for (int i = threadIdx.x; i < nsp; i += kRedWaves * 64) mx = fmaxf(mx, lp[i]);
-  const float M = block_max(mx, red);
+  float m = kNegInf;
+  for (int i = lane; i < nsp; i += 64) m = fmaxf(m, lp[i]);
+  const float M = wave_max(m);
   const bool empty = (M == kNegInf);
+  float l = 0.f;
+  if (!empty)
+    for (int i = lane; i < nsp; i += 64) l += fast_exp2((lp[i] - M) * kLog2e);
+  const float L = wave_sum(l);
+  const float inv = empty ? 0.f : 1.f / L;
 
-  float acc = 0.f, L = 0.f;
-  if (!empty) {
-    for (int i = w; i < nsp; i += kRedWaves) {
-      const float wt = fast_exp2((lp[i] - M) * kLog2e);
-      L += wt;
-      if (d < p.Dv) acc = fmaf(wt, op[(size_t)i * p.Dv + d], acc);
-    }
-  }
-  part[w][lane] = acc;
-  if (lane == 0) lsum[w] = L;
-  __syncthreads();
-  if (w == 0) {
-    float o = 0.f, lt = 0.f;
+  const int cols = p.Dv / 4;
+  for (int c = lane; c < cols; c += 64) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (!empty) {
+#pragma unroll 8
+      for (int s = 0; s < nsp; ++s) {
+        const float wt = fast_exp2((lp[s] - M) * kLog2e);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(op + (size_t)s * p.Dv + c * 4);
 #pragma unroll
-    for (int i = 0; i < kRedWaves; ++i) {
-      o += part[i][lane];
-      lt += lsum[i];
+        for (int r = 0; r < 4; ++r) acc[r] = fmaf(wt, v[r], acc[r]);
+      }
     }
-    o = empty ? 0.f : o / lt;
-    if (d < p.Dv) {
-      if constexpr (BF16)
-        static_cast<uint16_t*>(p.out)[row * p.Dv + d] = to_bf16(o);
-      else
-        static_cast<float*>(p.out)[row * p.Dv + d] = o;
+    if constexpr (BF16) {
+      u32x2 pk;
+      pk[0] = pack_bf16(acc[0] * inv, acc[1] * inv);
+      pk[1] = pack_bf16(acc[2] * inv, acc[3] * inv);
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (size_t)row * p.Dv + c * 4) = pk;
+    } else {
+      f32x4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = acc[r] * inv;
+      *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + (size_t)row * p.Dv + c * 4) = o;
     }
-    if (blockIdx.z == 0 && lane == 0 && p.lse)
-      p.lse[row] = empty ? kNegInf : M + fast_log2(lt) * kLn2;
   }
+  // dims past the last full float4 column (head dims not a multiple of 4)
+  for (int d = cols * 4 + lane; d < p.Dv; d += 64) {
+    float acc = 0.f;
+    if (!empty)
+      for (int s = 0; s < nsp; ++s)
+        acc = fmaf(fast_exp2((lp[s] - M) * kLog2e), op[(size_t)s * p.Dv + d], acc);
+    if constexpr (BF16)
+      static_cast<uint16_t*>(p.out)[(size_t)row * p.Dv + d] = to_bf16(acc * inv);
+    else
+      static_cast<float*>(p.out)[(size_t)row * p.Dv + d] = acc * inv;
+  }
+  if (lane == 0 && p.lse) p.lse[row] = empty ? kNegInf : M + fast_log2(L) * kLn2;
 }
 
 __global__ void zero_i32(int32_t* dst, size_t n) {
@@ -96,7 +105,8 @@ hipError_t launch_zero_i32(int32_t* dst, size_t n, hipStream_t st) {
 }
 
 hipError_t launch_reduce(const Params& p, bool bf16, hipStream_t st) {
-  dim3 grid(p.Hq, p.B, (p.Dv + 63) / 64);
+  const int rows = p.B * p.Hq;
+  dim3 grid((rows + kRedWaves - 1) / kRedWaves);
   if (bf16)
     hipLaunchKernelGGL(split_reduce<true>, grid, dim3(kRedWaves * 64), 0, st, p);
   else

@@ -380,3 +380,34 @@ def test_bf16_output_rounding_is_nearest_even():
         bt = inp.compact_block_table()
         for b in range(3):
             assert np.array_equal(o[b, :, :], inp.v_pages[bt[b, 0], :, :, 0])
+
+
+@pytest.mark.parametrize("spec", [PROP, PROP_MHA, PROP_MLA], ids=["gqa", "mha", "mla"])
+def test_rising_scores(spec):
+    """Scores that climb steeply with the token index: every tile's max exceeds
+    the running max by far more than the bf16 weights could hold unrescaled,
+    so each kernel's handling of a rising max (rescaling, or starting a split
+    over with a raised reference max) runs at every tile."""
+    from workloads import f32_to_bf16_bits
+    lens = [1000, 77] + list(spec["context_lens"][2:])
+    s = dict(spec, context_lens=lens,
+             num_blocks=sum(-(-n // spec["block_size"]) for n in lens) + 10)
+    inp = make_paged_inputs(seed=18, **s)
+    bt = inp.compact_block_table()
+    step = 8.0 if inp.kind == "mla" else 3.0
+    d = inp.head_dim - 1      # for the latent: a key-only dim, outside the value part
+    for b in range(inp.batch):
+        for tok in range(int(inp.context_lens[b])):
+            page, slot = bt[b, tok // inp.block_size], tok % inp.block_size
+            bits = f32_to_bf16_bits(np.array([step * tok], np.float32))[0]
+            if inp.kind == "mla":
+                inp.c_pages[page, slot, d] = bits
+            else:
+                inp.k_pages[page, :, slot, d] = bits
+    inp.q[:, :, d] = f32_to_bf16_bits(np.array([1.0], np.float32))[0]
+    ref_out, ref_lse = oracle.decode_inputs(inp)
+    t = to_device(inp, "cuda")
+    for S in (1, 3, 0):
+        say(f"rising scores {inp.kind} S={S}")
+        out, lse = run(inp, t, num_splits=S)
+        compare(inp, out, lse, ref_out, ref_lse, f"rising scores S={S}")
