@@ -46,7 +46,7 @@ pa_status check_shape(const pa_shape* s, bool mla) {
   if ((int64_t)s->max_context_len > (int64_t)s->max_blocks_per_seq * s->block_size)
     return PA_ERR_INVALID;
   if (s->dtype != PA_F32 && s->dtype != PA_BF16) return PA_ERR_INVALID;
-  if (!std::isfinite(s->scale)) return PA_ERR_INVALID;
+  if (!std::isfinite(s->scale) || !(s->scale > 0.f)) return PA_ERR_INVALID;
   if (mla && (s->num_kv_heads != 1 || s->head_dim_v > s->head_dim)) return PA_ERR_INVALID;
   if (pick_kernel(*s, mla) == Kernel::None) return PA_ERR_UNSUPPORTED;
   return PA_OK;
@@ -93,8 +93,9 @@ int heuristic_splits(const pa_shape& s, int cus, bool mla) {
   const int esz = s.dtype == PA_BF16 ? 2 : 4;
   long S;
   if (k == Kernel::MlaMfma) {
-    // one workgroup per (sequence, split) holds every head: fill the CUs once
-    S = (cus + s.batch - 1) / s.batch;
+    // one workgroup per (head group, sequence, split): fill the CUs once
+    const long groups = (long)s.batch * (s.num_q_heads / pa::mla_heads_per_workgroup(s.num_q_heads));
+    S = (cus + groups - 1) / groups;
   } else {
     long units;
     int heads_per_wg;

@@ -38,5 +38,7 @@ hipError_t launch_zero_i32(int32_t* dst, size_t n, hipStream_t st);
 bool mha_valu_supported(bool bf16, int D, int bs);
 bool gqa_mfma_supported(bool bf16, int D, int Dv, int bs, int G);
 bool mla_mfma_supported(bool bf16, int Dqk, int Dv, int bs, int Hq);
+// Query heads one MLA workgroup holds (the grid has Hq / this head groups).
+int mla_heads_per_workgroup(int Hq);
 
 }  // namespace pa

@@ -37,9 +37,14 @@
 // chunk in flight.  Each ring slot is its own LDS array and the chunk loop is
 // unrolled over the ring, so the compiler can tell the slots apart.
 //
-// LDS chunk rows are 1152 bytes (72 chunks of 16 bytes); chunk c of token row
-// t sits at position c ^ (t & 7), which spreads both the score reads (16 rows,
-// same chunk) and the transposed value reads over the banks.
+// LDS chunk rows are 1152 bytes (72 chunks of 16 bytes).  Chunk c of token
+// row t sits at position c ^ (t & 7); with it the score reads (16 rows, one
+// chunk each) and the transposed value reads run at the conflict-free rate
+// (measured against a linear read of the same size).  The probabilities are
+// stored so that the value product's B-operand read is linear: for head block
+// nb, the 16-byte slot q*16 + n holds tokens 8q .. 8q+7 of head 16 nb + n.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -66,10 +71,6 @@ typedef __attribute__((address_space(3))) float lds_float;
 // context, so no NaN or stale data reaches the value product.
 __device__ __attribute__((aligned(16))) uint32_t g_zero16[4] = {0u, 0u, 0u, 0u};
 
-__device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
 
 // Score products in the VGPR form of the MFMA, written as asm because the
 // compiler gives all MFMAs of a kernel one form and the value accumulators of
@@ -84,6 +85,11 @@ __device__ __forceinline__ void mfma_v_first(f32x4& d, const u32x4& a, const u32
 __device__ __forceinline__ void mfma_v(f32x4& d, const u32x4& a, const u32x4& b) {
   asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
+// Value products accumulate in AGPRs (asm too, so the accumulators are
+// pinned there whatever the wave's register budget).  Same padding rules.
+__device__ __forceinline__ void mfma_a(f32x4& d, const u32x4& a, const u32x4& b) {
+  asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
 template <int HB>
 __device__ __forceinline__ void mfma_v_drain(f32x4 (&d)[HB][2]) {
   if constexpr (HB == 1)
@@ -97,13 +103,14 @@ __device__ __forceinline__ void mfma_v_drain(f32x4 (&d)[HB][2]) {
 // an LDS write through the vector memory path: it cannot tell the ring slots
 // apart and would make every later LDS access wait for all loads in flight,
 // draining the ring each chunk.  Completion is awaited explicitly (wait_vm
-// before the barrier that opens each chunk).  M0 takes the LDS base; an SALU
-// write of M0 needs one wait state before the load that uses it.
+// before the barrier that opens each chunk).  The compiler sets M0 (the LDS
+// base) for the asm; an SALU write of M0 needs one wait state before the load
+// that uses it.
 __device__ __forceinline__ void dma16(const void* g, lds_char* wave_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                :
-               : "v"(g), "s"((uint32_t)(uintptr_t)wave_base)
-               : "memory", "m0");
+               : "v"(g), "{m0}"((uint32_t)(uintptr_t)wave_base)
+               : "memory");
 }
 
 // LDS stores that the compiler's wait-count pass cannot see as LDS accesses.
@@ -162,9 +169,10 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Byte offset of 16-byte chunk c of token row t inside a chunk buffer.
-__device__ __forceinline__ int swz(int t, int c) { return t * kRowB + ((c ^ (t & 7)) << 4); }
+__device__ __forceinline__ int row_key(int t) { return t & 7; }
 
 constexpr float kHeadroom = 16.0f;   // log2 units a chunk's max may exceed the reference max
+constexpr int kRing = 4;             // chunk slots: value product, scores, two loads in flight
 
 template <int NW, int HB>
 struct MlaCfg {
@@ -172,18 +180,17 @@ struct MlaCfg {
   static constexpr int NB = NH / 16;                 // head blocks (value N-blocks)
   static constexpr int DW = kDv / NW;                // value dims per wave
   static constexpr int MB = DW / 16;                 // value M-blocks per wave
-  static constexpr int NWI = kDmaInst / NW;          // direct-to-LDS loads per wave per chunk, at least
-  static constexpr int AHEAD = NW >= 4 ? 2 : 1;      // chunks in flight beyond the current one
-  static constexpr int RING = AHEAD + 2;             // 4, or 3
-  static_assert(AHEAD * NWI <= 63, "vmcnt range");
+  static constexpr int NWI = kDmaInst / NW;          // direct-to-LDS loads per wave per chunk
+  static constexpr int LOOK = 2;                     // score operand loads ahead of their MFMAs
+  static_assert(kDmaInst % NW == 0, "uniform load share");
+  static_assert(HB == 1 || HB == 2, "head blocks per wave");
 };
 
+// Probabilities of two consecutive chunks (written for chunk i while the
+// value product of chunk i - 1 reads the other buffer).
 template <int NW, int HB>
 struct MlaLds {
-  uint16_t p[MlaCfg<NW, HB>::NH * kCT];   // probabilities, [head][token] bf16
-  int restart[2];                         // per chunk parity: a head's max overflowed the headroom
-  float stat_m[MlaCfg<NW, HB>::NH];
-  float stat_l[MlaCfg<NW, HB>::NH];
+  uint16_t p[2][MlaCfg<NW, HB>::NH * kCT];
 };
 
 // Physical page ids of the split, one per lane for a window of 64 logical
@@ -217,33 +224,20 @@ __device__ __forceinline__ void issue_chunk(lds_char* dst, const char* cbase, in
   const int tok0 = t0 + ci * kCT;
   const char* src = cbase + (size_t)id * (kBS * kRowB) + (tok0 % kBS) * kRowB;
   const int lim = (ctx - tok0) * kRowB;              // bytes of the chunk that hold context tokens
+  // recompute the per-lane offsets at every issue rather than keep them in
+  // registers across the loop (a few VALU ops against ~18 VGPRs)
+  asm volatile("" : "+v"(lane));
 #pragma unroll
-  for (int k = 0; k < (kDmaInst + NW - 1) / NW; ++k) {
+  for (int k = 0; k < kDmaInst / NW; ++k) {
     const int j = w + NW * k;
-    if (kDmaInst % NW != 0 && j >= kDmaInst) break;
     const int slot = j * 64 + lane;                  // 16-byte slot of the chunk buffer
     const int t = slot / (kRowB / 16);
-    const int c = (slot % (kRowB / 16)) ^ (t & 7);
+    const int c = (slot % (kRowB / 16)) ^ row_key(t);
     const int off = t * kRowB + c * 16;
     const void* g = off < lim ? (const void*)(src + off) : (const void*)g_zero16;
     dma16(g, dst + j * 1024);
   }
 }
-
-// The ring slots, addressed by compile-time slot index.
-struct Ring {
-  lds_char* s0;
-  lds_char* s1;
-  lds_char* s2;
-  lds_char* s3;
-  template <int K>
-  __device__ __forceinline__ lds_char* at() const {
-    if constexpr (K == 0) return s0;
-    else if constexpr (K == 1) return s1;
-    else if constexpr (K == 2) return s2;
-    else return s3;
-  }
-};
 
 template <int NW, int HB>
 struct MlaState {
@@ -252,50 +246,35 @@ struct MlaState {
   float m[HB];                                        // reference max per score head (log2)
   float mtop[HB];                                     // largest chunk max seen (log2)
   float l[HB];                                        // this lane's share of the sum
+  bool bad;                                           // a chunk max overflowed the headroom
 };
 
-// One chunk of the split.  Returns true (uniformly over the workgroup) when a
-// head's max overflowed the headroom: the chunk's value product is skipped and
-// the caller starts the split over.
-template <int NW, int HB, int SLOT>
-__device__ __forceinline__ bool mla_chunk(const Params& p, MlaLds<NW, HB>& sm, const Ring& ring,
-                                          MlaState<NW, HB>& st, int ci, int nchunks, int t0,
-                                          int ctx, const char* cbase, const int* bt, PageIds& ids,
-                                          int p1, int w, int lane) {
+// Scores of one chunk: S^T for this wave's 16*HB heads, 32 tokens.
+template <int NW, int HB>
+__device__ __forceinline__ void chunk_scores(const lds_char* buf, const MlaState<NW, HB>& st,
+                                             f32x4 (&sa)[HB][2], int lane) {
   using C = MlaCfg<NW, HB>;
   const int quad = lane >> 4, n = lane & 15;
-  // wait for this wave's loads of chunk ci, then (barrier) for every wave's;
-  // the barrier also means every wave is done with the slot refilled below
-  const int ahead = min(C::AHEAD, nchunks - 1 - ci);
-  wait_vm_dyn(ahead * C::NWI);
-  lds_barrier();
-  if (ci + C::AHEAD + 1 < nchunks) {
-    const int cn = ci + C::AHEAD + 1;
-    const int id = chunk_page_id(ids, bt, t0, cn, p1, p.nblocks, lane);
-    issue_chunk<NW>(ring.template at<(SLOT + C::AHEAD + 1) % C::RING>(), cbase, id, t0, cn, ctx,
-                    w, lane);
-  }
-  const lds_char* buf = ring.template at<SLOT>();
-
-  // ---- scores.  Row n (and 16 + n), 16-byte chunk kb*4 + quad: with the
-  // swizzle its byte offset is n*kRowB + 16*(quad ^ (n & 3)) + 64*(kb ^ ((n>>2)&1)),
-  // i.e. one per-lane base for even and one for odd k-steps plus 64*kb.
+  // Row n (and 16 + n), 16-byte chunk kb*4 + quad: with the swizzle its byte
+  // offset is n*kRowB + 16*(quad ^ (n & 3)) + 64*(kb ^ ((n >> 2) & 1)), i.e.
+  // one per-lane base for even and one for odd k-steps plus 64*kb.
   const int xb = (n >> 2) & 1;
   const int sbase = n * kRowB + 16 * (quad ^ (n & 3));
   const lds_char* se = buf + sbase + 64 * xb;
   const lds_char* so = buf + sbase - 64 * xb;
-  f32x4 sa[HB][2];
-  // A operands one k-step ahead of the MFMAs that use them
-  u32x4 an0 = *(const lds_u32x4*)se;
-  u32x4 an1 = *(const lds_u32x4*)(se + 16 * kRowB);          // row 16 + n: same swizzle
+  auto load_a = [&](int kb, u32x4& x0, u32x4& x1) {
+    const lds_char* rp = ((kb & 1) ? so : se) + 64 * kb;
+    x0 = *(const lds_u32x4*)rp;
+    x1 = *(const lds_u32x4*)(rp + 16 * kRowB);               // row 16 + n: same swizzle
+  };
+  constexpr int L = C::LOOK;
+  u32x4 ab[L + 1][2];
+#pragma unroll
+  for (int kb = 0; kb < L; ++kb) load_a(kb, ab[kb][0], ab[kb][1]);
 #pragma unroll
   for (int kb = 0; kb < kKSteps; ++kb) {
-    const u32x4 a0 = an0, a1 = an1;
-    if (kb + 1 < kKSteps) {
-      const lds_char* rp = (((kb + 1) & 1) ? so : se) + 64 * (kb + 1);
-      an0 = *(const lds_u32x4*)rp;
-      an1 = *(const lds_u32x4*)(rp + 16 * kRowB);
-    }
+    if (kb + L < kKSteps) load_a(kb + L, ab[(kb + L) % (L + 1)][0], ab[(kb + L) % (L + 1)][1]);
+    const u32x4 a0 = ab[kb % (L + 1)][0], a1 = ab[kb % (L + 1)][1];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       if (kb == 0) {
@@ -308,96 +287,184 @@ __device__ __forceinline__ bool mla_chunk(const Params& p, MlaLds<NW, HB>& sm, c
     }
   }
   mfma_v_drain<HB>(sa);
-  const int tbase = t0 + ci * kCT;
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    float sc[8];
-    float mx = kNegInf;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sc[r] = (tbase + quad * 4 + r < ctx) ? sa[hb][0][r] * p.scale_log2 : kNegInf;
-      sc[4 + r] = (tbase + 16 + quad * 4 + r < ctx) ? sa[hb][1][r] * p.scale_log2 : kNegInf;
-      mx = fmaxf(mx, fmaxf(sc[r], sc[4 + r]));
-    }
-    mx = max_xor32(max_xor16(mx));                  // same in the 4 quads of a head
-    st.mtop[hb] = fmaxf(st.mtop[hb], mx);
-    if (st.m[hb] == kNegInf) st.m[hb] = mx;          // first chunk of the pass
-    if (mx > st.m[hb] + kHeadroom) ds_store_b32((lds_char*)&sm.restart[ci & 1], 1u);
-    const float mn = st.m[hb];
-    float pr[8];
-    float ls = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pr[j] = fast_exp2(sc[j] - mn);
-      ls += pr[j];
-    }
-    st.l[hb] += ls;
-    const int head = 16 * (HB * w + hb) + n;
-    lds_char* prow = (lds_char*)sm.p + head * (kCT * 2);
-    u32x2 v0, v1;
-    v0[0] = pack_bf16(pr[0], pr[1]);
-    v0[1] = pack_bf16(pr[2], pr[3]);
-    v1[0] = pack_bf16(pr[4], pr[5]);
-    v1[1] = pack_bf16(pr[6], pr[7]);
-    ds_store_b64(prow + quad * 8, v0);               // tokens quad*4 .. +3
-    ds_store_b64(prow + 32 + quad * 8, v1);          // tokens 16 + quad*4 .. +3
-  }
-  lds_barrier();
-  // every wave has read the other parity's flag (last chunk's) before the
-  // barrier above, and it is next written after the next chunk's first barrier
-  if (w == 0 && lane == 0) ds_store_b32((lds_char*)&sm.restart[(ci + 1) & 1], 0u);
-  if (__builtin_amdgcn_readfirstlane(sm.restart[ci & 1]) != 0) return true;
+}
 
-  // ---- values for dims DW*w .. DW*w + DW - 1 of every head
-  // A operand (V^T): tokens quad*8 .. +7 of dim DW*w + mb*16 + n, two transposed reads
-  auto load_va = [&](int mb) {
-    const int bc = (C::DW * w + mb * 16) * 2 + (n & 3) * 8;    // byte column this lane reads
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E - 1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Softmax of one head block of a chunk, in four stages so that the caller can
+// spread them between value-product MFMAs.  Stage 0: mask and the lane's max;
+// 1: the head's max, reference max and overflow check; 2: weights and sum (in
+// place); 3: probabilities to LDS ([head block][token / 8][head % 16] 16-byte
+// slots, which the value product reads linearly).
+struct SoftmaxRow {
+  float v[8];   // scores, then weights
+  float mx;
+};
+
+template <int NW, int HB, int STAGE>
+__device__ __forceinline__ void softmax_stage(SoftmaxRow& r, const f32x4 (&sa)[2],
+                                              MlaState<NW, HB>& st, int hb, int tbase, int ctx,
+                                              float cs, lds_char* pbuf, int w, int lane) {
+  const int quad = lane >> 4, n = lane & 15;
+  if constexpr (STAGE == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r.v[j] = sa[0][j];
+      r.v[4 + j] = sa[1][j];
+    }
+    if (tbase + kCT > ctx) {                          // only a split's last chunk runs past the context
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (tbase + quad * 4 + j >= ctx) r.v[j] = kNegInf;
+        if (tbase + 16 + quad * 4 + j >= ctx) r.v[4 + j] = kNegInf;
+      }
+    }
+    r.mx = fmaxf(fmaxf(fmaxf(r.v[0], r.v[1]), fmaxf(r.v[2], r.v[3])),
+                 fmaxf(fmaxf(r.v[4], r.v[5]), fmaxf(r.v[6], r.v[7])));
+  } else if constexpr (STAGE == 1) {
+    const float mx = max_xor32(max_xor16(r.mx)) * cs;    // same in the 4 quads; log2 units
+    st.mtop[hb] = fmaxf(st.mtop[hb], mx);
+    if (st.m[hb] == kNegInf) st.m[hb] = mx;          // first chunk of the first pass
+    st.bad |= mx > st.m[hb] + kHeadroom;
+  } else if constexpr (STAGE == 2) {
+    const float mn = st.m[hb];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r.v[j] = fast_exp2(fmaf(r.v[j], cs, -mn));
+    st.l[hb] += ((r.v[0] + r.v[1]) + (r.v[2] + r.v[3])) + ((r.v[4] + r.v[5]) + (r.v[6] + r.v[7]));
+  } else {
+    lds_char* prow = pbuf + (HB * w + hb) * (16 * kCT * 2) + n * 16;
+    u32x2 v0, v1;
+    v0[0] = pack_bf16(r.v[0], r.v[1]);
+    v0[1] = pack_bf16(r.v[2], r.v[3]);
+    v1[0] = pack_bf16(r.v[4], r.v[5]);
+    v1[1] = pack_bf16(r.v[6], r.v[7]);
+    ds_store_b64(prow + 256 * (quad >> 1) + 8 * (quad & 1), v0);        // tokens quad*4 .. +3
+    ds_store_b64(prow + 256 * (2 + (quad >> 1)) + 8 * (quad & 1), v1);  // tokens 16 + quad*4 ..
+  }
+}
+
+// The value product for dims DW*w .. DW*w + DW - 1 of every head.  A operand
+// (V^T): tokens quad*8 .. +7 of one dim per lane, two transposed reads; B
+// operand (P^T): one 16-byte slot.
+template <int NW, int HB>
+struct ValueOps {
+  const lds_char* buf;
+  const lds_char* pbuf;
+  int w, n, quad;
+  __device__ __forceinline__ u32x4 va(int mb) const {
+    const int bc = (MlaCfg<NW, HB>::DW * w + mb * 16) * 2 + (n & 3) * 8;   // byte column
     const int r0 = quad * 8 + (n >> 2), r1 = r0 + 4;
-    const lds_char* lo = buf + r0 * kRowB + (((bc >> 4) ^ (r0 & 7)) << 4) + (bc & 15);
-    const lds_char* hi = buf + r1 * kRowB + (((bc >> 4) ^ (r1 & 7)) << 4) + (bc & 15);
+    const lds_char* lo = buf + r0 * kRowB + (((bc >> 4) ^ row_key(r0)) << 4) + (bc & 15);
+    const lds_char* hi = buf + r1 * kRowB + (((bc >> 4) ^ row_key(r1)) << 4) + (bc & 15);
     const u32x2 vlo = lds_tr16(lo), vhi = lds_tr16(hi);
     return u32x4{vlo[0], vlo[1], vhi[0], vhi[1]};
-  };
-  // B operand (P^T): tokens quad*8 .. +7 of head nb*16 + n
-  auto load_pb = [&](int nb) {
-    return *(const lds_u32x4*)((const lds_char*)sm.p + (nb * 16 + n) * (kCT * 2) + quad * 16);
-  };
-  if constexpr (C::MB < C::NB) {
-    u32x4 va[C::MB];
-#pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb) va[mb] = load_va(mb);
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) {
-      const u32x4 pb = load_pb(nb);
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) st.acc[mb][nb] = mfma(va[mb], pb, st.acc[mb][nb]);
-    }
-  } else {
-    u32x4 pb[C::NB];
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) pb[nb] = load_pb(nb);
-#pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb) {
-      const u32x4 va = load_va(mb);
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) st.acc[mb][nb] = mfma(va, pb[nb], st.acc[mb][nb]);
-    }
   }
-  return false;
+  __device__ __forceinline__ u32x4 pb(int nb) const {
+    return *(const lds_u32x4*)(pbuf + nb * (16 * kCT * 2) + 16 * (quad * 16 + n));
+  }
+};
+
+// The value product runs in groups of at most 4 B operands (head blocks) by
+// every M-block, A operands two deep; with PV false only the softmax runs.
+// The softmax stages of this chunk go between the MFMA groups of the previous
+// chunk's value product, so one wave keeps both the MFMA pipe and the VALU
+// busy.
+template <int NW, int HB, bool PV>
+__device__ __forceinline__ void values_and_softmax(MlaState<NW, HB>& st, const ValueOps<NW, HB>& vo,
+                                                   const f32x4 (&sa)[HB][2], int tbase, int ctx,
+                                                   float cs, lds_char* pbuf, int w, int lane) {
+  using C = MlaCfg<NW, HB>;
+  constexpr int NBG = C::NB < 4 ? C::NB : 4;          // head blocks per group
+  constexpr int NHALF = C::NB / NBG;                  // passes over the M-blocks
+  constexpr int G = NHALF * C::MB;                    // MFMA groups
+  constexpr int STAGES = 4 * HB;
+  static_assert(C::NB % NBG == 0, "head block groups");
+  SoftmaxRow row;
+  auto stage = [&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    softmax_stage<NW, HB, k % 4>(row, sa[k / 4], st, k / 4, tbase, ctx, cs, pbuf, w, lane);
+  };
+  if constexpr (!PV) {
+    static_for<0, STAGES>(stage);
+  } else {
+    u32x4 pb[NBG];
+    u32x4 va[2];
+    static_for<0, G>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      constexpr int h = g / C::MB, mb = g % C::MB;
+      if constexpr (mb == 0) {
+#pragma unroll
+        for (int i = 0; i < NBG; ++i) pb[i] = vo.pb(h * NBG + i);
+        va[0] = vo.va(0);
+      }
+      if constexpr (mb + 1 < C::MB) va[(mb + 1) & 1] = vo.va(mb + 1);
+#pragma unroll
+      for (int i = 0; i < NBG; ++i) mfma_a(st.acc[mb][h * NBG + i], va[mb & 1], pb[i]);
+      // softmax stage k after group (k * G) / STAGES
+      static_for<0, STAGES>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr ((k * G) / STAGES == g) stage(kc);
+      });
+    });
+  }
+}
+
+// Value product alone (the split's last chunk).
+template <int NW, int HB>
+__device__ __forceinline__ void values_only(MlaState<NW, HB>& st, const ValueOps<NW, HB>& vo) {
+  using C = MlaCfg<NW, HB>;
+  constexpr int NBG = C::NB < 4 ? C::NB : 4;
+  constexpr int G = (C::NB / NBG) * C::MB;
+  u32x4 pb[NBG];
+  u32x4 va[2];
+  static_for<0, G>([&](auto gc) {
+    constexpr int g = decltype(gc)::value;
+    constexpr int h = g / C::MB, mb = g % C::MB;
+    if constexpr (mb == 0) {
+#pragma unroll
+      for (int i = 0; i < NBG; ++i) pb[i] = vo.pb(h * NBG + i);
+      va[0] = vo.va(0);
+    }
+    if constexpr (mb + 1 < C::MB) va[(mb + 1) & 1] = vo.va(mb + 1);
+#pragma unroll
+    for (int i = 0; i < NBG; ++i) mfma_a(st.acc[mb][h * NBG + i], va[mb & 1], pb[i]);
+  });
 }
 
 template <int NW, int HB>
 __global__ __launch_bounds__(NW * 64) void mla_mfma_partial(Params p) {
   using C = MlaCfg<NW, HB>;
-  __shared__ __attribute__((aligned(16))) char ring0[kChunkB];
-  __shared__ __attribute__((aligned(16))) char ring1[kChunkB];
-  __shared__ __attribute__((aligned(16))) char ring2[kChunkB];
-  __shared__ __attribute__((aligned(16))) char ring3[C::RING > 3 ? kChunkB : 16];
+  __shared__ __attribute__((aligned(16))) char ring_lds[kRing * kChunkB];
   __shared__ __attribute__((aligned(16))) MlaLds<NW, HB> sm;
-  const Ring ring{(lds_char*)ring0, (lds_char*)ring1, (lds_char*)ring2, (lds_char*)ring3};
+  lds_char* const ring = (lds_char*)ring_lds;
 
-  const int hg = blockIdx.x, b = blockIdx.z;
-  const int s = split_of_block(blockIdx.y, b, p.S);
+  // 1-D grid of HG x S x B workgroups.  With two head groups, the two
+  // workgroups of one (sequence, split) are 8 apart in dispatch order: the
+  // same XCD (workgroups go round-robin to the 8 XCDs) at about the same time,
+  // so the second reads the latent rows from that XCD's L2.
+  const int HG = p.Hq / C::NH;
+  int hg, u;
+  const int L = blockIdx.x, g16 = L >> 4;
+  if (HG == 2 && (g16 + 1) * 16 <= (int)gridDim.x) {
+    hg = (L >> 3) & 1;
+    u = (g16 << 3) | (L & 7);
+  } else if (HG == 2) {                               // last, partial group of 16
+    const int r = L - (g16 << 4);
+    hg = r & 1;
+    u = (g16 << 3) + (r >> 1);
+  } else {
+    hg = L % HG;
+    u = L / HG;
+  }
+  const int b = u / p.S;
+  const int s = split_of_block(u % p.S, b, p.S);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int quad = lane >> 4, n = lane & 15;
@@ -410,6 +477,7 @@ __global__ __launch_bounds__(NW * 64) void mla_mfma_partial(Params p) {
   const int t1 = min(ctx, (s * p.c + p.c) * kBS);
   const int p1 = min(pages, s * p.c + p.c);
   const int nchunks = t1 > t0 ? (t1 - t0 + kCT - 1) / kCT : 0;
+  const float cs = p.scale_log2;                      // > 0, checked by the host
 
   MlaState<NW, HB> st;
 #pragma unroll
@@ -422,10 +490,11 @@ __global__ __launch_bounds__(NW * 64) void mla_mfma_partial(Params p) {
     st.m[hb] = kNegInf;
     st.mtop[hb] = kNegInf;
   }
-  if (w == 0 && lane == 0) sm.restart[0] = sm.restart[1] = 0;
 
   const int* bt = p.block_table + (size_t)b * p.maxb;
   const char* cbase = static_cast<const char*>(p.k);
+  auto slot = [&](int ci) { return ring + (ci % kRing) * kChunkB; };
+  auto pslot = [&](int ci) { return (lds_char*)sm.p[ci & 1]; };
   PageIds ids;
   for (;;) {
 #pragma unroll
@@ -434,72 +503,82 @@ __global__ __launch_bounds__(NW * 64) void mla_mfma_partial(Params p) {
     for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) st.acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.bad = false;
     load_ids(ids, bt, s * p.c, p1, p.nblocks, lane);
-    // The first AHEAD + 1 chunks are issued even past the split's end (those
-    // loads read the zero block), so the count in flight is known here and
-    // one wait retires the query loads, which are older: no wait inside the
-    // loop has to allow for them.
-    issue_chunk<NW>(ring.at<0>(), cbase, chunk_page_id(ids, bt, t0, 0, p1, p.nblocks, lane), t0, 0,
+    // The first two chunks are issued even past the split's end (those loads
+    // read the zero block), so the count in flight is known here and one wait
+    // retires the query loads, which are older: no wait inside the loop has to
+    // allow for them.
+    issue_chunk<NW>(slot(0), cbase, chunk_page_id(ids, bt, t0, 0, p1, p.nblocks, lane), t0, 0,
                     ctx, w, lane);
-    issue_chunk<NW>(ring.at<1>(), cbase, chunk_page_id(ids, bt, t0, 1, p1, p.nblocks, lane), t0, 1,
+    issue_chunk<NW>(slot(1), cbase, chunk_page_id(ids, bt, t0, 1, p1, p.nblocks, lane), t0, 1,
                     ctx, w, lane);
-    if constexpr (C::AHEAD >= 2)
-      issue_chunk<NW>(ring.at<2>(), cbase, chunk_page_id(ids, bt, t0, 2, p1, p.nblocks, lane), t0,
-                      2, ctx, w, lane);
-    constexpr int kInit = (C::AHEAD + 1) * C::NWI;
+    constexpr int kInit = 2 * C::NWI;
     wait_vm<kInit <= 63 ? kInit : 0>();
 
-    bool again = false;
-    for (int c0 = 0; c0 < nchunks; c0 += C::RING) {
-      again = mla_chunk<NW, HB, 0>(p, sm, ring, st, c0, nchunks, t0, ctx, cbase, bt, ids, p1, w,
-                                   lane);
-      if (again) break;
-      if (c0 + 1 < nchunks) {
-        again = mla_chunk<NW, HB, 1>(p, sm, ring, st, c0 + 1, nchunks, t0, ctx, cbase, bt, ids, p1,
-                                     w, lane);
-        if (again) break;
-      }
-      if (c0 + 2 < nchunks) {
-        again = mla_chunk<NW, HB, 2>(p, sm, ring, st, c0 + 2, nchunks, t0, ctx, cbase, bt, ids, p1,
-                                     w, lane);
-        if (again) break;
-      }
-      if constexpr (C::RING > 3) {
-        if (c0 + 3 < nchunks) {
-          again = mla_chunk<NW, HB, 3>(p, sm, ring, st, c0 + 3, nchunks, t0, ctx, cbase, bt, ids,
-                                       p1, w, lane);
-          if (again) break;
-        }
-      }
+    for (int ci = 0; ci < nchunks; ++ci) {
+      // chunk ci has landed (this wave's loads, then, after the barrier,
+      // every wave's); the probabilities of ci - 1 are complete; the value
+      // product of ci - 2 is done, so its slot can be refilled
+      if (ci + 1 < max(nchunks, 2)) wait_vm<C::NWI>(); else wait_vm<0>();
+      lds_barrier();
+      if (ci + 2 < nchunks)
+        issue_chunk<NW>(slot(ci + 2), cbase,
+                        chunk_page_id(ids, bt, t0, ci + 2, p1, p.nblocks, lane), t0, ci + 2, ctx,
+                        w, lane);
+      f32x4 sa[HB][2];
+      chunk_scores<NW, HB>(slot(ci), st, sa, lane);
+      const ValueOps<NW, HB> vo{slot(ci + kRing - 1), pslot(ci + 1), w, n, quad};
+      if (ci > 0)
+        values_and_softmax<NW, HB, true>(st, vo, sa, t0 + ci * kCT, ctx, cs, pslot(ci), w, lane);
+      else
+        values_and_softmax<NW, HB, false>(st, vo, sa, t0 + ci * kCT, ctx, cs, pslot(ci), w, lane);
     }
-    if (!again) break;
-    // Start over with the raised reference max: drain this wave's loads, wait
-    // for every wave (all have read the flag and finished their loads), then
-    // clear the flags before the next pass's first barrier.
-    wait_vm<0>();
+    if (nchunks > 0) {
+      lds_barrier();                                  // the last chunk's probabilities
+      const ValueOps<NW, HB> vo{slot(nchunks - 1), pslot(nchunks - 1), w, n, quad};
+      values_only<NW, HB>(st, vo);
+    }
+    // Did any head's chunk max overflow the headroom over its reference max?
+    // Every wave votes through LDS (the ring's first bytes: every load has
+    // landed and every read of the ring is done after the barrier).
+    wait_vm<0>();                                     // loads issued past the end of a short split
     lds_barrier();
-    if (w == 0 && lane == 0) sm.restart[0] = sm.restart[1] = 0;
+    int* votes = (int*)ring_lds;
+    if (lane == 0) votes[w] = __builtin_amdgcn_ballot_w64(st.bad) != 0;
+    lds_barrier();
+    int any = 0;
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) st.m[hb] = st.mtop[hb];
+    for (int i = 0; i < NW; ++i) any |= votes[i];
+    lds_barrier();                                    // votes read before the ring is refilled
+    if (__builtin_amdgcn_readfirstlane(any) == 0) break;
+    // Start over with every head's reference max raised to its largest chunk
+    // max: no chunk can overflow then, so this happens at most once.
+    st.m[0] = st.mtop[0];
+    if constexpr (HB == 2) st.m[1] = st.mtop[1];
   }
-  wait_vm<0>();   // loads issued past the end of a short split
+  // the accumulators are read by VALU below: cover the last MFMA's latency
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
-  // ---- finish: per-head statistics to every wave, normalise, write
+  // ---- finish: per-head statistics to every wave (in the ring's LDS, free
+  // now), normalise, write
+  float* stat_m = (float*)ring_lds;
+  float* stat_l = stat_m + C::NH;
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const float lt = sum_xor32(sum_xor16(st.l[hb]));
     if (quad == 0) {
       const int head = 16 * (HB * w + hb) + n;
-      *((lds_float*)sm.stat_m + head) = st.m[hb];
-      *((lds_float*)sm.stat_l + head) = lt;
+      stat_m[head] = st.m[hb];
+      stat_l[head] = lt;
     }
   }
   lds_barrier();
   const size_t row0 = (size_t)b * p.Hq + head0;
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
-    const float mm = *((const lds_float*)sm.stat_m + nb * 16 + n);
-    const float lt = *((const lds_float*)sm.stat_l + nb * 16 + n);
+    const float mm = stat_m[nb * 16 + n];
+    const float lt = stat_l[nb * 16 + n];
     const float inv = (mm == kNegInf) ? 0.f : 1.f / lt;
     const size_t row = row0 + nb * 16 + n;
 #pragma unroll
@@ -522,8 +601,8 @@ __global__ __launch_bounds__(NW * 64) void mla_mfma_partial(Params p) {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       const int head = 16 * (HB * w + hb) + n;
-      const float mm = *((const lds_float*)sm.stat_m + head);
-      const float lt = *((const lds_float*)sm.stat_l + head);
+      const float mm = stat_m[head];
+      const float lt = stat_l[head];
       const float lse = (mm == kNegInf) ? kNegInf : (mm + fast_log2(lt)) * kLn2;
       const size_t row = row0 + head;
       if (p.final_write) {
@@ -537,8 +616,9 @@ __global__ __launch_bounds__(NW * 64) void mla_mfma_partial(Params p) {
 
 template <int NW, int HB>
 hipError_t launch_cfg(const Params& p, hipStream_t st) {
-  dim3 grid(p.Hq / MlaCfg<NW, HB>::NH, p.S, p.B);
-  hipLaunchKernelGGL((mla_mfma_partial<NW, HB>), grid, dim3(NW * 64), 0, st, p);
+  const long blocks = (long)(p.Hq / MlaCfg<NW, HB>::NH) * p.S * p.B;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((mla_mfma_partial<NW, HB>), dim3((unsigned)blocks), dim3(NW * 64), 0, st, p);
   return hipGetLastError();
 }
 
@@ -546,12 +626,13 @@ hipError_t launch_cfg(const Params& p, hipStream_t st) {
 
 bool mla_mfma_supported(bool bf16, int Dqk, int Dv, int bs, int Hq) {
   return bf16 && Dqk == kDqk && Dv == kDv && bs == kBS &&
-         (Hq % 128 == 0 || Hq == 64 || Hq == 32 || Hq == 16);
+         (Hq % 64 == 0 || Hq == 32 || Hq == 16);
 }
 
+int mla_heads_per_workgroup(int Hq) { return Hq % 64 == 0 ? 64 : Hq; }
+
 hipError_t launch_mla_mfma(const Params& p, hipStream_t st) {
-  if (p.Hq % 128 == 0) return launch_cfg<4, 2>(p, st);
-  if (p.Hq == 64) return launch_cfg<4, 1>(p, st);
+  if (p.Hq % 64 == 0) return launch_cfg<4, 1>(p, st);
   if (p.Hq == 32) return launch_cfg<2, 1>(p, st);
   if (p.Hq == 16) return launch_cfg<1, 1>(p, st);
   return hipErrorInvalidValue;

@@ -82,7 +82,7 @@ typedef struct pa_shape {
   int32_t max_blocks_per_seq; /* row length of block_table */
   int32_t num_blocks;         /* pages in the pool */
   int32_t max_context_len;    /* host-side upper bound of context_lens; sizes the grid */
-  float scale;                /* score scale, e.g. 1/sqrt(head_dim) */
+  float scale;                /* score scale, finite and > 0, e.g. 1/sqrt(head_dim) */
   int32_t dtype;              /* pa_dtype of q, caches and out */
 } pa_shape;
 
