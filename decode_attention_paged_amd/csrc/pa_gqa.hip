@@ -164,8 +164,12 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
 
   const int npairs = (p1 - p0 + 1) >> 1;
   int k = w;
-  PairTile cur, nxt;
   auto issue = [&](PairTile& t, int kk) {
+    if (kk >= npairs) {                              // past the split: read zeros (L2)
+      const char* z = reinterpret_cast<const char*>(g_zero_tile);
+      load_pair(t, z, z, z, z, koff, voff, ksel, vsel);
+      return;
+    }
     const int pa_ = p0 + 2 * kk;
     const bool hasb = pa_ + 1 < p1;
     const int ida = clampi(bt[pa_], 0, p.nblocks - 1);
@@ -173,19 +177,31 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
     load_pair(t, kbase + ida * pstride, kbase + idb * pstride, vbase + ida * pstride,
               vbase + idb * pstride, koff, voff, ksel, vsel);
   };
-  if (k < npairs) issue(cur, k);
-  for (; k < npairs; k += NW) {
-    if (k + NW < npairs) issue(nxt, k + NW);
-    const int pa_ = p0 + 2 * k;
+  auto consume = [&](PairTile& t, int kk) {
+    const int pa_ = p0 + 2 * kk;
     const bool hasb = pa_ + 1 < p1;
     const bool partial = !hasb || (pa_ + 2) * kBS > ctx;
     const int mypage = vsel ? pa_ + 1 : pa_;
     const int tok0 = (vsel && !hasb) ? -1 : mypage * kBS + (quad & 1) * 8;
     if (partial)
-      consume_pair<true>(cur, qf, acc, m, l, p.scale_log2, tok0, ctx);
+      consume_pair<true>(t, qf, acc, m, l, p.scale_log2, tok0, ctx);
     else
-      consume_pair<false>(cur, qf, acc, m, l, p.scale_log2, tok0, ctx);
-    cur = nxt;
+      consume_pair<false>(t, qf, acc, m, l, p.scale_log2, tok0, ctx);
+  };
+  // Two register tiles in turn: while one pair is consumed the next one's
+  // loads are in flight, and each consume waits only for its own loads (a
+  // copy between tiles at the loop edge would wait for all of them).  Every
+  // step issues its loads, past the split's end from the zero tile, so the
+  // wait counts are the same on every path.
+  PairTile t0, t1;
+  issue(t0, k);
+  issue(t1, k + NW);
+  for (; k < npairs; k += 2 * NW) {
+    consume(t0, k);
+    issue(t0, k + 2 * NW);
+    if (k + NW >= npairs) break;
+    consume(t1, k + NW);
+    issue(t1, k + 3 * NW);
   }
   const float ltot = sum_xor32(sum_xor16(l));
 

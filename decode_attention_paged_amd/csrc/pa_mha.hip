@@ -201,24 +201,34 @@ __global__ __launch_bounds__(NW * 64) void mha_valu_partial(Params p) {
 #pragma unroll
   for (int j = 0; j < C::DPL; ++j) st.acc[j] = 0.f;
 
-  int pg = p0 + w;
-  MhaTile<BF16, D, BS> cur, nxt;
-  if (pg < p1) {
-    const int id = clampi(bt[pg], 0, p.nblocks - 1);
-    load_tile(cur, kbase + id * kstride, vbase + id * vstride, lane);
-  }
-  for (; pg < p1; pg += NW) {
-    const int pn = pg + NW;
-    if (pn < p1) {
-      const int id = clampi(bt[pn], 0, p.nblocks - 1);
-      load_tile(nxt, kbase + id * kstride, vbase + id * vstride, lane);
+  auto issue = [&](MhaTile<BF16, D, BS>& t, int pg) {
+    if (pg >= p1) {                                  // past the split: read zeros (L2)
+      const char* z = reinterpret_cast<const char*>(g_zero_tile);
+      load_tile(t, z, z, lane);
+      return;
     }
+    const int id = clampi(bt[pg], 0, p.nblocks - 1);
+    load_tile(t, kbase + id * kstride, vbase + id * vstride, lane);
+  };
+  auto consume = [&](MhaTile<BF16, D, BS>& t, int pg) {
     const int nvalid = ctx - pg * BS;
     if (nvalid >= BS)
-      consume_tile<BF16, D, BS, false>(cur, st, qv, qf, p.scale_log2, lane, BS);
+      consume_tile<BF16, D, BS, false>(t, st, qv, qf, p.scale_log2, lane, BS);
     else
-      consume_tile<BF16, D, BS, true>(cur, st, qv, qf, p.scale_log2, lane, nvalid);
-    cur = nxt;
+      consume_tile<BF16, D, BS, true>(t, st, qv, qf, p.scale_log2, lane, nvalid);
+  };
+  // Two register tiles in turn (see the grouped-query kernel): each consume
+  // waits only for its own tile's loads; tiles past the split read zeros.
+  int pg = p0 + w;
+  MhaTile<BF16, D, BS> t0, t1;
+  issue(t0, pg);
+  issue(t1, pg + NW);
+  for (; pg < p1; pg += 2 * NW) {
+    consume(t0, pg);
+    issue(t0, pg + 2 * NW);
+    if (pg + NW >= p1) break;
+    consume(t1, pg + NW);
+    issue(t1, pg + 3 * NW);
   }
   const float ltot = across_rows_sum<C::LPR>(st.l);
 
