@@ -6,7 +6,10 @@
 One step = one decode-attention call over a batch: the split-KV partial
 kernel and the log-sum-exp reduction (pa_decode_partial + pa_reduce, which is
 exactly what pa_decode launches).  Inputs are seeded synthetic workloads that
-are already resident in HBM when the timed region starts.  The partial
+are already resident in HBM when the timed region starts; `value` comes from
+back-to-back steps, and `cold_call_ms` gives per-call times with L2 and the
+MALL flushed before each call (a 1 GiB rewrite outside the timed interval).
+The partial
 kernel, the dominant one, is also timed on its own with HIP events on the
 stream it is launched on; its algorithmic KV-read bytes per launch divided by
 that average duration give the achieved HBM bandwidth reported against the
@@ -205,6 +208,32 @@ class Case:
             r["reduce_ms"], _ = self._loop(self.reduce, steps)
         return r
 
+    def cold(self, calls: int, flush_bytes: int = 1 << 30):
+        """Per-call times with L2 and the 256 MB MALL flushed before each call.
+
+        A 1 GiB buffer is rewritten before every call (outside the timed
+        interval); HIP events on the launch stream bracket the call alone.
+        Returns (median, p10, p90) in ms.
+        """
+        import torch
+
+        flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+        evs = []
+        for i in range(calls):
+            flush.fill_(float(i))
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            self.step()
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in evs)
+        del flush
+        torch.cuda.empty_cache()
+        q = lambda f: t[min(len(t) - 1, int(f * len(t)))]
+        return q(0.5), q(0.1), q(0.9)
+
     def summary(self, r):
         frac = (self.kv_bytes / (r["partial_ms"] * 1e-3) / 1e9) / PEAK_HBM_GBS
         d = dict(
@@ -221,6 +250,10 @@ class Case:
             kv_gbps_step=round(self.kv_bytes / (r["ms_per_step"] * 1e-3) / 1e9, 1),
             frac_of_peak_partial=round(frac, 4),
         )
+        if "cold_ms" in r:
+            med, p10, p90 = r["cold_ms"]
+            d["cold_call_ms"] = {"median": round(med, 5), "p10": round(p10, 5), "p90": round(p90, 5)}
+            d["cold_kv_gbps"] = round(self.kv_bytes / (med * 1e-3) / 1e9, 1)
         if self.mla:
             d["mfma_tflops_partial"] = round(self.flops() / (r["partial_ms"] * 1e-3) / 1e12, 1)
             d["mfma_frac_of_bf16_peak"] = round(d["mfma_tflops_partial"] / PEAK_BF16_TFLOPS, 4)
@@ -295,6 +328,8 @@ def main():
 
     main_case = Case(args.config)
     r = main_case.time(args.steps, args.warmup)
+    if not args.only:
+        r["cold_ms"] = main_case.cold(min(args.steps, 50))
     main_sum = main_case.summary(r)
     inp = main_case.inp
 
@@ -330,6 +365,7 @@ def main():
                 continue
             c = Case(name)
             rr = c.time(max(20, args.steps // 4), max(5, args.warmup // 2))
+            rr["cold_ms"] = c.cold(20)
             per_config[name] = c.summary(rr)
             c.free()
             del c
@@ -363,6 +399,7 @@ def main():
             "parallelism": "single GPU",
         },
         "kv_gbps_step": main_sum["kv_gbps_step"],
+        "cold_call_ms": main_sum.get("cold_call_ms"),
         "kv_frac_of_peak_step": round(main_sum["kv_gbps_step"] / PEAK_HBM_GBS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,

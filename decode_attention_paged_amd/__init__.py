@@ -24,7 +24,7 @@ from ._lib import PaError, PaShape  # noqa: F401
 
 __all__ = [
     "decode", "decode_mla", "decode_partial", "decode_mla_partial", "reduce",
-    "choose_num_splits", "workspace_size", "workspace_init", "make_shape", "PaError",
+    "append_kv", "append_latent", "choose_num_splits", "workspace_size", "workspace_init", "make_shape", "PaError",
     "library_path",
 ]
 
@@ -211,3 +211,60 @@ def reduce(shape: PaShape, context_lens, num_splits, workspace, out, lse, mla=Fa
                                _ptr(workspace), _nbytes(workspace),
                                _ptr(out), _ptr(lse), _stream(stream))
     _lib.check(st, "pa_reduce")
+
+
+def append_kv(k_new, v_new, k_cache, v_cache, block_table, context_lens, stream=None):
+    """Write one new token per sequence into the paged K/V cache.
+
+    k_new [B][Hkv][D], v_new [B][Hkv][Dv]; the token goes to position
+    context_lens[b] (the length before the append).  context_lens is not
+    changed: the caller increments it before decoding the new token.
+    """
+    _need(k_new, "k_new", ndim=3)
+    if k_new.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {k_new.dtype}")
+    dev = k_new.device
+    _need(v_new, "v_new", k_new.dtype, 3, dev)
+    _need(k_cache, "k_cache", k_new.dtype, 4, dev)
+    _need(v_cache, "v_cache", k_new.dtype, 4, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    B, Hkv, D = k_new.shape
+    nb, Hk, bs, Dk = k_cache.shape
+    Dv = v_new.shape[2]
+    if (Hk, Dk) != (Hkv, D) or tuple(v_new.shape[:2]) != (B, Hkv):
+        raise ValueError("k_new / v_new do not match the cache heads or dims")
+    if tuple(v_cache.shape) != (nb, Hkv, Dv, bs):
+        raise ValueError("v_cache must be [num_blocks][Hkv][Dv][bs]")
+    if block_table.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_table / context_lens batch differs from k_new")
+    shape = make_shape(batch=B, num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=D, head_dim_v=Dv,
+                       block_size=bs, max_blocks_per_seq=block_table.shape[1], num_blocks=nb,
+                       max_context_len=0, scale=1.0, dtype=k_new.dtype)
+    st = _lib.load().pa_append_kv(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                  _ptr(v_cache), _ptr(block_table), _ptr(context_lens),
+                                  _stream(stream))
+    _lib.check(st, "pa_append_kv")
+
+
+def append_latent(c_new, kv_cache, block_table, context_lens, stream=None):
+    """MLA: write one new latent row per sequence (c_new [B][D]) into the paged cache."""
+    _need(c_new, "c_new", ndim=2)
+    if c_new.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {c_new.dtype}")
+    dev = c_new.device
+    _need(kv_cache, "kv_cache", c_new.dtype, 3, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    B, D = c_new.shape
+    nb, bs, Dc = kv_cache.shape
+    if Dc != D:
+        raise ValueError("c_new width differs from kv_cache")
+    if block_table.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_table / context_lens batch differs from c_new")
+    shape = make_shape(batch=B, num_q_heads=1, num_kv_heads=1, head_dim=D, head_dim_v=D,
+                       block_size=bs, max_blocks_per_seq=block_table.shape[1], num_blocks=nb,
+                       max_context_len=0, scale=1.0, dtype=c_new.dtype)
+    st = _lib.load().pa_append_latent(ctypes.byref(shape), _ptr(c_new), _ptr(kv_cache),
+                                      _ptr(block_table), _ptr(context_lens), _stream(stream))
+    _lib.check(st, "pa_append_latent")

@@ -50,6 +50,8 @@ SIGNATURES = {
     "pa_decode_partial": (_I32, [_SH, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "pa_decode_mla_partial": (_I32, [_SH, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "pa_reduce": (_I32, [_SH, _P, _I32, _I32, _P, _SZ, _P, _P, _P]),
+    "pa_append_kv": (_I32, [_SH, _P, _P, _P, _P, _P, _P, _P]),
+    "pa_append_latent": (_I32, [_SH, _P, _P, _P, _P, _P]),
 }
 
 _lib = None

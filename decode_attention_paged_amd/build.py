@@ -33,7 +33,7 @@ COMMON_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
-SOURCES = ["pa_api.hip", "pa_mha.hip", "pa_gqa.hip", "pa_mla.hip", "pa_reduce.hip"]
+SOURCES = ["pa_api.hip", "pa_mha.hip", "pa_gqa.hip", "pa_mla.hip", "pa_reduce.hip", "pa_append.hip"]
 
 
 def hipcc() -> str:

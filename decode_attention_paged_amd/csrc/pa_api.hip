@@ -338,4 +338,50 @@ pa_status pa_decode_mla(const pa_shape* shape, const void* q, const void* kv_cac
   return reduce ? run_reduce(shape, context_lens, S, workspace, out, lse, stream) : PA_OK;
 }
 
+
+// Shape checks of the append entry points: the decode's basic checks, without
+// kernel support or scale (the append moves bytes only).
+static pa_status check_append_shape(const pa_shape* s, bool mla) {
+  if (!s) return PA_ERR_INVALID;
+  if (s->batch > 65535) return PA_ERR_UNSUPPORTED;   // grid y limit
+  if (s->batch < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1 || s->head_dim < 1 ||
+      s->head_dim_v < 1 || s->block_size < 1 || s->max_blocks_per_seq < 1 || s->num_blocks < 1)
+    return PA_ERR_INVALID;
+  if (s->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;   // grid x limit
+  if (s->dtype != PA_F32 && s->dtype != PA_BF16) return PA_ERR_INVALID;
+  if (mla && s->num_kv_heads != 1) return PA_ERR_INVALID;
+  return PA_OK;
+}
+
+pa_status pa_append_kv(const pa_shape* shape, const void* k_new, const void* v_new, void* k_cache,
+                       void* v_cache, const int32_t* block_table, const int32_t* context_lens,
+                       void* stream) {
+  const pa_status st = check_append_shape(shape, false);
+  if (st != PA_OK) return st;
+  if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !context_lens)
+    return PA_ERR_INVALID;
+  const pa_shape& s = *shape;
+  pa::AppendParams a{k_new, v_new, k_cache, v_cache, block_table, context_lens,
+                     s.batch, s.num_kv_heads, s.head_dim, s.head_dim_v, s.block_size,
+                     s.max_blocks_per_seq, s.num_blocks};
+  const hipError_t e =
+      pa::launch_append(a, s.dtype == PA_BF16, false, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_append_latent(const pa_shape* shape, const void* c_new, void* kv_cache,
+                           const int32_t* block_table, const int32_t* context_lens,
+                           void* stream) {
+  const pa_status st = check_append_shape(shape, true);
+  if (st != PA_OK) return st;
+  if (!c_new || !kv_cache || !block_table || !context_lens) return PA_ERR_INVALID;
+  const pa_shape& s = *shape;
+  pa::AppendParams a{c_new, nullptr, kv_cache, nullptr, block_table, context_lens,
+                     s.batch, 1, s.head_dim, 0, s.block_size, s.max_blocks_per_seq,
+                     s.num_blocks};
+  const hipError_t e =
+      pa::launch_append(a, s.dtype == PA_BF16, true, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 }  // extern "C"

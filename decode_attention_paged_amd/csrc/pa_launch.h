@@ -34,6 +34,19 @@ hipError_t launch_mla_mfma(const Params& p, hipStream_t st);
 hipError_t launch_reduce(const Params& p, bool bf16, hipStream_t st);
 hipError_t launch_zero_i32(int32_t* dst, size_t n, hipStream_t st);
 
+// Arguments of the paged KV append (MLA: k_new / k_cache are the latent
+// row and pool, v_* unused, D the latent width).
+struct AppendParams {
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  int B, Hkv, D, Dv, bs, maxb, nblocks;
+};
+hipError_t launch_append(const AppendParams& a, bool bf16, bool mla, hipStream_t st);
+
 // Which kernels exist (host-side predicates used by validation and dispatch).
 bool mha_valu_supported(bool bf16, int D, int bs);
 bool gqa_mfma_supported(bool bf16, int D, int Dv, int bs, int G);

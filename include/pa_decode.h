@@ -181,6 +181,38 @@ pa_status pa_reduce(const pa_shape* shape, const int32_t* context_lens, int32_t 
                     int32_t mla, const void* workspace, size_t workspace_bytes, void* out,
                     float* lse, void* stream);
 
+/*
+ * Paged KV append: write one new token per sequence into the cache at the
+ * position that token takes, the step that precedes a decode call (page 1,
+ * vLLM README snippets: KV memory managed in fixed pages through a block
+ * table).  With n = context_lens[b], the length BEFORE the append:
+ *     page = block_table[b * max_blocks_per_seq + n / block_size]
+ *     slot = n % block_size
+ *     k_cache[page][g][slot][:]  = k_new[b][g][:]        g < num_kv_heads
+ *     v_cache[page][g][:][slot]  = v_new[b][g][:]
+ * after which a decode with context_lens[b] + 1 sees the token.  The caller
+ * increments context_lens; the library does not.  k_new is
+ * [batch][num_kv_heads][head_dim], v_new [batch][num_kv_heads][head_dim_v],
+ * both dtype, device memory.  A sequence whose n is negative or not below
+ * max_blocks_per_seq * block_size, or whose page id is outside
+ * [0, num_blocks), writes nothing.  Any head dims; no workspace; scale and
+ * num_q_heads are not used.  Errors: PA_ERR_INVALID for a bad shape or a NULL
+ * pointer, PA_ERR_UNSUPPORTED for batch or num_kv_heads above 65535,
+ * PA_ERR_HIP for a failed launch.
+ */
+pa_status pa_append_kv(const pa_shape* shape, const void* k_new, const void* v_new,
+                       void* k_cache, void* v_cache, const int32_t* block_table,
+                       const int32_t* context_lens, void* stream);
+
+/*
+ * MLA variant: kv_cache[page][slot][:] = c_new[b][:], c_new [batch][head_dim]
+ * (the whole latent row: keys and values come from the same memory).
+ * num_kv_heads must be 1.  Otherwise as pa_append_kv.
+ */
+pa_status pa_append_latent(const pa_shape* shape, const void* c_new, void* kv_cache,
+                           const int32_t* block_table, const int32_t* context_lens,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,6 +9,9 @@ passages it follows.  Every function here is pinned by ``tests/test_oracle.py``
 """
 
 from .decode_ref import (  # noqa: F401
+    append_kv,
+    append_latent,
+    append_slot,
     as_f64,
     attend,
     bf16_bits_to_f64,

@@ -308,3 +308,49 @@ def decode_inputs(inp, heads=None):
                                 dv=inp.head_dim_v, dtype=inp.dtype, heads=heads)
     return paged_decode(inp.q, inp.k_pages, inp.v_pages, bt, inp.context_lens, inp.scale,
                         dtype=inp.dtype, heads=heads)
+
+
+# ---------------------------------------------------------------------------
+# Paged KV append (the step before decode: the new token's K/V rows go to the
+# page and slot its position selects; page 1, vLLM README snippets on KV
+# memory managed in pages through a block table).
+# ---------------------------------------------------------------------------
+
+def append_slot(block_table_row: np.ndarray, n: int, bs: int):
+    """(page, slot) where the token at position n lives, or None when the
+    position is outside the block table or the table entry is negative."""
+    if n < 0 or n >= len(block_table_row) * bs:
+        return None
+    page = int(block_table_row[n // bs])
+    if page < 0:
+        return None
+    return page, n % bs
+
+
+def append_kv(k_pool, v_pool, block_table, context_lens, k_new, v_new):
+    """Copies of the K/V pools with row k_new[b] / v_new[b] written at position
+    context_lens[b] of every sequence.  Layouts: k_pool [pages][Hkv][bs][D],
+    v_pool [pages][Hkv][Dv][bs]; k_new [B][Hkv][D], v_new [B][Hkv][Dv].  The
+    elements are moved as they are (bits for bf16)."""
+    k_out, v_out = k_pool.copy(), v_pool.copy()
+    bs = k_pool.shape[2]
+    for b in range(len(context_lens)):
+        loc = append_slot(block_table[b], int(context_lens[b]), bs)
+        if loc is None:
+            continue
+        page, slot = loc
+        k_out[page, :, slot, :] = k_new[b]
+        v_out[page, :, :, slot] = v_new[b]
+    return k_out, v_out
+
+
+def append_latent(c_pool, block_table, context_lens, c_new):
+    """MLA: a copy of the latent pool [pages][bs][D] with c_new[b] written at
+    position context_lens[b] of every sequence."""
+    out = c_pool.copy()
+    bs = c_pool.shape[1]
+    for b in range(len(context_lens)):
+        loc = append_slot(block_table[b], int(context_lens[b]), bs)
+        if loc is not None:
+            out[loc[0], loc[1], :] = c_new[b]
+    return out

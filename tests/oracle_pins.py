@@ -344,9 +344,85 @@ def pin_sampled_heads(o):
         assert np.array_equal(so[b, h], out[b, h]) and sl[b, h] == lse[b, h]
 
 
+def _nan_equal(a, b):
+    return np.array_equal(np.isnan(a), np.isnan(b)) and np.array_equal(a[~np.isnan(a)], b[~np.isnan(b)])
+
+
+def pin_append_then_decode(o):
+    """Append: removing each sequence's last token (NaN in its slot) and
+    appending it back restores the pools exactly, and decoding at ctx + 1 then
+    matches the pure-Python brute force.  Positions cover a new page (4 with
+    bs = 4), a page's last slot (15) and the first token (0)."""
+    full = [5, 16, 1]
+    q, k, v, bt, ctx, scale = tiny_paged(53, 3, 4, 2, 6, 5, 4, full)
+    before = ctx - 1
+    k0, v0 = k.copy(), v.copy()
+    k_new = np.zeros((3, 2, 6))
+    v_new = np.zeros((3, 2, 5))
+    for b in range(3):
+        n = int(before[b])
+        page, slot = bt[b, n // 4], n % 4
+        k_new[b], v_new[b] = k[page, :, slot, :], v[page, :, :, slot]
+        k0[page, :, slot, :] = np.nan
+        v0[page, :, :, slot] = np.nan
+    k1, v1 = o.append_kv(k0, v0, bt, before, k_new, v_new)
+    assert _nan_equal(k1, k) and _nan_equal(v1, v)
+    assert np.isnan(k0).any() and not np.isnan(k1).any()        # the inputs are not modified
+    out, lse = o.paged_decode(q, k1, v1, bt, ctx, scale, dtype="f64")
+    bo, bl = brute_force(q, k, v, bt, ctx, scale)
+    _close(out, bo, what="append out")
+    _close(lse, bl, what="append lse")
+
+
+def pin_append_out_of_range(o):
+    """A position past the block table, a negative one, or a -1 table entry
+    writes nothing."""
+    q, k, v, bt, ctx, scale = tiny_paged(54, 3, 2, 1, 4, 4, 4, [8, 3, 2])
+    bt = bt.copy()
+    bt[2, 0] = -1
+    pos = np.array([8, -1, 1])                 # 8 = 2 pages x 4 slots: table full
+    k_new = np.ones((3, 1, 4))
+    v_new = np.ones((3, 1, 4))
+    k1, v1 = o.append_kv(k, v, bt, pos, k_new, v_new)
+    assert np.array_equal(k1, k) and np.array_equal(v1, v)
+
+
+def pin_append_latent(o):
+    """MLA append restores the latent pool, and the latent decode at ctx + 1
+    then matches the MQA reading decoded by brute force."""
+    rng = np.random.default_rng(55)
+    bs, Dc, dv = 4, 6, 4
+    full = [4, 7]
+    n_pages = [-(-c // bs) for c in full]
+    perm = rng.permutation(sum(n_pages) + 2)
+    bt = np.full((2, max(n_pages)), -1, dtype=np.int64)
+    bt[0, :n_pages[0]] = perm[:n_pages[0]]
+    bt[1, :n_pages[1]] = perm[n_pages[0]:n_pages[0] + n_pages[1]]
+    c = rng.standard_normal((len(perm), bs, Dc))
+    q = rng.standard_normal((2, 3, Dc))
+    ctx = np.asarray(full)
+    before = ctx - 1
+    c0 = c.copy()
+    c_new = np.zeros((2, Dc))
+    for b in range(2):
+        n = int(before[b])
+        page, slot = bt[b, n // bs], n % bs
+        c_new[b] = c[page, slot]
+        c0[page, slot] = np.nan
+    c1 = o.append_latent(c0, bt, before, c_new)
+    assert _nan_equal(c1, c)
+    out, lse = o.paged_decode_mla(q, c1, bt, ctx, 0.4, dv=dv, dtype="f64")
+    k = c[:, None, :, :]                                  # MQA: one KV head, K = whole row
+    v = np.transpose(c[:, :, :dv], (0, 2, 1))[:, None]    # V = leading dv entries, [D][bs]
+    bo, bl = brute_force(q, k, v, bt, ctx, 0.4)
+    _close(out, bo, what="latent append out")
+    _close(lse, bl, what="latent append lse")
+
+
 ALL_PINS = [
     pin_bruteforce, pin_mla_bruteforce, pin_bf16_widening, pin_sdpa, pin_ctx_one,
     pin_identical_keys, pin_two_token_closed_form, pin_split_invariance,
     pin_page_permutation, pin_constant_values, pin_stability, pin_score_shift,
     pin_gqa_equals_mha, pin_mla_equals_mqa, pin_batch_independence, pin_sampled_heads,
+    pin_append_then_decode, pin_append_out_of_range, pin_append_latent,
 ]

@@ -173,3 +173,42 @@ def test_split_heuristic_fills_the_gpu(lib):
 def test_split_heuristic_invalid_shape(lib):
     s = shape(batch=0)
     assert lib.pa_choose_num_splits(ctypes.byref(s), 256, 0) == 0
+
+
+# ----------------------------------------------------------------------------
+# Paged KV append: validation only (no launch)
+# ----------------------------------------------------------------------------
+
+def append(lib, s, *, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, ctx=FAKE):
+    return lib.pa_append_kv(ctypes.byref(s) if s is not None else None, kn, vn, kc, vc, bt, ctx,
+                            NULL)
+
+
+def append_latent(lib, s, *, cn=FAKE, cc=FAKE, bt=FAKE, ctx=FAKE):
+    return lib.pa_append_latent(ctypes.byref(s) if s is not None else None, cn, cc, bt, ctx, NULL)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("batch", 0), ("num_kv_heads", 0), ("head_dim", 0), ("head_dim_v", -3), ("block_size", 0),
+    ("max_blocks_per_seq", 0), ("num_blocks", 0), ("dtype", 5),
+])
+def test_append_invalid_shapes(lib, field, value):
+    assert append(lib, shape(**{field: value})) == _lib.PA_ERR_INVALID
+
+
+def test_append_null_pointers(lib):
+    assert append(lib, None) == _lib.PA_ERR_INVALID
+    s = shape()
+    for kw in ("kn", "vn", "kc", "vc", "bt", "ctx"):
+        assert append(lib, s, **{kw: NULL}) == _lib.PA_ERR_INVALID, kw
+    ms = shape(num_q_heads=16, num_kv_heads=1, head_dim=576, head_dim_v=512, block_size=64)
+    assert append_latent(lib, None) == _lib.PA_ERR_INVALID
+    for kw in ("cn", "cc", "bt", "ctx"):
+        assert append_latent(lib, ms, **{kw: NULL}) == _lib.PA_ERR_INVALID, kw
+    # the latent pool has one KV head
+    assert append_latent(lib, shape(num_kv_heads=2, num_q_heads=2)) == _lib.PA_ERR_INVALID
+
+
+def test_append_grid_limits(lib):
+    assert append(lib, shape(batch=70000)) == _lib.PA_ERR_UNSUPPORTED
+    assert append(lib, shape(num_kv_heads=70000, num_q_heads=70000)) == _lib.PA_ERR_UNSUPPORTED

@@ -184,6 +184,28 @@ def _split_ranges_gap(num_pages, c, ns):
     return [(min(num_pages, s * c + (1 if s else 0)), min(num_pages, (s + 1) * c)) for s in range(ns)]
 
 
+def _append_slot_off_by_one(bt_row, n, bs):
+    if n < 0 or n >= len(bt_row) * bs or bt_row[n // bs] < 0:
+        return None
+    return int(bt_row[n // bs]), (n + 1) % bs
+
+
+def _append_slot_previous_page(bt_row, n, bs):
+    if n < 0 or n >= len(bt_row) * bs or bt_row[n // bs] < 0:
+        return None
+    return int(bt_row[max(0, n // bs - 1)]), n % bs
+
+
+def _append_slot_no_table_check(bt_row, n, bs):
+    if n < 0 or n >= len(bt_row) * bs:
+        return None
+    return int(bt_row[n // bs]), n % bs
+
+
+def _append_kv_skips_last(k_pool, v_pool, bt, ctx, k_new, v_new):
+    return ref._orig_append_kv(k_pool, v_pool, bt[:-1], ctx[:-1], k_new[:-1], v_new[:-1])
+
+
 MUTANTS = {
     "scores_noscale": ("scores", _scores_noscale),
     "scores_negated": ("scores", _scores_negated),
@@ -208,6 +230,10 @@ MUTANTS = {
     "chunk_l_not_rescaled": ("chunk_partial", _chunk_l_not_rescaled),
     "split_ranges_overlap": ("split_page_ranges", _split_ranges_overlap),
     "split_ranges_gap": ("split_page_ranges", _split_ranges_gap),
+    "append_slot_off_by_one": ("append_slot", _append_slot_off_by_one),
+    "append_slot_previous_page": ("append_slot", _append_slot_previous_page),
+    "append_slot_no_table_check": ("append_slot", _append_slot_no_table_check),
+    "append_kv_skips_last_sequence": ("append_kv", _append_kv_skips_last),
 }
 
 
@@ -216,6 +242,7 @@ def test_mutant_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
     monkeypatch.setitem(ref.__dict__, "_orig_attend", ref.attend)
     monkeypatch.setitem(ref.__dict__, "_orig_gather_kv", ref.gather_kv)
+    monkeypatch.setitem(ref.__dict__, "_orig_append_kv", ref.append_kv)
     monkeypatch.setattr(ref, attr, fn)
     caught = []
     for pin in ALL_PINS:
