@@ -128,22 +128,26 @@ class Case:
         out, lse = P(self.out.data_ptr()), P(self.lse.data_ptr())
         bt, ctx = P(t["block_table"].data_ptr()), P(t["context_lens"].data_ptr())
         q = P(t["q"].data_ptr())
-        # MHA/GQA: pa_decode is one launch (the last workgroup of each unit
-        # merges the splits).  MLA: pa_decode_mla launches the partial kernel
-        # and the reduction; they are called here one by one so that each can
-        # be timed.
-        self.fused = not self.mla
+        # A decode call is one launch when the splits merge inside the partial
+        # kernel (MHA/GQA with small per-unit partials), else the partial
+        # kernel and the reduction (pa_decode_launches says which).  Two-launch
+        # calls are made here as the two calls they consist of, so that each
+        # kernel can be timed alone.
+        self.fused = pa.decode_launches(self.shape, self.S, self.mla) == 1
         if self.mla:
             kv = P(t["kv_cache"].data_ptr())
             self._partial = (lib.pa_decode_mla_partial,
                              (sh, q, kv, bt, ctx, self.S, out, lse, ws, wsb, stream))
-            self._reduce = (lib.pa_reduce,
-                            (sh, ctx, self.S, int(self.mla), ws, wsb, out, lse, stream))
         else:
             k, v = P(t["k_cache"].data_ptr()), P(t["v_cache"].data_ptr())
-            self._partial = (lib.pa_decode,
-                             (sh, q, k, v, bt, ctx, self.S, out, lse, ws, wsb, stream))
-            self._reduce = None
+            if self.fused:
+                self._partial = (lib.pa_decode,
+                                 (sh, q, k, v, bt, ctx, self.S, out, lse, ws, wsb, stream))
+            else:
+                self._partial = (lib.pa_decode_partial,
+                                 (sh, q, k, v, bt, ctx, self.S, out, lse, ws, wsb, stream))
+        self._reduce = None if self.fused else (
+            lib.pa_reduce, (sh, ctx, self.S, int(self.mla), ws, wsb, out, lse, stream))
         self.kv_bytes = inp.kv_bytes_read()
         self.tokens = int(inp.context_lens.astype("int64").sum())
 
@@ -351,7 +355,7 @@ def main():
         "frac": round(achieved / PEAK_HBM_GBS, 4),
         "traffic": traffic,
         "kernel": (f"{main_case.family} split-KV kernel with fused reduction" if main_case.fused
-                   else f"{main_case.family} partial kernel"),
+                   else f"{main_case.family} partial kernel (the reduction is a second launch)"),
         "algorithmic_bytes_per_launch": main_case.kv_bytes,
         "avg_launch_ms": round(r["partial_ms"], 5),
     }

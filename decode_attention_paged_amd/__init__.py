@@ -24,7 +24,7 @@ from ._lib import PaError, PaShape  # noqa: F401
 
 __all__ = [
     "decode", "decode_mla", "decode_partial", "decode_mla_partial", "reduce",
-    "append_kv", "append_latent", "choose_num_splits", "workspace_size", "workspace_init", "make_shape", "PaError",
+    "append_kv", "append_latent", "choose_num_splits", "decode_launches", "workspace_size", "workspace_init", "make_shape", "PaError",
     "library_path",
 ]
 
@@ -122,6 +122,14 @@ def choose_num_splits(shape: PaShape, num_cus: int = 0, mla: bool = False) -> in
     if s <= 0:
         raise PaError(_lib.PA_ERR_INVALID, "pa_choose_num_splits")
     return s
+
+
+def decode_launches(shape: PaShape, num_splits: int = 0, mla: bool = False) -> int:
+    """Kernel launches one decode call makes (1: fused or a single split; 2: + reduction)."""
+    n = _lib.load().pa_decode_launches(ctypes.byref(shape), int(num_splits), int(mla))
+    if n <= 0:
+        raise PaError(_lib.PA_ERR_INVALID, "pa_decode_launches")
+    return n
 
 
 def workspace_size(shape: PaShape, num_splits: int = 0, mla: bool = False) -> int:

@@ -43,6 +43,7 @@ SIGNATURES = {
     "pa_status_string": (ctypes.c_char_p, [_I32]),
     "pa_version": (_I32, []),
     "pa_choose_num_splits": (_I32, [_SH, _I32, _I32]),
+    "pa_decode_launches": (_I32, [_SH, _I32, _I32]),
     "pa_decode_workspace_size": (_SZ, [_SH, _I32, _I32]),
     "pa_workspace_init": (_I32, [_SH, _I32, _I32, _P, _SZ, _P]),
     "pa_decode": (_I32, [_SH, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),

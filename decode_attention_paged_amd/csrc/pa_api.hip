@@ -12,6 +12,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 65535;          // grid y limit
+constexpr long kFusedMergeBytes = 4 * 1024;   // largest per-unit partial set merged in-kernel
 constexpr double kSplitBytesValu = 128.0 * 1024.0;   // KV bytes per workgroup, VALU kernel
 constexpr double kSplitBytesMfma = 1024.0 * 1024.0;  // KV bytes per workgroup, MFMA kernel
 
@@ -184,6 +185,20 @@ pa::Params make_params(const pa_shape& s, int S, const void* q, const void* k, c
   return p;
 }
 
+// Whether pa_decode merges in-kernel for this shape and split count.  The
+// fused merge costs every workgroup a device-scope arrival atomic (a round
+// trip it waits for) and leaves the merge to the last workgroup of each unit
+// as a serial tail; a separate reduction launch merges all units in parallel
+// for a few microseconds.  Measured on MI355X, the separate launch wins from
+// 8 KiB of partials per unit up (batch 16 x 32 heads at 16 splits: 110 us
+// against 116 us), so only tiny merges stay in-kernel.
+bool fuses(const pa_shape& s, int S, Kernel kern) {
+  if (S <= 1 || kern == Kernel::MlaMfma || kern == Kernel::None) return false;
+  const long unit_heads = kern == Kernel::GqaMfma ? s.num_q_heads / s.num_kv_heads : 1;
+  const long merge_bytes = (long)S * unit_heads * (s.head_dim_v + 1) * 4;
+  return merge_bytes <= kFusedMergeBytes;
+}
+
 // Launch the partial kernel.  With `fused` (and a kernel that supports it)
 // the last workgroup of every (sequence, head unit) also merges the splits,
 // so no reduction launch is needed; *needs_reduce tells the caller.
@@ -204,7 +219,11 @@ pa_status run_partial(const pa_shape* shape, const void* q, const void* k, const
   if (S > 1 && (!ws || ws_bytes < workspace_bytes_for(*shape, S))) return PA_ERR_WORKSPACE;
   pa::Params p = make_params(*shape, S, q, k, mla ? k : v, bt, ctx, out, lse, ws);
   const Kernel kern = pick_kernel(*shape, mla);
-  p.fused = (fused && S > 1 && kern != Kernel::MlaMfma) ? 1 : 0;
+  // The fused merge runs in the last workgroup of each unit, after every
+  // other split of the unit: cheap when the unit's partials are small, a
+  // serial tail when they are large.  Above kFusedMergeBytes per unit the
+  // separate reduction launch (all units in parallel) is faster.
+  p.fused = (fused && fuses(*shape, S, kern)) ? 1 : 0;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (kern) {
@@ -244,6 +263,14 @@ const char* pa_status_string(int32_t status) {
 }
 
 int32_t pa_version(void) { return 100; }
+
+int32_t pa_decode_launches(const pa_shape* shape, int32_t num_splits, int32_t mla) {
+  if (check_shape(shape, mla != 0) != PA_OK) return 0;
+  const int S = resolve_splits(*shape, num_splits, mla != 0);
+  if (S < 1) return 0;
+  if (S == 1) return 1;
+  return fuses(*shape, S, pick_kernel(*shape, mla != 0)) ? 1 : 2;
+}
 
 int32_t pa_choose_num_splits(const pa_shape* shape, int32_t num_cus, int32_t mla) {
   if (check_shape(shape, mla != 0) != PA_OK) return 0;

@@ -105,6 +105,15 @@ int32_t pa_version(void);
 int32_t pa_choose_num_splits(const pa_shape* shape, int32_t num_cus, int32_t mla);
 
 /*
+ * Kernel launches a pa_decode / pa_decode_mla call with this shape and split
+ * count makes: 1 when S resolves to 1 or the splits are merged inside the
+ * partial kernel (MHA/GQA, when a unit's partials are at most 4 KiB), 2 when
+ * a separate reduction launch follows (MLA, larger partials).  0 on an
+ * invalid shape.  num_splits <= 0 resolves through the heuristic.  Host only.
+ */
+int32_t pa_decode_launches(const pa_shape* shape, int32_t num_splits, int32_t mla);
+
+/*
  * Bytes of workspace a call with this shape and split count needs: float32
  * partials o[batch][num_q_heads][S][head_dim_v], float32 lse[batch][num_q_heads][S]
  * and int32 arrival counters [batch][num_q_heads], each 256-byte aligned.  0 when
@@ -129,10 +138,12 @@ pa_status pa_workspace_init(const pa_shape* shape, int32_t num_splits, int32_t m
 
 /*
  * Paged split-KV decode attention, MHA and GQA (num_q_heads a multiple of
- * num_kv_heads).  One kernel launch: each workgroup computes one split's
- * partial; the last workgroup of each (sequence, head unit) to finish merges
- * that unit's splits with the log-sum-exp weights (a sequence that needs a
- * single split is written directly).  `lse` may be NULL.  `workspace` may be
+ * num_kv_heads).  Each workgroup computes one split's partial; the last
+ * workgroup of each (sequence, head unit) to finish merges that unit's splits
+ * with the log-sum-exp weights (a sequence that needs a single split is
+ * written directly) -- one launch -- unless the unit's partials are large,
+ * when a reduction launch merges every unit in parallel instead (see
+ * pa_decode_launches).  `lse` may be NULL.  `workspace` may be
  * NULL only when S resolves to 1; its counters must be zero (see above).
  * Supported: PA_F32 with head_dim 64 or 128; PA_BF16 with head_dim 64 or 128;
  * head_dim_v == head_dim; block_size 16 or 32.

@@ -212,3 +212,23 @@ def test_append_null_pointers(lib):
 def test_append_grid_limits(lib):
     assert append(lib, shape(batch=70000)) == _lib.PA_ERR_UNSUPPORTED
     assert append(lib, shape(num_kv_heads=70000, num_q_heads=70000)) == _lib.PA_ERR_UNSUPPORTED
+
+
+def test_decode_launches(lib):
+    """One launch when the splits merge in-kernel (small per-unit partials) or
+    S == 1; two when a reduction launch follows; 0 for a bad shape."""
+    def n(s, S, mla=0):
+        return lib.pa_decode_launches(ctypes.byref(s), S, mla)
+    mha = shape(batch=16, num_q_heads=32, num_kv_heads=32, max_context_len=4096,
+                max_blocks_per_seq=256, num_blocks=65536)
+    assert n(mha, 1) == 1
+    assert n(mha, 4) == 1                        # 4 x 1 head x 129 x 4 B = 2 KiB per unit
+    assert n(mha, 16) == 2                       # 8 KiB: separate reduction
+    gqa = shape(batch=1, num_q_heads=32, num_kv_heads=8, max_context_len=131072,
+                max_blocks_per_seq=8192, num_blocks=8192)
+    assert n(gqa, 2) == 2                        # 2 x 4 heads x 129 x 4 B: just over 4 KiB
+    assert n(gqa, 64) == 2
+    mla = shape(batch=32, num_q_heads=128, num_kv_heads=1, head_dim=576, head_dim_v=512,
+                block_size=64, max_context_len=8192, max_blocks_per_seq=128, num_blocks=4096)
+    assert n(mla, 4, 1) == 2 and n(mla, 1, 1) == 1
+    assert n(shape(batch=0), 4) == 0
