@@ -97,6 +97,10 @@ int heuristic_splits(const pa_shape& s, int cus, bool mla) {
     // one workgroup per (head group, sequence, split): fill the CUs once
     const long groups = (long)s.batch * (s.num_q_heads / pa::mla_heads_per_workgroup(s.num_q_heads));
     S = (cus + groups - 1) / groups;
+    // one-token pages: a split holds at most mla_max_split_tokens ids
+    const long max_c = pa::mla_max_split_tokens(s.block_size);
+    const long s_min = ((long)P + max_c - 1) / max_c;
+    if (S < s_min) S = s_min;
   } else {
     long units;
     int heads_per_wg;
@@ -217,8 +221,12 @@ pa_status run_partial(const pa_shape* shape, const void* q, const void* k, const
   const int S = resolve_splits(*shape, num_splits, mla);
   if (S < 1) return PA_ERR_HIP;
   if (S > 1 && (!ws || ws_bytes < workspace_bytes_for(*shape, S))) return PA_ERR_WORKSPACE;
-  pa::Params p = make_params(*shape, S, q, k, mla ? k : v, bt, ctx, out, lse, ws);
   const Kernel kern = pick_kernel(*shape, mla);
+  if (kern == Kernel::MlaMfma) {
+    const int P = max_pages(*shape);
+    if ((P + S - 1) / S > pa::mla_max_split_tokens(shape->block_size)) return PA_ERR_UNSUPPORTED;
+  }
+  pa::Params p = make_params(*shape, S, q, k, mla ? k : v, bt, ctx, out, lse, ws);
   // The fused merge runs in the last workgroup of each unit, after every
   // other split of the unit: cheap when the unit's partials are small, a
   // serial tail when they are large.  Above kFusedMergeBytes per unit the

@@ -53,7 +53,6 @@ namespace {
 
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
-constexpr int kBS = 64;                    // tokens per page
 constexpr int kRowB = kDqk * 2;            // 1152 bytes per latent row
 constexpr int kCT = 32;                    // tokens per chunk
 constexpr int kChunkB = kCT * kRowB;       // 36864 bytes per chunk
@@ -193,51 +192,107 @@ struct MlaLds {
   uint16_t p[2][MlaCfg<NW, HB>::NH * kCT];
 };
 
-// Physical page ids of the split, one per lane for a window of 64 logical
-// pages, so the chunk loop reads them with v_readlane instead of a memory load
-// (a vector load there would have to wait for every chunk in flight).
-struct PageIds {
+constexpr int kMaxIdsBS1 = 2048;   // token ids of one split held in LDS (one-token pages)
+
+// Where the rows of chunk ci come from, for 64-token pages (one page id per
+// chunk) and for one-token pages (a per-sequence token-index list: every row
+// has its own id).  Rows at or past the split's end t1 are read from the
+// zero block, so no NaN or stale data reaches the value product and no token
+// is counted by two splits.
+template <int NW, int BS>
+struct ChunkSource;
+
+template <int NW>
+struct ChunkSource<NW, 64> {
+  // Physical page ids of the split, one per lane for a window of 64 logical
+  // pages, read in the chunk loop with v_readlane (a vector load there would
+  // have to wait for every chunk in flight).
+  const int* bt;
+  const char* cbase;
+  int t0, t1, p1, nblocks, w, lane;
   int v;      // lane L: id of logical page base + L
   int base;   // first logical page of the window (wave-uniform)
+
+  __device__ __forceinline__ void load_window(int first) {
+    const int pg = first + lane;
+    v = pg < p1 ? clampi(bt[pg], 0, nblocks - 1) : 0;
+    base = first;
+  }
+  __device__ __forceinline__ void begin(int first_page) { load_window(first_page); }
+  // Page id of chunk ci; reloads the id window when the chunk leaves it
+  // (every 128 chunks at most; that reload waits for the loads in flight).
+  __device__ __forceinline__ int page_of(int ci) {
+    const int pg = (t0 + ci * kCT) / 64;
+    if (pg >= base + 64) load_window(pg);
+    return __builtin_amdgcn_readlane(v, pg - base);
+  }
+  // Issue this wave's share (kDmaInst / NW loads of 1 KiB) of chunk ci into dst.
+  __device__ __forceinline__ void issue(lds_char* dst, int ci) {
+    const int tok0 = t0 + ci * kCT;
+    const char* src = cbase + (size_t)page_of(ci) * (64 * kRowB) + (tok0 % 64) * kRowB;
+    const int lim = (t1 - tok0) * kRowB;             // bytes of the chunk inside the split
+    int ln = lane;
+    // recompute the per-lane offsets at every issue rather than keep them in
+    // registers across the loop (a few VALU ops against ~18 VGPRs)
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int k = 0; k < kDmaInst / NW; ++k) {
+      const int j = w + NW * k;
+      const int slot = j * 64 + ln;                  // 16-byte slot of the chunk buffer
+      const int t = slot / (kRowB / 16);
+      const int c = (slot % (kRowB / 16)) ^ row_key(t);
+      const int off = t * kRowB + c * 16;
+      const void* g = off < lim ? (const void*)(src + off) : (const void*)g_zero16;
+      dma16(g, dst + j * 1024);
+    }
+  }
 };
 
-__device__ __forceinline__ void load_ids(PageIds& ids, const int* bt, int base, int p1, int nblocks,
-                                         int lane) {
-  const int pg = base + lane;
-  ids.v = pg < p1 ? clampi(bt[pg], 0, nblocks - 1) : 0;
-  ids.base = base;
-}
-
-// Page id of chunk ci; reloads the id window when the chunk leaves it (every
-// 128 chunks at most; that reload waits for the loads in flight).
-__device__ __forceinline__ int chunk_page_id(PageIds& ids, const int* bt, int t0, int ci, int p1,
-                                             int nblocks, int lane) {
-  const int pg = (t0 + ci * kCT) / kBS;
-  if (pg >= ids.base + 64) load_ids(ids, bt, pg, p1, nblocks, lane);
-  return __builtin_amdgcn_readlane(ids.v, pg - ids.base);
-}
-
-// Issue this wave's share (NWI 1 KiB loads) of chunk `ci` into `dst`.
 template <int NW>
-__device__ __forceinline__ void issue_chunk(lds_char* dst, const char* cbase, int id, int t0,
-                                            int ci, int ctx, int w, int lane) {
-  const int tok0 = t0 + ci * kCT;
-  const char* src = cbase + (size_t)id * (kBS * kRowB) + (tok0 % kBS) * kRowB;
-  const int lim = (ctx - tok0) * kRowB;              // bytes of the chunk that hold context tokens
-  // recompute the per-lane offsets at every issue rather than keep them in
-  // registers across the loop (a few VALU ops against ~18 VGPRs)
-  asm volatile("" : "+v"(lane));
-#pragma unroll
-  for (int k = 0; k < kDmaInst / NW; ++k) {
-    const int j = w + NW * k;
-    const int slot = j * 64 + lane;                  // 16-byte slot of the chunk buffer
-    const int t = slot / (kRowB / 16);
-    const int c = (slot % (kRowB / 16)) ^ row_key(t);
-    const int off = t * kRowB + c * 16;
-    const void* g = off < lim ? (const void*)(src + off) : (const void*)g_zero16;
-    dma16(g, dst + j * 1024);
+struct ChunkSource<NW, 1> {
+  // The split's token ids (at most kMaxIdsBS1, checked by the host) are
+  // copied into LDS once per pass; each 1 KiB load of a chunk spans at most
+  // two token rows (64 slots of 16 bytes, rows of 72), whose ids are read
+  // from LDS by every lane.
+  const int* bt;
+  const char* cbase;
+  int t0, t1, p1, nblocks, w, lane;
+  int* ids;   // LDS, kMaxIdsBS1 entries: id of token t0 + i
+
+  __device__ __forceinline__ void begin(int /*first_page*/) {
+    // no loads are in flight here (start of a pass), so the full barrier is free
+    const int n = t1 - t0;
+    for (int i = threadIdx.x; i < n; i += NW * 64) ids[i] = clampi(bt[t0 + i], 0, nblocks - 1);
+    __syncthreads();
   }
-}
+  __device__ __forceinline__ void issue(lds_char* dst, int ci) {
+    const int tok0 = t0 + ci * kCT;
+    const int nrows = t1 - tok0;                     // rows of the chunk inside the split
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    // ids of the two rows each load touches, all read before the first load
+    int id0[kDmaInst / NW], id1[kDmaInst / NW];
+#pragma unroll
+    for (int k = 0; k < kDmaInst / NW; ++k) {
+      const int T = ((w + NW * k) * 64) / (kRowB / 16);   // first row load k touches
+      const int i0 = tok0 - t0 + T;                  // rows past the split never use their id
+      id0[k] = ids[min(i0, kMaxIdsBS1 - 1)];
+      id1[k] = ids[min(i0 + 1, kMaxIdsBS1 - 1)];
+    }
+#pragma unroll
+    for (int k = 0; k < kDmaInst / NW; ++k) {
+      const int j = w + NW * k;
+      const int T = (j * 64) / (kRowB / 16);
+      const int slot = j * 64 + ln;
+      const int t = slot / (kRowB / 16);
+      const int c = (slot % (kRowB / 16)) ^ row_key(t);
+      const int id = t == T ? id0[k] : id1[k];
+      const void* g = t < nrows ? (const void*)(cbase + (size_t)id * kRowB + c * 16)
+                                : (const void*)g_zero16;
+      dma16(g, dst + j * 1024);
+    }
+  }
+};
 
 template <int NW, int HB>
 struct MlaState {
@@ -310,7 +365,7 @@ struct SoftmaxRow {
 
 template <int NW, int HB, int STAGE>
 __device__ __forceinline__ void softmax_stage(SoftmaxRow& r, const f32x4 (&sa)[2],
-                                              MlaState<NW, HB>& st, int hb, int tbase, int ctx,
+                                              MlaState<NW, HB>& st, int hb, int tbase, int tend,
                                               float cs, lds_char* pbuf, int w, int lane) {
   const int quad = lane >> 4, n = lane & 15;
   if constexpr (STAGE == 0) {
@@ -319,11 +374,11 @@ __device__ __forceinline__ void softmax_stage(SoftmaxRow& r, const f32x4 (&sa)[2
       r.v[j] = sa[0][j];
       r.v[4 + j] = sa[1][j];
     }
-    if (tbase + kCT > ctx) {                          // only a split's last chunk runs past the context
+    if (tbase + kCT > tend) {                         // only a split's last chunk runs past its end
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (tbase + quad * 4 + j >= ctx) r.v[j] = kNegInf;
-        if (tbase + 16 + quad * 4 + j >= ctx) r.v[4 + j] = kNegInf;
+        if (tbase + quad * 4 + j >= tend) r.v[j] = kNegInf;
+        if (tbase + 16 + quad * 4 + j >= tend) r.v[4 + j] = kNegInf;
       }
     }
     r.mx = fmaxf(fmaxf(fmaxf(r.v[0], r.v[1]), fmaxf(r.v[2], r.v[3])),
@@ -378,7 +433,7 @@ struct ValueOps {
 // busy.
 template <int NW, int HB, bool PV>
 __device__ __forceinline__ void values_and_softmax(MlaState<NW, HB>& st, const ValueOps<NW, HB>& vo,
-                                                   const f32x4 (&sa)[HB][2], int tbase, int ctx,
+                                                   const f32x4 (&sa)[HB][2], int tbase, int tend,
                                                    float cs, lds_char* pbuf, int w, int lane) {
   using C = MlaCfg<NW, HB>;
   constexpr int NBG = C::NB < 4 ? C::NB : 4;          // head blocks per group
@@ -389,7 +444,7 @@ __device__ __forceinline__ void values_and_softmax(MlaState<NW, HB>& st, const V
   SoftmaxRow row;
   auto stage = [&](auto kc) {
     constexpr int k = decltype(kc)::value;
-    softmax_stage<NW, HB, k % 4>(row, sa[k / 4], st, k / 4, tbase, ctx, cs, pbuf, w, lane);
+    softmax_stage<NW, HB, k % 4>(row, sa[k / 4], st, k / 4, tbase, tend, cs, pbuf, w, lane);
   };
   if constexpr (!PV) {
     static_for<0, STAGES>(stage);
@@ -438,11 +493,12 @@ __device__ __forceinline__ void values_only(MlaState<NW, HB>& st, const ValueOps
   });
 }
 
-template <int NW, int HB>
+template <int NW, int HB, int BS>
 __global__ __launch_bounds__(NW * 64) void mla_mfma_partial(Params p) {
   using C = MlaCfg<NW, HB>;
   __shared__ __attribute__((aligned(16))) char ring_lds[kRing * kChunkB];
   __shared__ __attribute__((aligned(16))) MlaLds<NW, HB> sm;
+  __shared__ int ids_lds[BS == 1 ? kMaxIdsBS1 : 1];
   lds_char* const ring = (lds_char*)ring_lds;
 
   // 1-D grid of HG x S x B workgroups.  With two head groups, the two
@@ -470,11 +526,11 @@ __global__ __launch_bounds__(NW * 64) void mla_mfma_partial(Params p) {
   const int quad = lane >> 4, n = lane & 15;
   const int head0 = hg * C::NH;
   const int ctx = clampi(p.context_lens[b], 0, p.max_ctx);
-  const int pages = (ctx + kBS - 1) / kBS;
+  const int pages = (ctx + BS - 1) / BS;
   const int nsplit = splits_of(pages, p.c);
   if (s >= (nsplit > 0 ? nsplit : 1)) return;
-  const int t0 = s * p.c * kBS;
-  const int t1 = min(ctx, (s * p.c + p.c) * kBS);
+  const int t0 = s * p.c * BS;
+  const int t1 = min(ctx, (s * p.c + p.c) * BS);
   const int p1 = min(pages, s * p.c + p.c);
   const int nchunks = t1 > t0 ? (t1 - t0 + kCT - 1) / kCT : 0;
   const float cs = p.scale_log2;                      // > 0, checked by the host
@@ -495,7 +551,16 @@ __global__ __launch_bounds__(NW * 64) void mla_mfma_partial(Params p) {
   const char* cbase = static_cast<const char*>(p.k);
   auto slot = [&](int ci) { return ring + (ci % kRing) * kChunkB; };
   auto pslot = [&](int ci) { return (lds_char*)sm.p[ci & 1]; };
-  PageIds ids;
+  ChunkSource<NW, BS> src;
+  src.bt = bt;
+  src.cbase = cbase;
+  src.t0 = t0;
+  src.t1 = t1;
+  src.p1 = p1;
+  src.nblocks = p.nblocks;
+  src.w = w;
+  src.lane = lane;
+  if constexpr (BS == 1) src.ids = ids_lds;
   for (;;) {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) st.l[hb] = 0.f;
@@ -504,15 +569,13 @@ __global__ __launch_bounds__(NW * 64) void mla_mfma_partial(Params p) {
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) st.acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     st.bad = false;
-    load_ids(ids, bt, s * p.c, p1, p.nblocks, lane);
+    src.begin(s * p.c);
     // The first two chunks are issued even past the split's end (those loads
     // read the zero block), so the count in flight is known here and one wait
     // retires the query loads, which are older: no wait inside the loop has to
     // allow for them.
-    issue_chunk<NW>(slot(0), cbase, chunk_page_id(ids, bt, t0, 0, p1, p.nblocks, lane), t0, 0,
-                    ctx, w, lane);
-    issue_chunk<NW>(slot(1), cbase, chunk_page_id(ids, bt, t0, 1, p1, p.nblocks, lane), t0, 1,
-                    ctx, w, lane);
+    src.issue(slot(0), 0);
+    src.issue(slot(1), 1);
     constexpr int kInit = 2 * C::NWI;
     wait_vm<kInit <= 63 ? kInit : 0>();
 
@@ -522,17 +585,14 @@ __global__ __launch_bounds__(NW * 64) void mla_mfma_partial(Params p) {
       // product of ci - 2 is done, so its slot can be refilled
       if (ci + 1 < max(nchunks, 2)) wait_vm<C::NWI>(); else wait_vm<0>();
       lds_barrier();
-      if (ci + 2 < nchunks)
-        issue_chunk<NW>(slot(ci + 2), cbase,
-                        chunk_page_id(ids, bt, t0, ci + 2, p1, p.nblocks, lane), t0, ci + 2, ctx,
-                        w, lane);
+      if (ci + 2 < nchunks) src.issue(slot(ci + 2), ci + 2);
       f32x4 sa[HB][2];
       chunk_scores<NW, HB>(slot(ci), st, sa, lane);
       const ValueOps<NW, HB> vo{slot(ci + kRing - 1), pslot(ci + 1), w, n, quad};
       if (ci > 0)
-        values_and_softmax<NW, HB, true>(st, vo, sa, t0 + ci * kCT, ctx, cs, pslot(ci), w, lane);
+        values_and_softmax<NW, HB, true>(st, vo, sa, t0 + ci * kCT, t1, cs, pslot(ci), w, lane);
       else
-        values_and_softmax<NW, HB, false>(st, vo, sa, t0 + ci * kCT, ctx, cs, pslot(ci), w, lane);
+        values_and_softmax<NW, HB, false>(st, vo, sa, t0 + ci * kCT, t1, cs, pslot(ci), w, lane);
     }
     if (nchunks > 0) {
       lds_barrier();                                  // the last chunk's probabilities
@@ -618,18 +678,25 @@ template <int NW, int HB>
 hipError_t launch_cfg(const Params& p, hipStream_t st) {
   const long blocks = (long)(p.Hq / MlaCfg<NW, HB>::NH) * p.S * p.B;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mla_mfma_partial<NW, HB>), dim3((unsigned)blocks), dim3(NW * 64), 0, st, p);
+  if (p.bs == 1)
+    hipLaunchKernelGGL((mla_mfma_partial<NW, HB, 1>), dim3((unsigned)blocks), dim3(NW * 64), 0, st,
+                       p);
+  else
+    hipLaunchKernelGGL((mla_mfma_partial<NW, HB, 64>), dim3((unsigned)blocks), dim3(NW * 64), 0, st,
+                       p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool mla_mfma_supported(bool bf16, int Dqk, int Dv, int bs, int Hq) {
-  return bf16 && Dqk == kDqk && Dv == kDv && bs == kBS &&
+  return bf16 && Dqk == kDqk && Dv == kDv && (bs == 64 || bs == 1) &&
          (Hq % 64 == 0 || Hq == 32 || Hq == 16);
 }
 
 int mla_heads_per_workgroup(int Hq) { return Hq % 64 == 0 ? 64 : Hq; }
+
+int mla_max_split_tokens(int bs) { return bs == 1 ? kMaxIdsBS1 : 0x7fffffff; }
 
 hipError_t launch_mla_mfma(const Params& p, hipStream_t st) {
   if (p.Hq % 64 == 0) return launch_cfg<4, 1>(p, st);

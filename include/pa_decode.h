@@ -158,8 +158,13 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
  * token (page 2/3: MLA compresses the KV cache into a latent vector and
  * caches only it).  Keys are whole latent rows (head_dim wide), values their
  * first head_dim_v entries, read from the same memory.  num_kv_heads must be 1.
- * Supported: PA_BF16, head_dim 576, head_dim_v 512, block_size 64,
- * num_q_heads a multiple of 16.
+ * Supported: PA_BF16, head_dim 576, head_dim_v 512, num_q_heads 16, 32 or a
+ * multiple of 64; block_size 64, or block_size 1: then block_table[b] is a
+ * per-sequence list of token (row) ids, as a sparse top-k selection produces
+ * (page 5, the DeepSeek V4 note on CSA and HCA: attention over the top 1024
+ * entries plus a 128-entry window, or densely over every entry), and a split may
+ * hold at most 2048 tokens (PA_ERR_UNSUPPORTED for an explicit num_splits
+ * that needs more; the heuristic never does).
  */
 pa_status pa_decode_mla(const pa_shape* shape, const void* q, const void* kv_cache,
                         const int32_t* block_table, const int32_t* context_lens,

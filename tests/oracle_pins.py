@@ -112,9 +112,18 @@ def pin_bruteforce(o):
 
 def pin_mla_bruteforce(o):
     """P-1 for the latent variant: keys are whole latents, values their head."""
-    rng = np.random.default_rng(21)
-    B, Hq, Dc, dv, bs = 2, 3, 6, 4, 4
-    ctxs = [6, 9]
+    _mla_brute(o, 21, 4, [6, 9])
+
+
+def pin_mla_token_index_list(o):
+    """The latent variant with one-token pages: block_table rows are token-id
+    lists (a sparse top-k selection), checked against the brute force."""
+    _mla_brute(o, 22, 1, [5, 11])
+
+
+def _mla_brute(o, seed, bs, ctxs):
+    rng = np.random.default_rng(seed)
+    B, Hq, Dc, dv = 2, 3, 6, 4
     n_pages = [-(-c // bs) for c in ctxs]
     total = sum(n_pages) + 2
     perm = rng.permutation(total)
@@ -420,7 +429,8 @@ def pin_append_latent(o):
 
 
 ALL_PINS = [
-    pin_bruteforce, pin_mla_bruteforce, pin_bf16_widening, pin_sdpa, pin_ctx_one,
+    pin_bruteforce, pin_mla_bruteforce, pin_mla_token_index_list, pin_bf16_widening, pin_sdpa,
+    pin_ctx_one,
     pin_identical_keys, pin_two_token_closed_form, pin_split_invariance,
     pin_page_permutation, pin_constant_values, pin_stability, pin_score_shift,
     pin_gqa_equals_mha, pin_mla_equals_mqa, pin_batch_independence, pin_sampled_heads,

@@ -232,3 +232,16 @@ def test_decode_launches(lib):
                 block_size=64, max_context_len=8192, max_blocks_per_seq=128, num_blocks=4096)
     assert n(mla, 4, 1) == 2 and n(mla, 1, 1) == 1
     assert n(shape(batch=0), 4) == 0
+
+
+def test_token_index_split_limit(lib):
+    """With one-token pages the latent kernel holds at most 2048 token ids per
+    split: an explicit split count that needs more is unsupported, and the
+    heuristic never picks one."""
+    s = shape(batch=1, num_q_heads=128, num_kv_heads=1, head_dim=576, head_dim_v=512,
+              block_size=1, max_context_len=5000, max_blocks_per_seq=5000, num_blocks=10000,
+              scale=192 ** -0.5)
+    st = lib.pa_decode_mla(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 2, FAKE, NULL, FAKE, 1 << 40,
+                           NULL)
+    assert st == _lib.PA_ERR_UNSUPPORTED              # ceil(5000 / 2) > 2048
+    assert lib.pa_choose_num_splits(ctypes.byref(s), 256, 1) >= 3

@@ -119,6 +119,13 @@ SMALL = {
     "mla_bf16_h64": dict(kind="mla", dtype="bf16", batch=1, num_q_heads=64, num_kv_heads=1,
                          head_dim=576, head_dim_v=512, block_size=64, context_lens=[129],
                          num_blocks=5, scale=192 ** -0.5),
+    # one-token pages: block_table rows are token-index lists
+    "mla_bf16_bs1_h128": dict(kind="mla", dtype="bf16", batch=3, num_q_heads=128,
+                              num_kv_heads=1, head_dim=576, head_dim_v=512, block_size=1,
+                              context_lens=[1, 100, 333], num_blocks=600, scale=192 ** -0.5),
+    "mla_bf16_bs1_h32": dict(kind="mla", dtype="bf16", batch=2, num_q_heads=32, num_kv_heads=1,
+                             head_dim=576, head_dim_v=512, block_size=1, context_lens=[47, 65],
+                             num_blocks=200, scale=192 ** -0.5),
 }
 
 
@@ -149,7 +156,8 @@ def sample_pairs(inp, n, seed):
     return sorted(pairs)
 
 
-@pytest.mark.parametrize("name", ["llama_mha_bf16", "long_gqa_bf16", "ragged_gqa_bf16", "mla_bf16"])
+@pytest.mark.parametrize("name", ["llama_mha_bf16", "long_gqa_bf16", "ragged_gqa_bf16", "mla_bf16",
+                                  "mla_topk_bf16", "mla_allentries_bf16"])
 def test_full_size_sampled(name):
     say(f"full {name}: drawing inputs")
     inp = make_config(name)

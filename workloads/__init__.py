@@ -276,14 +276,30 @@ CONFIGS = {
         head_dim_v=512, block_size=64, context_lens=[8192] * 32, num_blocks=4096,
         scale=1.0 / math.sqrt(192), seed=5,
         meta=dict(desc="MLA latent bf16: B32, 128 heads, latent 576 (V = first 512), ctx 8192, bs64")),
+    # Token-index lists over a latent cache (one-token pages): each sequence
+    # attends to 1152 scattered entries (a top-1024 selection plus a 128-entry
+    # window), or densely to 8192 entries, out of a pool of 32 x 8192 rows.
+    "mla_topk_bf16": dict(
+        kind="mla", dtype="bf16", batch=32, num_q_heads=128, num_kv_heads=1, head_dim=576,
+        head_dim_v=512, block_size=1, context_lens=[1152] * 32, num_blocks=262144,
+        scale=1.0 / math.sqrt(192), seed=6,
+        meta=dict(desc="MLA latent bf16 over token-index lists: B32, 128 heads, 1152 entries "
+                       "per sequence (top-1024 + 128-window stand-in), bs1, 262144-row pool")),
+    "mla_allentries_bf16": dict(
+        kind="mla", dtype="bf16", batch=32, num_q_heads=128, num_kv_heads=1, head_dim=576,
+        head_dim_v=512, block_size=1, context_lens=[8192] * 32, num_blocks=262144,
+        scale=1.0 / math.sqrt(192), seed=7,
+        meta=dict(desc="MLA latent bf16 over token-index lists: B32, 128 heads, 8192 entries "
+                       "per sequence (every entry), bs1, 262144-row pool")),
 }
 
-CONFIG_ORDER = ["tiny_mha_f32", "llama_mha_bf16", "long_gqa_bf16", "ragged_gqa_bf16", "mla_bf16"]
+CONFIG_ORDER = ["tiny_mha_f32", "llama_mha_bf16", "long_gqa_bf16", "ragged_gqa_bf16", "mla_bf16",
+                "mla_topk_bf16", "mla_allentries_bf16"]
 
 
 def make_config(name: str, *, poison: bool = True, values: bool = True, seed: int | None = None,
                 **overrides) -> PagedDecodeInputs:
-    """Draw one of the five named workloads (optionally with fields overridden)."""
+    """Draw one of the named workloads (optionally with fields overridden)."""
     spec = dict(CONFIGS[name])
     spec.update(overrides)
     if seed is not None:
