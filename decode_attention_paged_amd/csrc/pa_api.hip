@@ -95,7 +95,8 @@ int heuristic_splits(const pa_shape& s, int cus, bool mla) {
   long S;
   if (k == Kernel::MlaMfma) {
     // one workgroup per (head group, sequence, split): fill the CUs once
-    const long groups = (long)s.batch * (s.num_q_heads / pa::mla_heads_per_workgroup(s.num_q_heads));
+    const long groups =
+        (long)s.batch * (s.num_q_heads / pa::mla_heads_per_workgroup(s.num_q_heads, s.block_size));
     S = (cus + groups - 1) / groups;
     // one-token pages: a split holds at most mla_max_split_tokens ids
     const long max_c = pa::mla_max_split_tokens(s.block_size);

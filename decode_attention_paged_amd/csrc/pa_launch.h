@@ -52,7 +52,7 @@ bool mha_valu_supported(bool bf16, int D, int bs);
 bool gqa_mfma_supported(bool bf16, int D, int Dv, int bs, int G);
 bool mla_mfma_supported(bool bf16, int Dqk, int Dv, int bs, int Hq);
 // Query heads one MLA workgroup holds (the grid has Hq / this head groups).
-int mla_heads_per_workgroup(int Hq);
+int mla_heads_per_workgroup(int Hq, int bs);
 // Longest split (tokens) the MLA kernel takes for this page size (one-token
 // pages keep a split's token ids in LDS).
 int mla_max_split_tokens(int bs);
