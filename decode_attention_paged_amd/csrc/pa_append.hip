@@ -1,6 +1,7 @@
 // Paged KV append: the new token of every sequence goes to the page and slot
-// its position selects (page 1, vLLM README: the KV cache lives in fixed-size
-// pages named by a per-sequence block table), right before the decode step
+// its position selects (the wenku.it search page for "paged attention", its
+// vLLM README snippets: the KV cache lives in fixed-size pages named by a
+// per-sequence block table), right before the decode step
 // reads it.  Position n = context_lens[b] (the length before the append):
 //   page = block_table[b][n / bs], slot = n % bs.
 // A sequence whose position is outside its block table, or whose page id is

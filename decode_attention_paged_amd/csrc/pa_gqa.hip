@@ -8,7 +8,7 @@
 // pairs of pages round-robin (a pair is 32 tokens, the MFMA contraction
 // depth of the value product) and merge their running states in LDS at the
 // end, which yields the split's (o_s, lse_s) of Flash-Decoding's second step
-// (page 4).
+// (the "flash decoding ++" entry, its three-steps snippet).
 //
 // Operand layouts (MFMA 16x16x32 bf16: A[i][k] in lane i + 16*(k/8), element
 // k%8; B[k][j] in lane j + 16*(k/8); D[i][j] in lane j + 16*(i/4), reg i%4):

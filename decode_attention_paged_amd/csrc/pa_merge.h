@@ -1,7 +1,8 @@
 // Split results: writing a split's (o_s, lse_s), and the fused reduction run
 // by the last workgroup of a (sequence, head unit) to finish.
 //
-// The reduction is Flash-Decoding's third step (page 4): rescale each split
+// The reduction is Flash-Decoding's third step (the "flash decoding ++" entry,
+// its three-steps snippet): rescale each split
 // output by exp(lse_s - max lse) and sum, normalised by the sum of weights;
 // lse = max + ln(sum of weights).
 #pragma once

@@ -2,9 +2,9 @@
 //
 // One workgroup per (split, query head, sequence); its NW waves take the
 // split's pages round-robin and each keeps its own running (max, sum, acc)
-// state, merged in LDS at the end (the per-chunk step of Flash-Decoding,
-// page 4: attention of the query with each chunk, recording its
-// log-sum-exp).  A single query row per KV head gives no operand reuse, so
+// state, merged in LDS at the end (the per-chunk step of Flash-Decoding in
+// the "flash decoding ++" entry, its three-steps snippet: attention of the
+// query with each chunk, recording its log-sum-exp).  A single query row per KV head gives no operand reuse, so
 // the dot products run on the VALU (v_dot2_f32_bf16 for bf16) rather than
 // on MFMA.
 //

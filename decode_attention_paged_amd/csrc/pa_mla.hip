@@ -870,8 +870,11 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
   const int HG = p.Hq / kWideNH;
   const int hg = blockIdx.x % HG;
   const int u = blockIdx.x / HG;
-  const int b = u / p.S;
-  const int s = split_of_block(u % p.S, b, p.S);
+  // split-major: the splits of sequence b are B workgroups apart, so with B a
+  // multiple of 8 they share an XCD (workgroups go round-robin to the 8
+  // XCDs) and its L2 serves the queries to all but the first
+  const int b = u % p.B;
+  const int s = u / p.B;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int quad = lane >> 4, n = lane & 15;

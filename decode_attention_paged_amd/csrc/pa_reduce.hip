@@ -1,5 +1,6 @@
 // Log-sum-exp weighted reduction of split partials (Flash-Decoding's third
-// step, page 4: rescale each split's output by its log-sum-exp and combine).
+// step in the "flash decoding ++" entry, its three-steps snippet: rescale
+// each split's output by its log-sum-exp and combine).
 //
 //   M = max_s lse_s,  w_s = exp(lse_s - M),
 //   out = sum_s w_s o_s / sum_s w_s,  lse = M + ln(sum_s w_s).

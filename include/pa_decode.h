@@ -12,11 +12,14 @@
  *       out[b][h][:] = sum_i exp(s_i - m) v_i / sum_i exp(s_i - m),  m = max_i s_i
  *       lse[b][h]    = m + ln(sum_i exp(s_i - m))          (natural log)
  *   This is scaled dot-product softmax attention of one query row per head
- *   (page 1, "Transformer introduction": each query scored against every key,
- *   scores re-weighting the values; page 2: multi-head attention as h
- *   self-attentions), over KV memory managed in fixed pages as PagedAttention
- *   does (page 1, vLLM README snippets).  It is evaluated with Flash-Decoding's
- *   three steps (page 4, "Flash Decoding mainly has three steps"): the pages of
+ *   (the wenku.it search page for "paged attention", its "Transformer
+ *   introduction" snippet: each query scored against every key, scores
+ *   re-weighting the values; the wenku.it search page for "Multi-head Latent
+ *   Attention (MLA)": multi-head attention as h self-attentions), over KV
+ *   memory managed in fixed pages as PagedAttention does (the "paged
+ *   attention" search page, its vLLM README snippets).  It is evaluated with
+ *   Flash-Decoding's three steps (the "flash decoding ++" entry, its
+ *   three-steps snippet): the pages of
  *   a sequence are cut into contiguous splits, each split's attention is
  *   computed in parallel with its log-sum-exp, and the split results are
  *   rescaled and reduced into the exact output.
@@ -94,8 +97,8 @@ int32_t pa_version(void);
 
 /*
  * Split-count heuristic (the split control that Flash-Decoding adds when
- * batch x heads alone cannot fill the GPU; page 4, the TRT-LLM
- * multi_block_mode / vLLM PagedAttention V2 snippet).  Picks S so that the
+ * batch x heads alone cannot fill the GPU; the "flash decoding ++" entry,
+ * its TRT-LLM multi_block_mode / vLLM PagedAttention V2 snippet).  Picks S so that the
  * partial kernel launches enough workgroups for `num_cus` compute units
  * while each split keeps enough pages to amortise its partial write.
  * num_cus <= 0 queries the current HIP device.  Returns S >= 1, or 0 if the
@@ -155,16 +158,18 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
 
 /*
  * MLA latent decode: every query head attends to one shared latent row per
- * token (page 2/3: MLA compresses the KV cache into a latent vector and
- * caches only it).  Keys are whole latent rows (head_dim wide), values their
- * first head_dim_v entries, read from the same memory.  num_kv_heads must be 1.
- * Supported: PA_BF16, head_dim 576, head_dim_v 512, num_q_heads 16, 32 or a
- * multiple of 64; block_size 64, or block_size 1: then block_table[b] is a
- * per-sequence list of token (row) ids, as a sparse top-k selection produces
- * (page 5, the DeepSeek V4 note on CSA and HCA: attention over the top 1024
- * entries plus a 128-entry window, or densely over every entry), and a split may
- * hold at most 2048 tokens (PA_ERR_UNSUPPORTED for an explicit num_splits
- * that needs more; the heuristic never does).
+ * token (the "Multi-head Latent Attention (MLA)" search page and the
+ * FlashMLA-ETAP related-papers page, their MLA abstracts: MLA compresses the
+ * KV cache into a latent vector and caches only it).  Keys are whole latent
+ * rows (head_dim wide), values their first head_dim_v entries, read from the
+ * same memory.  num_kv_heads must be 1.  Supported: PA_BF16, head_dim 576,
+ * head_dim_v 512, num_q_heads 16, 32 or a multiple of 64; block_size 64, or
+ * block_size 1: then block_table[b] is a per-sequence list of token (row)
+ * ids, as a sparse top-k selection produces (the "llms-attention" post, its
+ * DeepSeek V4 note on CSA and HCA: attention over the top 1024 entries plus
+ * a 128-entry window, or densely over every entry), and a split may hold at
+ * most 2048 tokens (PA_ERR_UNSUPPORTED for an explicit num_splits that needs
+ * more; the heuristic never does).
  */
 pa_status pa_decode_mla(const pa_shape* shape, const void* q, const void* kv_cache,
                         const int32_t* block_table, const int32_t* context_lens,
@@ -178,8 +183,9 @@ pa_status pa_decode_mla(const pa_shape* shape, const void* q, const void* kv_cac
  * partial into `workspace` (or, when S resolves to 1, out/lse directly) and
  * does not touch the counters.
  * pa_reduce merges them: M = max_s lse_s, w_s = exp(lse_s - M),
- * out = sum_s w_s o_s / sum_s w_s, lse = M + ln(sum_s w_s) (page 4, step
- * three: rescale the split results by their log-sum-exp and reduce).
+ * out = sum_s w_s o_s / sum_s w_s, lse = M + ln(sum_s w_s) (the "flash
+ * decoding ++" entry, the third of its three steps: rescale the split results
+ * by their log-sum-exp and reduce).
  * pa_reduce with S == 1 does nothing and returns PA_OK.
  */
 pa_status pa_decode_partial(const pa_shape* shape, const void* q, const void* k_cache,
@@ -199,9 +205,9 @@ pa_status pa_reduce(const pa_shape* shape, const int32_t* context_lens, int32_t 
 
 /*
  * Paged KV append: write one new token per sequence into the cache at the
- * position that token takes, the step that precedes a decode call (page 1,
- * vLLM README snippets: KV memory managed in fixed pages through a block
- * table).  With n = context_lens[b], the length BEFORE the append:
+ * position that token takes, the step that precedes a decode call (the
+ * "paged attention" search page, its vLLM README snippets: KV memory managed
+ * in fixed pages through a block table).  With n = context_lens[b], the length BEFORE the append:
  *     page = block_table[b * max_blocks_per_seq + n / block_size]
  *     slot = n % block_size
  *     k_cache[page][g][slot][:]  = k_new[b][g][:]        g < num_kv_heads

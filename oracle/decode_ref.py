@@ -7,13 +7,15 @@ the HIP library and imports nothing from it.
 What it computes
 ----------------
 Decode attention is ordinary scaled dot-product softmax attention for one
-query row per head (the "Transformer introduction" snippet on page 1, the
-attention-per-word passage: every query is scored against every key of the
-sequence and the scores re-weight the values; page 2, the Multi-Head
-Attention passage: h self-attentions side by side, whose formula the page
-cuts off at its left-hand side).  Softmax needs a reduction along the whole
-row (page 5, the SoftmaxAttn blurb).  The Flash-Decoding snippets on page 4
-(the three-step description and the "main idea" paragraph) state that
+query row per head (the wenku.it search page for "paged attention", its
+"Transformer introduction" snippet, the attention-per-word passage: every
+query is scored against every key of the sequence and the scores re-weight
+the values; the wenku.it search page for "Multi-head Latent Attention (MLA)",
+its Multi-Head Attention passage: h self-attentions side by side, whose
+formula the page cuts off at its left-hand side).  Softmax needs a reduction
+along the whole row (the "llms-attention" post, its SoftmaxAttn blurb).  The
+Flash-Decoding snippets of the "flash decoding ++" entry (the three-step
+description and the "main idea" paragraph) state that
 splitting K/V into chunks, recording a log-sum-exp per chunk and rescaling
 the chunk results gives the same, correct attention output.  So the
 reference result is the plain definition, written out in float64:
@@ -25,9 +27,10 @@ reference result is the plain definition, written out in float64:
         lse  = m + ln sum_i exp(s_i - m)          (natural log)
 
 ``paged_decode_split`` additionally walks the three Flash-Decoding steps in
-their page-4 order (split, per-chunk attention with a running max and sum,
+the order that entry gives (split, per-chunk attention with a running max and sum,
 log-sum-exp rescale and merge) so the merge identity itself can be checked.
-``paged_decode_mla`` is the latent (MLA) variant named on pages 1-3: every
+``paged_decode_mla`` is the latent (MLA) variant of the two search pages and
+the FlashMLA-ETAP related-papers page (its MLA abstracts): every
 query head attends to one shared latent vector per token; keys are the whole
 latent, values its leading ``dv`` entries.
 
@@ -125,7 +128,7 @@ def attend(q_vec, keys, values, scale):
 
 
 # --------------------------------------------------------------------------
-# Flash-Decoding steps (page 4): split, per-chunk partials, LSE merge
+# Flash-Decoding steps ("flash decoding ++" entry): split, per-chunk partials, LSE merge
 # --------------------------------------------------------------------------
 
 def split_page_ranges(num_pages: int, pages_per_split: int, num_splits: int):
@@ -312,8 +315,8 @@ def decode_inputs(inp, heads=None):
 
 # ---------------------------------------------------------------------------
 # Paged KV append (the step before decode: the new token's K/V rows go to the
-# page and slot its position selects; page 1, vLLM README snippets on KV
-# memory managed in pages through a block table).
+# page and slot its position selects; the "paged attention" search page, its
+# vLLM README snippets on KV memory managed in pages through a block table).
 # ---------------------------------------------------------------------------
 
 def append_slot(block_table_row: np.ndarray, n: int, bs: int):
