@@ -24,7 +24,10 @@ from .decode_ref import (  # noqa: F401
     merge_partials,
     paged_decode,
     paged_decode_mla,
+    paged_decode_mla_rows,
+    paged_decode_rows,
     paged_decode_split,
+    row_context,
     scores,
     split_page_ranges,
     token_locations,

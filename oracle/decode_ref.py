@@ -303,9 +303,82 @@ def paged_decode_mla(q, c_pool, block_table, context_lens, scale, dv=512, dtype=
     return out, lse
 
 
+# --------------------------------------------------------------------------
+# Several query rows per sequence (chunked prefill, draft verification).  The
+# pages name the prefill stage and FlashAttention's exact attention over many
+# query rows (the FlashMLA-ETAP related-papers page, its FlashAttention
+# abstracts; the "llms-attention" post) but give no mask.  Reading taken: the
+# q_len rows are the sequence's last q_len tokens, whose K/V are already in
+# the cache, and row j (position ctx - q_len + j) attends causally to the
+# tokens up to and including its own position.  At q_len = 1 this is the
+# decode definition above.
+# --------------------------------------------------------------------------
+
+def row_context(ctx: int, q_len: int, j: int) -> int:
+    """Tokens that query row j of q_len sees: ctx - q_len + 1 + j, at least 0."""
+    return max(0, int(ctx) - q_len + 1 + j)
+
+
+def _rows_by_j(rows, q_len):
+    if rows is None:
+        return {j: None for j in range(q_len)}
+    by = {}
+    for b, j, h in rows:
+        by.setdefault(int(j), []).append((int(b), int(h)))
+    return by
+
+
+def paged_decode_rows(q, k_pool, v_pool, block_table, context_lens, scale, dtype="bf16",
+                      rows=None):
+    """Reference attention of q_len query rows per sequence over paged K/V.
+
+    q [B][q_len][Hq][D]; returns (out [B][q_len][Hq][Dv], lse [B][q_len][Hq]).
+    Row j is the decode of its own query row over the first
+    row_context(ctx_b, q_len, j) tokens.  ``rows`` optionally restricts the
+    work to (b, j, h) triples (others stay NaN).
+    """
+    if q.ndim != 4:
+        raise ValueError("q must be [B][q_len][Hq][D]")
+    B, L, Hq, _ = q.shape
+    Dv = v_pool.shape[2]
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    out = np.full((B, L, Hq, Dv), np.nan)
+    lse = np.full((B, L, Hq), np.nan)
+    for j, heads in _rows_by_j(rows, L).items():
+        ctx_j = np.array([row_context(c, L, j) for c in ctx], dtype=np.int64)
+        out[:, j], lse[:, j] = paged_decode(np.ascontiguousarray(q[:, j]), k_pool, v_pool,
+                                            block_table, ctx_j, scale, dtype=dtype, heads=heads)
+    return out, lse
+
+
+def paged_decode_mla_rows(q, c_pool, block_table, context_lens, scale, dv=512, dtype="bf16",
+                          rows=None):
+    """The latent variant with q_len query rows per sequence (q [B][q_len][Hq][Dqk])."""
+    if q.ndim != 4:
+        raise ValueError("q must be [B][q_len][Hq][Dqk]")
+    B, L, Hq, _ = q.shape
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    out = np.full((B, L, Hq, dv), np.nan)
+    lse = np.full((B, L, Hq), np.nan)
+    for j, heads in _rows_by_j(rows, L).items():
+        ctx_j = np.array([row_context(c, L, j) for c in ctx], dtype=np.int64)
+        out[:, j], lse[:, j] = paged_decode_mla(np.ascontiguousarray(q[:, j]), c_pool, block_table,
+                                                ctx_j, scale, dv=dv, dtype=dtype, heads=heads)
+    return out, lse
+
+
 def decode_inputs(inp, heads=None):
-    """Run the reference on a workload object (compact pages + compact table)."""
+    """Run the reference on a workload object (compact pages + compact table).
+
+    For workloads with several query rows (q [B][q_len][Hq][D]) ``heads`` are
+    (b, j, h) triples."""
     bt = inp.compact_block_table()
+    if inp.q.ndim == 4:
+        if inp.kind == "mla":
+            return paged_decode_mla_rows(inp.q, inp.c_pages, bt, inp.context_lens, inp.scale,
+                                         dv=inp.head_dim_v, dtype=inp.dtype, rows=heads)
+        return paged_decode_rows(inp.q, inp.k_pages, inp.v_pages, bt, inp.context_lens,
+                                 inp.scale, dtype=inp.dtype, rows=heads)
     if inp.kind == "mla":
         return paged_decode_mla(inp.q, inp.c_pages, bt, inp.context_lens, inp.scale,
                                 dv=inp.head_dim_v, dtype=inp.dtype, heads=heads)

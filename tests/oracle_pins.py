@@ -428,6 +428,165 @@ def pin_append_latent(o):
     _close(lse, bl, what="latent append lse")
 
 
+# --------------------------------------------------------------------------
+# Several query rows per sequence: the rows are the last q_len tokens and
+# row j attends causally to positions 0 .. ctx - q_len + j
+# --------------------------------------------------------------------------
+
+ROW_CASES = [
+    # (seed, B, q_len, Hq, Hkv, D, Dv, bs, ctxs)
+    (50, 2, 3, 4, 2, 6, 6, 4, [7, 3]),          # ctx == q_len for b = 1
+    (51, 1, 4, 2, 1, 5, 3, 2, [9]),
+    (52, 3, 2, 3, 3, 4, 4, 16, [1, 17, 2]),     # ctx < q_len: row 0 of b = 0 sees nothing
+]
+
+
+def _tiny_rows(seed, B, L, Hq, Hkv, D, Dv, bs, ctxs):
+    q0, k, v, bt, ctx, scale = tiny_paged(seed, B, Hq, Hkv, D, Dv, bs, ctxs)
+    q = np.random.default_rng(seed + 1000).standard_normal((B, L, Hq, D))
+    return q, k, v, bt, ctx, scale
+
+
+def brute_force_rows(q, k, v, bt, ctxs, scale):
+    """Pure-Python causal attention: row j of sequence b sees positions i with
+    i <= ctx_b - q_len + j."""
+    B, L, Hq, D = q.shape
+    _, Hkv, bs, _ = k.shape
+    Dv = v.shape[2]
+    G = Hq // Hkv
+    ql, kl, vl, btl = q.tolist(), k.tolist(), v.tolist(), bt.tolist()
+    out = np.zeros((B, L, Hq, Dv))
+    lse = np.zeros((B, L, Hq))
+    for b in range(B):
+        last = int(ctxs[b]) - L          # position of row 0
+        for j in range(L):
+            for h in range(Hq):
+                g = h // G
+                vis = [i for i in range(int(ctxs[b])) if i <= last + j]
+                if not vis:
+                    out[b, j, h] = 0.0
+                    lse[b, j, h] = -math.inf
+                    continue
+                s = [scale * math.fsum(ql[b][j][h][d] * kl[btl[b][i // bs]][g][i % bs][d]
+                                       for d in range(D)) for i in vis]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                tot = math.fsum(e)
+                for d in range(Dv):
+                    out[b, j, h, d] = math.fsum(e[n] * vl[btl[b][i // bs]][g][d][i % bs]
+                                                for n, i in enumerate(vis)) / tot
+                lse[b, j, h] = m + math.log(tot)
+    return out, lse
+
+
+def pin_rows_bruteforce(o):
+    """Several query rows against pure-Python causal loops on tiny inputs."""
+    for case in ROW_CASES:
+        q, k, v, bt, ctx, scale = _tiny_rows(*case)
+        ref_o, ref_l = brute_force_rows(q, k, v, bt, ctx, scale)
+        out, lse = o.paged_decode_rows(q, k, v, bt, ctx, scale, dtype="f64")
+        _close(out, ref_o, what=f"rows out case {case[0]}")
+        _close(lse, ref_l, what=f"rows lse case {case[0]}")
+
+
+def pin_rows_sdpa(o):
+    """Dense (identity-paged) inputs against torch's SDPA on CPU in float64: a
+    fresh prompt (ctx == q_len) with is_causal, and a continuation with the
+    equivalent explicit mask."""
+    import torch
+    import torch.nn.functional as F
+
+    rng = np.random.default_rng(53)
+    for (B, L, Hq, Hkv, D, bs, ctx) in [(2, 8, 4, 2, 16, 4, 8), (1, 5, 6, 3, 8, 16, 37)]:
+        pages = -(-ctx // bs)
+        kd = rng.standard_normal((B, Hkv, pages * bs, D))
+        vd = rng.standard_normal((B, Hkv, pages * bs, D))
+        q = rng.standard_normal((B, L, Hq, D))
+        k_pool = kd.reshape(B, Hkv, pages, bs, D).transpose(0, 2, 1, 3, 4).reshape(B * pages, Hkv, bs, D)
+        v_pool = vd.reshape(B, Hkv, pages, bs, D).transpose(0, 2, 1, 4, 3).reshape(B * pages, Hkv, D, bs)
+        bt = np.arange(B * pages).reshape(B, pages)
+        scale = 1.0 / math.sqrt(D)
+        out, _ = o.paged_decode_rows(q, k_pool, v_pool, bt, np.full(B, ctx), scale, dtype="f64")
+        G = Hq // Hkv
+        kt = torch.from_numpy(np.ascontiguousarray(kd[:, :, :ctx])).repeat_interleave(G, dim=1)
+        vt = torch.from_numpy(np.ascontiguousarray(vd[:, :, :ctx])).repeat_interleave(G, dim=1)
+        qt = torch.from_numpy(np.ascontiguousarray(q.transpose(0, 2, 1, 3)))     # [B][Hq][L][D]
+        if ctx == L:
+            ref = F.scaled_dot_product_attention(qt, kt, vt, scale=scale, is_causal=True)
+        else:
+            allowed = torch.arange(ctx)[None, :] <= (ctx - L + torch.arange(L))[:, None]
+            ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=allowed, scale=scale)
+        _close(out, ref.numpy().transpose(0, 2, 1, 3), what=f"rows sdpa L{L} ctx{ctx}")
+
+
+def pin_rows_single_is_decode(o):
+    """One query row is the single-token decode, bit for bit; the last of
+    several rows sees the whole context and equals the decode of that row."""
+    q, k, v, bt, ctx, scale = _tiny_rows(54, 2, 3, 4, 2, 8, 8, 4, [10, 5])
+    out1, lse1 = o.paged_decode_rows(q[:, :1], k, v, bt, ctx, scale, dtype="f64")
+    ref_o, ref_l = o.paged_decode(np.ascontiguousarray(q[:, 0]), k, v, bt, ctx, scale, dtype="f64")
+    assert np.array_equal(out1[:, 0], ref_o) and np.array_equal(lse1[:, 0], ref_l)
+    out, lse = o.paged_decode_rows(q, k, v, bt, ctx, scale, dtype="f64")
+    ref_o, ref_l = brute_force(np.ascontiguousarray(q[:, 2]), k, v, bt, ctx, scale)
+    _close(out[:, 2], ref_o, what="last row out")
+    _close(lse[:, 2], ref_l, what="last row lse")
+
+
+def pin_rows_causality(o):
+    """Changing K/V at positions a row cannot see leaves that row unchanged
+    (bitwise) and changes the rows that can see them."""
+    q, k, v, bt, ctx, scale = _tiny_rows(55, 1, 4, 2, 2, 4, 4, 4, [11])
+    base_o, _ = o.paged_decode_rows(q, k, v, bt, ctx, scale, dtype="f64")
+    pos = 11 - 4 + 2                       # rows 0, 1 see up to 7, 8; rows 2, 3 see it
+    k2, v2 = k.copy(), v.copy()
+    page, slot = bt[0][pos // 4], pos % 4
+    k2[page, :, slot, :] += 3.0
+    v2[page, :, :, slot] -= 5.0
+    new_o, _ = o.paged_decode_rows(q, k2, v2, bt, ctx, scale, dtype="f64")
+    assert np.array_equal(new_o[0, :2], base_o[0, :2])
+    assert not np.allclose(new_o[0, 2:], base_o[0, 2:])
+
+
+def pin_mla_rows_bruteforce(o):
+    """The latent variant with several query rows, 64-token-like pages and
+    one-token pages (token-id lists), against pure-Python causal loops."""
+    for seed, bs, ctxs, L in ((56, 4, [6, 9], 3), (57, 1, [5, 2], 3)):
+        rng = np.random.default_rng(seed)
+        B, Hq, Dc, dv = 2, 3, 6, 4
+        n_pages = [-(-c // bs) for c in ctxs]
+        total = sum(n_pages) + 2
+        perm = rng.permutation(total)
+        bt = np.full((B, max(n_pages)), -1, dtype=np.int64)
+        off = 0
+        for b, n in enumerate(n_pages):
+            bt[b, :n] = perm[off:off + n]
+            off += n
+        c = rng.standard_normal((total, bs, Dc))
+        q = rng.standard_normal((B, L, Hq, Dc))
+        scale = 0.41
+        cl, qll, btl = c.tolist(), q.tolist(), bt.tolist()
+        ref_o = np.zeros((B, L, Hq, dv))
+        ref_l = np.zeros((B, L, Hq))
+        for b in range(B):
+            for j in range(L):
+                vis = [i for i in range(ctxs[b]) if i <= ctxs[b] - L + j]
+                for h in range(Hq):
+                    if not vis:
+                        ref_l[b, j, h] = -math.inf
+                        continue
+                    r = [cl[btl[b][i // bs]][i % bs] for i in vis]
+                    s = [scale * math.fsum(qll[b][j][h][d] * x[d] for d in range(Dc)) for x in r]
+                    m = max(s)
+                    e = [math.exp(x - m) for x in s]
+                    tot = math.fsum(e)
+                    ref_o[b, j, h] = [math.fsum(e[i] * r[i][d] for i in range(len(r))) / tot
+                                      for d in range(dv)]
+                    ref_l[b, j, h] = m + math.log(tot)
+        out, lse = o.paged_decode_mla_rows(q, c, bt, np.array(ctxs), scale, dv=dv, dtype="f64")
+        _close(out, ref_o, what=f"mla rows out bs{bs}")
+        _close(lse, ref_l, what=f"mla rows lse bs{bs}")
+
+
 ALL_PINS = [
     pin_bruteforce, pin_mla_bruteforce, pin_mla_token_index_list, pin_bf16_widening, pin_sdpa,
     pin_ctx_one,
@@ -435,4 +594,6 @@ ALL_PINS = [
     pin_page_permutation, pin_constant_values, pin_stability, pin_score_shift,
     pin_gqa_equals_mha, pin_mla_equals_mqa, pin_batch_independence, pin_sampled_heads,
     pin_append_then_decode, pin_append_out_of_range, pin_append_latent,
+    pin_rows_bruteforce, pin_rows_sdpa, pin_rows_single_is_decode, pin_rows_causality,
+    pin_mla_rows_bruteforce,
 ]

@@ -206,6 +206,22 @@ def _append_kv_skips_last(k_pool, v_pool, bt, ctx, k_new, v_new):
     return ref._orig_append_kv(k_pool, v_pool, bt[:-1], ctx[:-1], k_new[:-1], v_new[:-1])
 
 
+def _row_context_off_by_one(ctx, q_len, j):
+    return max(0, int(ctx) - q_len + j)
+
+
+def _row_context_no_mask(ctx, q_len, j):
+    return int(ctx)
+
+
+def _row_context_reversed(ctx, q_len, j):
+    return max(0, int(ctx) - j)
+
+
+def _row_context_one_past(ctx, q_len, j):
+    return min(int(ctx), max(0, int(ctx) - q_len + 2 + j))
+
+
 MUTANTS = {
     "scores_noscale": ("scores", _scores_noscale),
     "scores_negated": ("scores", _scores_negated),
@@ -234,6 +250,10 @@ MUTANTS = {
     "append_slot_previous_page": ("append_slot", _append_slot_previous_page),
     "append_slot_no_table_check": ("append_slot", _append_slot_no_table_check),
     "append_kv_skips_last_sequence": ("append_kv", _append_kv_skips_last),
+    "rows_context_off_by_one": ("row_context", _row_context_off_by_one),
+    "rows_unmasked": ("row_context", _row_context_no_mask),
+    "rows_reversed": ("row_context", _row_context_reversed),
+    "rows_see_one_ahead": ("row_context", _row_context_one_past),
 }
 
 
