@@ -43,10 +43,11 @@ KERNEL_OF = {"mha": "pa_mha.hip", "gqa": "pa_gqa.hip", "mla": "pa_mla.hip"}
 
 
 def kernel_family(inp) -> str:
+    """Which partial kernel serves the workload (the library's own dispatch rule)."""
     if inp.kind == "mla":
         return "mla"
-    if inp.dtype == "bf16" and inp.num_q_heads != inp.num_kv_heads and inp.head_dim == 128 \
-            and inp.block_size == 16 and inp.num_q_heads // inp.num_kv_heads <= 16:
+    cols = inp.num_q_heads // inp.num_kv_heads * inp.q_len   # MFMA columns: (row, head) pairs
+    if inp.dtype == "bf16" and inp.head_dim == 128 and inp.block_size == 16 and 2 <= cols <= 16:
         return "gqa"
     return "mha"
 
@@ -111,14 +112,15 @@ class Case:
             batch=inp.batch, num_q_heads=inp.num_q_heads, num_kv_heads=inp.num_kv_heads,
             head_dim=inp.head_dim, head_dim_v=inp.head_dim_v, block_size=inp.block_size,
             max_blocks_per_seq=inp.max_blocks_per_seq, num_blocks=inp.num_blocks,
-            max_context_len=inp.max_context_len, scale=inp.scale, dtype=torch_dtype(inp.dtype))
+            max_context_len=inp.max_context_len, scale=inp.scale, dtype=torch_dtype(inp.dtype),
+            q_len=inp.q_len)
         self.S = pa.choose_num_splits(self.shape, 0, self.mla)
         nbytes = pa.workspace_size(self.shape, self.S, self.mla)
         # zero-filled: the fused reduction's arrival counters start at 0
         self.ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device="cuda")
-        self.out = torch.empty((inp.batch, inp.num_q_heads, inp.head_dim_v),
-                               dtype=torch_dtype(inp.dtype), device="cuda")
-        self.lse = torch.empty((inp.batch, inp.num_q_heads), dtype=torch.float32, device="cuda")
+        rows = (inp.batch, inp.num_q_heads) if inp.q_len == 1 else (inp.batch, inp.q_len, inp.num_q_heads)
+        self.out = torch.empty(rows + (inp.head_dim_v,), dtype=torch_dtype(inp.dtype), device="cuda")
+        self.lse = torch.empty(rows, dtype=torch.float32, device="cuda")
         lib = _lib.load()
         P = ctypes.c_void_p
         stream = P(torch.cuda.current_stream().cuda_stream)
@@ -171,8 +173,9 @@ class Case:
 
     def flops(self) -> float:
         i = self.inp
-        toks = self.tokens
-        return 2.0 * toks * i.num_q_heads * (i.head_dim + i.head_dim_v)
+        # (query row, context token) pairs: row j of q_len sees ctx - q_len + 1 + j tokens
+        pairs = sum(max(0, int(c) - i.q_len + 1 + j) for c in i.context_lens for j in range(i.q_len))
+        return 2.0 * pairs * i.num_q_heads * (i.head_dim + i.head_dim_v)
 
     def _loop(self, fn, steps: int):
         """Average ms per call of `fn` over `steps` back-to-back calls.
@@ -246,7 +249,8 @@ class Case:
             kernel=self.family,
             ms_per_step=round(r["ms_per_step"], 5),
             ev_ms_per_step=round(r["ev_ms_per_step"], 5),
-            tokens_per_s=round(self.inp.batch / (r["ms_per_step"] * 1e-3), 1),
+            tokens_per_s=round(self.inp.batch * self.inp.q_len / (r["ms_per_step"] * 1e-3), 1),
+            q_len=self.inp.q_len,
             partial_ms=round(r["partial_ms"], 5),
             reduce_ms=round(r["reduce_ms"], 5),
             kv_bytes=self.kv_bytes,

@@ -5,7 +5,8 @@ the library's HIP kernels; this module only checks tensors, sizes the
 workspace (a torch allocation) and passes pointers and the current stream.
 
 Layouts (see include/pa_decode.h):
-    q            [B][Hq][D]                 float32 or bfloat16
+    q            [B][Hq][D], or [B][q_len][Hq][D] for several query rows
+                 (the sequence's last q_len tokens, causal)  float32 or bfloat16
     k_cache      [num_blocks][Hkv][bs][D]
     v_cache      [num_blocks][Hkv][D][bs]
     kv_cache     [num_blocks][bs][Dqk]      (MLA latent; values = first Dv entries)
@@ -65,14 +66,25 @@ def _need(t, name, dtype=None, ndim=None, device=None):
 
 
 def make_shape(*, batch, num_q_heads, num_kv_heads, head_dim, head_dim_v, block_size,
-               max_blocks_per_seq, num_blocks, max_context_len, scale, dtype) -> PaShape:
+               max_blocks_per_seq, num_blocks, max_context_len, scale, dtype, q_len=1) -> PaShape:
     code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     return PaShape(batch, num_q_heads, num_kv_heads, head_dim, head_dim_v, block_size,
-                   max_blocks_per_seq, num_blocks, int(max_context_len), float(scale), code)
+                   max_blocks_per_seq, num_blocks, int(max_context_len), float(scale), code,
+                   int(q_len))
+
+
+def _q_dims(q):
+    """(B, q_len, Hq, D) of a [B][Hq][D] or [B][q_len][Hq][D] query tensor."""
+    if q.dim() == 3:
+        B, Hq, D = q.shape
+        return B, 1, Hq, D
+    if q.dim() == 4:
+        return tuple(q.shape)
+    raise ValueError("q must be [B][Hq][D] or [B][q_len][Hq][D]")
 
 
 def _mha_shape(q, k_cache, v_cache, block_table, context_lens, max_context_len, scale):
-    _need(q, "q", ndim=3)
+    _need(q, "q")
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
     dev = q.device
@@ -80,7 +92,7 @@ def _mha_shape(q, k_cache, v_cache, block_table, context_lens, max_context_len, 
     _need(v_cache, "v_cache", q.dtype, 4, dev)
     _need(block_table, "block_table", torch.int32, 2, dev)
     _need(context_lens, "context_lens", torch.int32, 1, dev)
-    B, Hq, D = q.shape
+    B, L, Hq, D = _q_dims(q)
     nb, Hkv, bs, Dk = k_cache.shape
     if Dk != D:
         raise ValueError("k_cache head dim differs from q")
@@ -95,18 +107,18 @@ def _mha_shape(q, k_cache, v_cache, block_table, context_lens, max_context_len, 
     return make_shape(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
                       head_dim_v=v_cache.shape[2], block_size=bs,
                       max_blocks_per_seq=block_table.shape[1], num_blocks=nb,
-                      max_context_len=max_context_len, scale=scale, dtype=q.dtype)
+                      max_context_len=max_context_len, scale=scale, dtype=q.dtype, q_len=L)
 
 
 def _mla_shape(q, kv_cache, block_table, context_lens, max_context_len, scale, head_dim_v):
-    _need(q, "q", ndim=3)
+    _need(q, "q")
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
     dev = q.device
     _need(kv_cache, "kv_cache", q.dtype, 3, dev)
     _need(block_table, "block_table", torch.int32, 2, dev)
     _need(context_lens, "context_lens", torch.int32, 1, dev)
-    B, Hq, D = q.shape
+    B, L, Hq, D = _q_dims(q)
     nb, bs, Dc = kv_cache.shape
     if Dc != D:
         raise ValueError("kv_cache width differs from q")
@@ -114,7 +126,7 @@ def _mla_shape(q, kv_cache, block_table, context_lens, max_context_len, scale, h
         max_context_len = int(context_lens.max().item()) if B else 0
     return make_shape(batch=B, num_q_heads=Hq, num_kv_heads=1, head_dim=D, head_dim_v=head_dim_v,
                       block_size=bs, max_blocks_per_seq=block_table.shape[1], num_blocks=nb,
-                      max_context_len=max_context_len, scale=scale, dtype=q.dtype)
+                      max_context_len=max_context_len, scale=scale, dtype=q.dtype, q_len=L)
 
 
 def choose_num_splits(shape: PaShape, num_cus: int = 0, mla: bool = False) -> int:
@@ -138,16 +150,19 @@ def workspace_size(shape: PaShape, num_splits: int = 0, mla: bool = False) -> in
 
 def _outputs(shape, q, out, lse, workspace, num_splits, mla):
     B, Hq, Dv = shape.batch, shape.num_q_heads, shape.head_dim_v
+    rows = (B, Hq) if q.dim() == 3 else (B, q.shape[1], Hq)
     if out is None:
-        out = torch.empty((B, Hq, Dv), dtype=q.dtype, device=q.device)
+        out = torch.empty(rows + (Dv,), dtype=q.dtype, device=q.device)
     else:
-        _need(out, "out", q.dtype, 3, q.device)
-        if tuple(out.shape) != (B, Hq, Dv):
-            raise ValueError("out must be [B][Hq][Dv]")
+        _need(out, "out", q.dtype, q.dim(), q.device)
+        if tuple(out.shape) != rows + (Dv,):
+            raise ValueError("out must be [B][Hq][Dv] (or [B][q_len][Hq][Dv])")
     if lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        lse = torch.empty(rows, dtype=torch.float32, device=q.device)
     elif lse is not False:
-        _need(lse, "lse", torch.float32, 2, q.device)
+        _need(lse, "lse", torch.float32, q.dim() - 1, q.device)
+        if tuple(lse.shape) != rows:
+            raise ValueError("lse must be [B][Hq] (or [B][q_len][Hq])")
     need = workspace_size(shape, num_splits, mla)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         # zero-filled: the fused reduction's arrival counters must start at 0

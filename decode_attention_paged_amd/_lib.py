@@ -30,6 +30,7 @@ class PaShape(ctypes.Structure):
         ("max_context_len", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
     ]
 
 

@@ -15,6 +15,10 @@ constexpr int kMaxSplits = 65535;          // grid y limit
 constexpr long kFusedMergeBytes = 4 * 1024;   // largest per-unit partial set merged in-kernel
 constexpr double kSplitBytesValu = 128.0 * 1024.0;   // KV bytes per workgroup, VALU kernel
 constexpr double kSplitBytesMfma = 1024.0 * 1024.0;  // KV bytes per workgroup, MFMA kernel
+constexpr int kMaxQLen = 16;                         // query rows per sequence
+
+// Query rows per sequence (0 and 1 both mean one row).
+int rows_of(const pa_shape& s) { return s.q_len > 1 ? s.q_len : 1; }
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -30,8 +34,10 @@ Kernel pick_kernel(const pa_shape& s, bool mla) {
   }
   if (s.head_dim_v != s.head_dim) return Kernel::None;
   const int G = s.num_q_heads / s.num_kv_heads;
-  if (pa::gqa_mfma_supported(bf16, s.head_dim, s.head_dim_v, s.block_size, G)) return Kernel::GqaMfma;
-  if (pa::mha_valu_supported(bf16, s.head_dim, s.block_size)) return Kernel::MhaValu;
+  const int ql = rows_of(s);
+  if (pa::gqa_mfma_supported(bf16, s.head_dim, s.head_dim_v, s.block_size, G, ql))
+    return Kernel::GqaMfma;
+  if (ql == 1 && pa::mha_valu_supported(bf16, s.head_dim, s.block_size)) return Kernel::MhaValu;
   return Kernel::None;
 }
 
@@ -44,6 +50,8 @@ pa_status check_shape(const pa_shape* s, bool mla) {
       s->max_context_len < 0)
     return PA_ERR_INVALID;
   if (s->num_q_heads % s->num_kv_heads != 0) return PA_ERR_INVALID;
+  if (s->q_len < 0) return PA_ERR_INVALID;
+  if (s->q_len > kMaxQLen) return PA_ERR_UNSUPPORTED;
   if ((int64_t)s->max_context_len > (int64_t)s->max_blocks_per_seq * s->block_size)
     return PA_ERR_INVALID;
   if (s->dtype != PA_F32 && s->dtype != PA_BF16) return PA_ERR_INVALID;
@@ -95,8 +103,8 @@ int heuristic_splits(const pa_shape& s, int cus, bool mla) {
   long S;
   if (k == Kernel::MlaMfma) {
     // one workgroup per (head group, sequence, split): fill the CUs once
-    const long groups =
-        (long)s.batch * (s.num_q_heads / pa::mla_heads_per_workgroup(s.num_q_heads, s.block_size));
+    const long groups = (long)s.batch * rows_of(s) *
+                        (s.num_q_heads / pa::mla_heads_per_workgroup(s.num_q_heads, s.block_size));
     S = (cus + groups - 1) / groups;
     // one-token pages: a split holds at most mla_max_split_tokens ids
     const long max_c = pa::mla_max_split_tokens(s.block_size);
@@ -108,7 +116,7 @@ int heuristic_splits(const pa_shape& s, int cus, bool mla) {
     double target_bytes;
     if (k == Kernel::GqaMfma) {
       units = (long)s.batch * s.num_kv_heads;
-      heads_per_wg = s.num_q_heads / s.num_kv_heads;
+      heads_per_wg = s.num_q_heads / s.num_kv_heads * rows_of(s);   // partial rows per workgroup
       target_bytes = kSplitBytesMfma;
     } else {
       units = (long)s.batch * s.num_q_heads;
@@ -145,17 +153,18 @@ int resolve_splits(const pa_shape& s, int32_t num_splits, bool mla) {
   return S;
 }
 
-// Workspace layout (S > 1): o_part f32 [B][Hq][S][Dv] | lse_part f32 [B][Hq][S]
-// | counters i32 [B][Hq], each 256-byte aligned.
+// Workspace layout (S > 1), R = B * q_len * Hq rows: o_part f32 [R][S][Dv] |
+// lse_part f32 [R][S] | counters i32 [R], each 256-byte aligned.
+size_t ws_rows(const pa_shape& s) { return (size_t)s.batch * rows_of(s) * s.num_q_heads; }
 size_t ws_lse_offset(const pa_shape& s, int S) {
-  return align_up((size_t)s.batch * s.num_q_heads * S * s.head_dim_v * sizeof(float));
+  return align_up(ws_rows(s) * S * s.head_dim_v * sizeof(float));
 }
 size_t ws_counter_offset(const pa_shape& s, int S) {
-  return ws_lse_offset(s, S) + align_up((size_t)s.batch * s.num_q_heads * S * sizeof(float));
+  return ws_lse_offset(s, S) + align_up(ws_rows(s) * S * sizeof(float));
 }
 size_t workspace_bytes_for(const pa_shape& s, int S) {
   if (S <= 1) return 0;
-  return ws_counter_offset(s, S) + align_up((size_t)s.batch * s.num_q_heads * sizeof(int32_t));
+  return ws_counter_offset(s, S) + align_up(ws_rows(s) * sizeof(int32_t));
 }
 
 pa::Params make_params(const pa_shape& s, int S, const void* q, const void* k, const void* v,
@@ -177,6 +186,7 @@ pa::Params make_params(const pa_shape& s, int S, const void* q, const void* k, c
   p.maxb = s.max_blocks_per_seq;
   p.nblocks = s.num_blocks;
   p.max_ctx = s.max_context_len;
+  p.ql = rows_of(s);
   p.S = S;
   const int P = max_pages(s);
   p.c = P > 0 ? (P + S - 1) / S : 1;
@@ -198,7 +208,7 @@ pa::Params make_params(const pa_shape& s, int S, const void* q, const void* k, c
 // 8 KiB of partials per unit up (batch 16 x 32 heads at 16 splits: 110 us
 // against 116 us), so only tiny merges stay in-kernel.
 bool fuses(const pa_shape& s, int S, Kernel kern) {
-  if (S <= 1 || kern == Kernel::MlaMfma || kern == Kernel::None) return false;
+  if (S <= 1 || kern == Kernel::MlaMfma || kern == Kernel::None || rows_of(s) > 1) return false;
   const long unit_heads = kern == Kernel::GqaMfma ? s.num_q_heads / s.num_kv_heads : 1;
   const long merge_bytes = (long)S * unit_heads * (s.head_dim_v + 1) * 4;
   return merge_bytes <= kFusedMergeBytes;
@@ -310,7 +320,7 @@ pa_status pa_workspace_init(const pa_shape* shape, int32_t num_splits, int32_t m
   if (S <= 1) return PA_OK;
   if (!workspace || workspace_bytes < workspace_bytes_for(*shape, S)) return PA_ERR_WORKSPACE;
   int32_t* cnt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ws_counter_offset(*shape, S));
-  const size_t n = (size_t)shape->batch * shape->num_q_heads;
+  const size_t n = ws_rows(*shape);
   return pa::launch_zero_i32(cnt, n, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK
                                                                                     : PA_ERR_HIP;
 }

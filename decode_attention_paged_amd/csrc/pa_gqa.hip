@@ -62,9 +62,11 @@ __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x
 template <bool PARTIAL>
 __device__ __forceinline__ void consume_pair(PairTile& t, const u32x4 (&qf)[4], f32x4 (&acc)[8],
                                              float& m, float& l, float scale_log2, int tok0,
-                                             int ctx) {
+                                             int ctx_col, int ctx) {
   // tok0: logical index of this lane's first score token; the lane's tokens
-  // are tok0 .. tok0+7 (tok0 < 0 marks a page missing from the pair).
+  // are tok0 .. tok0+7 (tok0 < 0 marks a page missing from the pair).  The
+  // lane's column sees tokens below ctx_col (ctx, or less for an earlier
+  // query row); V rows at or past ctx are zeroed.
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -79,20 +81,23 @@ __device__ __forceinline__ void consume_pair(PairTile& t, const u32x4 (&qf)[4], 
   }
   if constexpr (PARTIAL) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sc[j] = (tok0 >= 0 && tok0 + j < ctx) ? sc[j] : kNegInf;
+    for (int j = 0; j < 8; ++j) sc[j] = (tok0 >= 0 && tok0 + j < ctx_col) ? sc[j] : kNegInf;
   }
   float mx = sc[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sc[j]);
   mx = max_xor32(max_xor16(mx));
   const float mn = fmaxf(m, mx);
-  const float alpha = fast_exp2(m - mn);
+  // a column that has seen no token yet (an early query row) keeps m = -inf
+  // and takes weights of 0 instead of exp2(-inf - -inf)
+  const float mref = (PARTIAL && mn == kNegInf) ? 0.f : mn;
+  const float alpha = fast_exp2(m - mref);
   m = mn;
   float pr[8];
   float ls = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    pr[j] = fast_exp2(sc[j] - mn);
+    pr[j] = fast_exp2(sc[j] - mref);
     ls += pr[j];
   }
   l = fmaf(l, alpha, ls);
@@ -130,17 +135,25 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int quad = lane >> 4, n = lane & 15;
   const int G = p.Hq / p.Hkv;
+  const int ql = p.ql;
+  const int NC = G * ql;                             // MFMA columns in use (<= 16)
   const int ctx = clampi(p.context_lens[b], 0, p.max_ctx);
+  // column n is query row cj = n / G of head cg = n % G; row j sees the first
+  // ctx - ql + 1 + j tokens (causal over the last ql positions)
+  const int cj = n / G, cg = n - cj * G;
+  const int ctx_col = ctx - ql + 1 + cj;
+  const int ctx_lo = ctx - ql + 1;                   // the shortest any column sees
   const int pages = (ctx + kBS - 1) / kBS;
   const int nsplit = splits_of(pages, p.c);
   if (s >= (nsplit > 0 ? nsplit : 1)) return;
   const int p0 = s * p.c;
   const int p1 = min(pages, p0 + p.c);
 
-  // Q^T as the B operand of the score MFMA: column n = head kvh*G + n
+  // Q^T as the B operand of the score MFMA: column n = (row cj, head kvh*G + cg)
   u32x4 qf[4];
-  if (n < G) {
-    const char* qr = static_cast<const char*>(p.q) + ((size_t)b * p.Hq + kvh * G + n) * kRowB;
+  if (n < NC) {
+    const char* qr =
+        static_cast<const char*>(p.q) + (((size_t)b * ql + cj) * p.Hq + kvh * G + cg) * kRowB;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) qf[kb] = ld128(qr + kb * 64 + quad * 16);
   } else {
@@ -180,13 +193,13 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
   auto consume = [&](PairTile& t, int kk) {
     const int pa_ = p0 + 2 * kk;
     const bool hasb = pa_ + 1 < p1;
-    const bool partial = !hasb || (pa_ + 2) * kBS > ctx;
+    const bool partial = !hasb || (pa_ + 2) * kBS > ctx_lo;
     const int mypage = vsel ? pa_ + 1 : pa_;
     const int tok0 = (vsel && !hasb) ? -1 : mypage * kBS + (quad & 1) * 8;
     if (partial)
-      consume_pair<true>(t, qf, acc, m, l, p.scale_log2, tok0, ctx);
+      consume_pair<true>(t, qf, acc, m, l, p.scale_log2, tok0, ctx_col, ctx);
     else
-      consume_pair<false>(t, qf, acc, m, l, p.scale_log2, tok0, ctx);
+      consume_pair<false>(t, qf, acc, m, l, p.scale_log2, tok0, ctx_col, ctx);
   };
   // Two register tiles in turn: while one pair is consumed the next one's
   // loads are in flight, and each consume waits only for its own loads (a
@@ -219,8 +232,9 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
   __syncthreads();
 
   const bool direct = split_is_direct(p, nsplit);
-  for (int idx = threadIdx.x; idx < G * kD; idx += NW * 64) {
+  for (int idx = threadIdx.x; idx < NC * kD; idx += NW * 64) {
     const int hn = idx / kD, d = idx % kD;
+    const int rj = hn / G, rg = hn - rj * G;
     float M = kNegInf;
 #pragma unroll
     for (int i = 0; i < NW; ++i) M = fmaxf(M, sm_m[i][hn]);
@@ -234,7 +248,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
     }
     o = empty ? 0.f : o / L;
     const float lse = empty ? kNegInf : (M + fast_log2(L)) * kLn2;
-    const size_t row = (size_t)b * p.Hq + kvh * G + hn;
+    const size_t row = ((size_t)b * ql + rj) * p.Hq + kvh * G + rg;
     if (direct) {
       store_out<true>(p, row, d, o);
       if (d == 0 && p.lse) p.lse[row] = lse;
@@ -257,8 +271,9 @@ constexpr int kGqaWaves = 4;
 
 }  // namespace
 
-bool gqa_mfma_supported(bool bf16, int D, int Dv, int bs, int G) {
-  return bf16 && D == kD && Dv == kD && bs == kBS && G >= 2 && G <= 16;
+bool gqa_mfma_supported(bool bf16, int D, int Dv, int bs, int G, int ql) {
+  const int cols = G * ql;
+  return bf16 && D == kD && Dv == kD && bs == kBS && G >= 1 && cols >= 2 && cols <= 16;
 }
 
 hipError_t launch_gqa_mfma(const Params& p, hipStream_t st) {

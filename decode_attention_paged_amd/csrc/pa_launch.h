@@ -9,17 +9,18 @@ namespace pa {
 // Everything a partial or reduce kernel needs, passed by value as the kernel
 // argument.  Pointers are device pointers owned by the caller.
 struct Params {
-  const void* q;             // [B][Hq][Dqk]
+  const void* q;             // [B][ql][Hq][Dqk]
   const void* k;             // MHA/GQA: [nb][Hkv][bs][D]; MLA: latent [nb][bs][Dqk]
   const void* v;             // MHA/GQA: [nb][Hkv][Dv][bs]; MLA: unused (aliases k)
   const int32_t* block_table;  // [B][maxb]
   const int32_t* context_lens; // [B]
-  void* out;                 // [B][Hq][Dv] dtype
-  float* lse;                // [B][Hq] or nullptr
-  float* o_part;             // [B][Hq][S][Dv] (S > 1)
-  float* lse_part;           // [B][Hq][S]     (S > 1)
-  int32_t* counters;         // [B][Hq] arrival counters of the fused reduction (S > 1)
+  void* out;                 // [B][ql][Hq][Dv] dtype
+  float* lse;                // [B][ql][Hq] or nullptr
+  float* o_part;             // [B][ql][Hq][S][Dv] (S > 1)
+  float* lse_part;           // [B][ql][Hq][S]     (S > 1)
+  int32_t* counters;         // [B][Hq] arrival counters of the fused reduction (S > 1, ql == 1)
   int32_t B, Hq, Hkv, D, Dv, bs, maxb, nblocks, max_ctx;
+  int32_t ql;                // query rows per sequence (>= 1): rows are (b, j, h), j < ql
   int32_t S;                 // splits in the grid
   int32_t c;                 // pages per split
   float scale_log2;          // scale * log2(e)
@@ -49,7 +50,9 @@ hipError_t launch_append(const AppendParams& a, bool bf16, bool mla, hipStream_t
 
 // Which kernels exist (host-side predicates used by validation and dispatch).
 bool mha_valu_supported(bool bf16, int D, int bs);
-bool gqa_mfma_supported(bool bf16, int D, int Dv, int bs, int G);
+// G query heads per KV head, ql query rows: the kernel's 16 MFMA columns hold
+// the G * ql (row, head) pairs of a KV head.
+bool gqa_mfma_supported(bool bf16, int D, int Dv, int bs, int G, int ql);
 bool mla_mfma_supported(bool bf16, int Dqk, int Dv, int bs, int Hq);
 // Query heads one MLA workgroup holds (the grid has Hq / this head groups).
 int mla_heads_per_workgroup(int Hq, int bs);

@@ -310,6 +310,31 @@ struct ValueOps {
   }
 };
 
+// Head group hg and (sequence, split) unit u of workgroup L, for HG head
+// groups per unit and U units.  The HG workgroups of a unit are 8 apart in
+// dispatch order: workgroups go round-robin to the 8 XCDs, so they run on the
+// same XCD at about the same time and all but the first read the latent rows
+// from its L2.  Head groups are groups of query heads, or of query rows when
+// a sequence has several.
+__device__ __forceinline__ void group_and_unit(int L, int HG, int U, int& hg, int& u) {
+  const int full = (U / 8) * 8 * HG;                  // workgroups in whole groups of 8 units
+  if (L < full) {
+    const int g = L / (8 * HG), r = L - g * 8 * HG;
+    hg = r >> 3;
+    u = g * 8 + (r & 7);
+  } else {
+    const int r = L - full;
+    hg = r % HG;
+    u = (U / 8) * 8 + r / HG;
+  }
+}
+
+// Causal end of the query row that head group head0 (of Hq * ql row-heads)
+// belongs to: row j sees ctx - ql + 1 + j tokens.
+__device__ __forceinline__ int row_end(int ctx, int head0, const Params& p) {
+  return ctx - p.ql + 1 + head0 / p.Hq;
+}
+
 // ---------------------------------------------------------------------------
 // Role-split workgroup: two waves per SIMD, one scoring and one accumulating.
 //
@@ -617,35 +642,21 @@ __global__ __launch_bounds__((RoleCfg<HH, HBW>::NW * 64)) void mla_roles_partial
   __shared__ __attribute__((aligned(16))) uint16_t pl_lds[2 * C::NH * kCT];
   __shared__ int ids_lds[BS == 1 ? kMaxIdsBS1 : 1];
 
-  // 1-D grid of HG x S x B workgroups.  With two head groups, the two
-  // workgroups of one (sequence, split) are 8 apart in dispatch order: the
-  // same XCD (workgroups go round-robin to the 8 XCDs) at about the same time,
-  // so the second reads the latent rows from that XCD's L2.
-  const int HG = p.Hq / C::NH;
+  // 1-D grid of HG x S x B workgroups, HG = ql * Hq / NH head groups
+  const int HG = p.ql * p.Hq / C::NH;
   int hg, u;
-  const int L = blockIdx.x, g16 = L >> 4;
-  if (HG == 2 && (g16 + 1) * 16 <= (int)gridDim.x) {
-    hg = (L >> 3) & 1;
-    u = (g16 << 3) | (L & 7);
-  } else if (HG == 2) {                               // last, partial group of 16
-    const int r = L - (g16 << 4);
-    hg = r & 1;
-    u = (g16 << 3) + (r >> 1);
-  } else {
-    hg = L % HG;
-    u = L / HG;
-  }
+  group_and_unit(blockIdx.x, HG, p.S * p.B, hg, u);
   const int b = u / p.S;
   const int s = split_of_block(u % p.S, b, p.S);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int head0 = hg * C::NH;
+  const int head0 = hg * C::NH;                       // of the ql * Hq row-heads
   const int ctx = clampi(p.context_lens[b], 0, p.max_ctx);
   const int pages = (ctx + BS - 1) / BS;
   const int nsplit = splits_of(pages, p.c);
   if (s >= (nsplit > 0 ? nsplit : 1)) return;
   const int t0 = s * p.c * BS;
-  const int t1 = min(ctx, (s * p.c + p.c) * BS);
+  const int t1 = min(row_end(ctx, head0, p), (s * p.c + p.c) * BS);
   const int p1 = min(pages, s * p.c + p.c);
   const int nchunks = t1 > t0 ? (t1 - t0 + kCT - 1) / kCT : 0;
 
@@ -661,7 +672,7 @@ __global__ __launch_bounds__((RoleCfg<HH, HBW>::NW * 64)) void mla_roles_partial
   src.lane = lane;
   if constexpr (BS == 1) src.ids = ids_lds;
   auto begin_pass = [&]() { src.begin(s * p.c); };
-  const size_t row0 = (size_t)b * p.Hq + head0;
+  const size_t row0 = (size_t)b * p.ql * p.Hq + head0;
 
   if (w < C::NS) {
     ScoreRole<HH, HBW, BS> r{sh, w & 1, w >> 1, lane, t0, t1, p.scale_log2};
@@ -718,7 +729,7 @@ __global__ __launch_bounds__((RoleCfg<HH, HBW>::NW * 64)) void mla_roles_partial
 template <int HH, int HBW>
 hipError_t launch_roles(const Params& p, hipStream_t st) {
   using C = RoleCfg<HH, HBW>;
-  const long blocks = (long)(p.Hq / C::NH) * p.S * p.B;
+  const long blocks = (long)(p.ql * p.Hq / C::NH) * p.S * p.B;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
   if (p.bs == 1)
     hipLaunchKernelGGL((mla_roles_partial<HH, HBW, 1>), dim3((unsigned)blocks), dim3(C::NW * 64), 0,
@@ -867,9 +878,9 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
   __shared__ __attribute__((aligned(16))) char ring_lds[kRing * kChunkB];
   __shared__ __attribute__((aligned(16))) uint16_t pl_lds[2 * kWideNH * kCT];
 
-  const int HG = p.Hq / kWideNH;
-  const int hg = blockIdx.x % HG;
-  const int u = blockIdx.x / HG;
+  const int HG = p.ql * p.Hq / kWideNH;               // head groups (of query rows too)
+  int hg, u;
+  group_and_unit(blockIdx.x, HG, p.S * p.B, hg, u);
   // split-major: the splits of sequence b are B workgroups apart, so with B a
   // multiple of 8 they share an XCD (workgroups go round-robin to the 8
   // XCDs) and its L2 serves the queries to all but the first
@@ -884,14 +895,14 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
   const int nsplit = splits_of(pages, p.c);
   if (s >= (nsplit > 0 ? nsplit : 1)) return;
   const int t0 = s * p.c * 64;
-  const int t1 = min(ctx, (s * p.c + p.c) * 64);
+  const int t1 = min(row_end(ctx, head0, p), (s * p.c + p.c) * 64);
   const int p1 = min(pages, s * p.c + p.c);
   const int nchunks = t1 > t0 ? (t1 - t0 + kCT - 1) / kCT : 0;
   const float cs = p.scale_log2;                      // > 0, checked by the host
   const int nwi = (kDmaInst - w + kWideNW - 1) / kWideNW;   // this wave's loads per chunk
 
   WideState st;
-  const size_t row0 = (size_t)b * p.Hq + head0;
+  const size_t row0 = (size_t)b * p.ql * p.Hq + head0;
   {
     const char* qr = static_cast<const char*>(p.q) + (row0 + 16 * w + n) * kRowB;
 #pragma unroll
@@ -1010,7 +1021,7 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
 }
 
 hipError_t launch_wide(const Params& p, hipStream_t st) {
-  const long blocks = (long)(p.Hq / kWideNH) * p.S * p.B;
+  const long blocks = (long)(p.ql * p.Hq / kWideNH) * p.S * p.B;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(mla_wide_partial, dim3((unsigned)blocks), dim3(kWideNW * 64), 0, st, p);
   return hipGetLastError();

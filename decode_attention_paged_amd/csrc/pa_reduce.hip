@@ -5,7 +5,7 @@
 //   M = max_s lse_s,  w_s = exp(lse_s - M),
 //   out = sum_s w_s o_s / sum_s w_s,  lse = M + ln(sum_s w_s).
 //
-// One wave per (sequence, query head) row, four rows per workgroup.  The
+// One wave per (sequence, query row, head) row, four rows per workgroup.  The
 // row's split weights come from its lse values (uniform across the wave);
 // each lane owns float4 columns of the output and sums the splits it needs
 // with 16-byte loads, several splits in flight at once.  Only the splits the
@@ -34,8 +34,8 @@ template <bool BF16>
 __global__ __launch_bounds__(kRedWaves * 64) void split_reduce(Params p) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRedWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (row >= p.B * p.Hq) return;
-  const int b = row / p.Hq;
+  if (row >= p.B * p.ql * p.Hq) return;
+  const int b = row / (p.ql * p.Hq);                 // rows are (sequence, query row, head)
   const int ctx = clampi(p.context_lens[b], 0, p.max_ctx);
   const int pages = (ctx + p.bs - 1) / p.bs;
   int nsp = splits_of(pages, p.c);
@@ -106,7 +106,7 @@ hipError_t launch_zero_i32(int32_t* dst, size_t n, hipStream_t st) {
 }
 
 hipError_t launch_reduce(const Params& p, bool bf16, hipStream_t st) {
-  const int rows = p.B * p.Hq;
+  const int rows = p.B * p.ql * p.Hq;
   dim3 grid((rows + kRedWaves - 1) / kRedWaves);
   if (bf16)
     hipLaunchKernelGGL(split_reduce<true>, grid, dim3(kRedWaves * 64), 0, st, p);

@@ -24,16 +24,26 @@
  *   computed in parallel with its log-sum-exp, and the split results are
  *   rescaled and reduced into the exact output.
  *
+ * Several query rows (q_len > 1: chunked prefill, draft verification): the
+ *   rows are each sequence's last q_len tokens, whose K/V are already in the
+ *   cache, and row j (position context_lens[b] - q_len + j) attends to
+ *   positions 0 .. context_lens[b] - q_len + j.  The pages name the prefill
+ *   stage and FlashAttention's exact attention over many query rows (the
+ *   FlashMLA-ETAP related-papers page, its FlashAttention abstracts) but no
+ *   mask; this causal reading reduces to the definition above at q_len = 1.
+ *   A row that sees no token gives out = 0 and lse = -inf.
+ *
  * Memory layouts (all row-major, contiguous, device memory):
- *   q            [batch][num_q_heads][head_dim]                    dtype
+ *   q            [batch][q_len][num_q_heads][head_dim]             dtype
  *   k_cache      [num_blocks][num_kv_heads][block_size][head_dim]  dtype
  *   v_cache      [num_blocks][num_kv_heads][head_dim_v][block_size] dtype
  *   kv_cache     [num_blocks][block_size][head_dim]  (MLA latent)  dtype
  *                keys are whole rows, values the first head_dim_v entries
  *   block_table  [batch][max_blocks_per_seq]                        int32
  *   context_lens [batch]                                            int32
- *   out          [batch][num_q_heads][head_dim_v]                   dtype
- *   lse          [batch][num_q_heads]                               float32
+ *   out          [batch][q_len][num_q_heads][head_dim_v]            dtype
+ *   lse          [batch][q_len][num_q_heads]                        float32
+ *   (q_len = 1 drops that axis: q [batch][num_q_heads][head_dim] etc.)
  *   dtype PA_F32 = float32, PA_BF16 = bfloat16 (accumulation is float32;
  *   bf16 outputs are rounded to nearest even).
  *
@@ -87,6 +97,7 @@ typedef struct pa_shape {
   int32_t max_context_len;    /* host-side upper bound of context_lens; sizes the grid */
   float scale;                /* score scale, finite and > 0, e.g. 1/sqrt(head_dim) */
   int32_t dtype;              /* pa_dtype of q, caches and out */
+  int32_t q_len;              /* query rows per sequence, 0..16 (0 and 1: one row) */
 } pa_shape;
 
 /* Human-readable name of a status code.  Never NULL. */
@@ -118,8 +129,8 @@ int32_t pa_decode_launches(const pa_shape* shape, int32_t num_splits, int32_t ml
 
 /*
  * Bytes of workspace a call with this shape and split count needs: float32
- * partials o[batch][num_q_heads][S][head_dim_v], float32 lse[batch][num_q_heads][S]
- * and int32 arrival counters [batch][num_q_heads], each 256-byte aligned.  0 when
+ * partials o[R][S][head_dim_v], float32 lse[R][S] and int32 arrival counters
+ * [R], R = batch * q_len * num_q_heads rows, each 256-byte aligned.  0 when
  * S resolves to 1 (the partial kernel then writes out/lse directly).
  * num_splits <= 0 resolves through the heuristic (which may query the device).
  * Returns 0 on an invalid shape.  Host only.
@@ -149,7 +160,10 @@ pa_status pa_workspace_init(const pa_shape* shape, int32_t num_splits, int32_t m
  * pa_decode_launches).  `lse` may be NULL.  `workspace` may be
  * NULL only when S resolves to 1; its counters must be zero (see above).
  * Supported: PA_F32 with head_dim 64 or 128; PA_BF16 with head_dim 64 or 128;
- * head_dim_v == head_dim; block_size 16 or 32.
+ * head_dim_v == head_dim; block_size 16 or 32.  With q_len > 1: PA_BF16,
+ * head_dim 128, block_size 16 and (num_q_heads / num_kv_heads) * q_len <= 16
+ * (each KV tile is then read once for all rows and heads of its group); the
+ * splits are merged by a reduction launch.
  */
 pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
                     const void* v_cache, const int32_t* block_table,
@@ -169,7 +183,8 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
  * DeepSeek V4 note on CSA and HCA: attention over the top 1024 entries plus
  * a 128-entry window, or densely over every entry), and a split may hold at
  * most 2048 tokens (PA_ERR_UNSUPPORTED for an explicit num_splits that needs
- * more; the heuristic never does).
+ * more; the heuristic never does).  Any q_len up to 16; its rows run as
+ * further head groups, each with its own causal end.
  */
 pa_status pa_decode_mla(const pa_shape* shape, const void* q, const void* kv_cache,
                         const int32_t* block_table, const int32_t* context_lens,

@@ -64,9 +64,27 @@ def test_status_strings(lib):
     assert lib.pa_version() >= 100
 
 
-def test_shape_struct_size_matches_header():
-    # 10 int32 fields + one float, no padding
-    assert ctypes.sizeof(PaShape) == 11 * 4
+def test_shape_struct_matches_header(tmp_path):
+    """The ctypes struct has the header's size and field offsets (checked by
+    compiling the header with the host C compiler)."""
+    import shutil
+    import subprocess
+    assert ctypes.sizeof(PaShape) == 12 * 4       # 11 int32 fields + one float, no padding
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    names = [f[0] for f in PaShape._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "pa_decode.h"\n'
+                   'int main(void) {\n  printf("%zu\\n", sizeof(pa_shape));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(pa_shape, {n}));\n' for n in names)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(PaShape)
+    assert got[1:] == [getattr(PaShape, n).offset for n in names]
 
 
 @pytest.mark.parametrize("field,value", [
@@ -75,6 +93,7 @@ def test_shape_struct_size_matches_header():
     ("num_kv_heads", 3),            # 8 % 3 != 0
     ("max_context_len", 8 * 16 + 1),  # longer than the block table allows
     ("scale", math.inf), ("scale", 0.0), ("scale", -0.125), ("scale", math.nan),
+    ("q_len", -1),
 ])
 def test_invalid_shapes(lib, field, value):
     assert decode(lib, shape(**{field: value})) == _lib.PA_ERR_INVALID
@@ -91,9 +110,30 @@ def test_null_shape_and_pointers(lib):
     dict(head_dim=96, head_dim_v=96),                   # no kernel for D = 96
     dict(head_dim=128, head_dim_v=64),                  # Dv != D for MHA
     dict(block_size=8, max_context_len=50),             # no kernel for bs = 8
+    dict(q_len=17),                                     # more query rows than any kernel takes
+    dict(q_len=2, dtype=_lib.PA_F32),                   # several rows: bf16 MFMA kernel only
+    dict(q_len=2, head_dim=64, head_dim_v=64),          # several rows: head_dim 128 only
+    dict(q_len=5, num_kv_heads=2),                      # G = 4 heads x 5 rows: 20 > 16 columns
 ])
 def test_unsupported(lib, kw):
     assert decode(lib, shape(**kw)) == _lib.PA_ERR_UNSUPPORTED
+
+
+def test_several_rows_supported(lib):
+    """Several query rows pass validation (explicit split count, no launch: the
+    workspace check fails first) and the workspace holds a row per (b, j, h)."""
+    for kw in (dict(q_len=2), dict(q_len=16), dict(q_len=4, num_kv_heads=2)):
+        s = shape(**kw)
+        assert decode(lib, s, splits=4) == _lib.PA_ERR_WORKSPACE, kw
+        up = lambda x: -(-x // 256) * 256
+        rows = 2 * kw["q_len"] * 8
+        assert lib.pa_decode_workspace_size(ctypes.byref(s), 4, 0) == \
+            up(rows * 4 * 128 * 4) + up(rows * 4 * 4) + up(rows * 4), kw
+        # q_len = 0 and 1 both mean one row
+    assert lib.pa_decode_workspace_size(ctypes.byref(shape(q_len=0)), 4, 0) == \
+        lib.pa_decode_workspace_size(ctypes.byref(shape(q_len=1)), 4, 0)
+    # several rows never fuse the merge into the partial kernel
+    assert lib.pa_decode_launches(ctypes.byref(shape(q_len=2)), 2, 0) == 2
 
 
 def test_workspace_checks(lib):

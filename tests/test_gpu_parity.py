@@ -142,6 +142,57 @@ def test_small_shapes(name):
 
 
 # ----------------------------------------------------------------------------------------------
+# Several query rows per sequence (the last q_len tokens, causal): every output compared.
+# Contexts shorter than q_len leave early rows with no token (out = 0, lse = -inf).
+# ----------------------------------------------------------------------------------------------
+
+ROWS = {
+    "rows_mha_q4": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=4, num_kv_heads=4,
+                        head_dim=128, block_size=16, context_lens=[3, 37, 300], num_blocks=64,
+                        q_len=4),
+    "rows_mha_q16": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=2, num_kv_heads=2,
+                         head_dim=128, block_size=16, context_lens=[16, 200], num_blocks=30,
+                         q_len=16),
+    "rows_gqa_g4_q4": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=8, num_kv_heads=2,
+                           head_dim=128, block_size=16, context_lens=[2, 17, 333], num_blocks=60,
+                           q_len=4),
+    "rows_gqa_g8_q2": dict(kind="mha", dtype="bf16", batch=4, num_q_heads=16, num_kv_heads=2,
+                           head_dim=128, block_size=16, context_lens=[1, 16, 1000, 47],
+                           num_blocks=90, q_len=2),
+    "rows_gqa_g2_q8": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=6, num_kv_heads=3,
+                           head_dim=128, block_size=16, context_lens=[33, 95], num_blocks=20,
+                           q_len=8),
+    "rows_mla_h128_q2": dict(kind="mla", dtype="bf16", batch=2, num_q_heads=128, num_kv_heads=1,
+                             head_dim=576, head_dim_v=512, block_size=64, context_lens=[65, 300],
+                             num_blocks=12, scale=192 ** -0.5, q_len=2),
+    "rows_mla_h64_q3": dict(kind="mla", dtype="bf16", batch=2, num_q_heads=64, num_kv_heads=1,
+                            head_dim=576, head_dim_v=512, block_size=64, context_lens=[129, 2],
+                            num_blocks=8, scale=192 ** -0.5, q_len=3),
+    "rows_mla_h16_q4": dict(kind="mla", dtype="bf16", batch=2, num_q_heads=16, num_kv_heads=1,
+                            head_dim=576, head_dim_v=512, block_size=64, context_lens=[1, 700],
+                            num_blocks=20, scale=192 ** -0.5, q_len=4),
+    "rows_mla_bs1_h128_q2": dict(kind="mla", dtype="bf16", batch=3, num_q_heads=128,
+                                 num_kv_heads=1, head_dim=576, head_dim_v=512, block_size=1,
+                                 context_lens=[1, 100, 333], num_blocks=600, scale=192 ** -0.5,
+                                 q_len=2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ROWS))
+def test_several_rows(name):
+    inp = make_paged_inputs(name=name, seed=300 + sorted(ROWS).index(name), **ROWS[name])
+    assert inp.q_len == ROWS[name]["q_len"]
+    ref_out, ref_lse = oracle.decode_inputs(inp)
+    t = to_device(inp, "cuda", poison=True)
+    P = -(-inp.max_context_len // inp.block_size)
+    for S in [0, 1, 2, 3, 7, P + 5]:
+        say(f"{name} S={S}")
+        out, lse = run(inp, t, num_splits=S)
+        assert tuple(out.shape) == (inp.batch, inp.q_len, inp.num_q_heads, inp.head_dim_v)
+        compare(inp, out, lse, ref_out, ref_lse, f"{name} S={S}")
+
+
+# ----------------------------------------------------------------------------------------------
 # Full-size workloads in the launch configuration the benchmark times (heuristic split count):
 # sampled (sequence, head) rows against the oracle, every output finite.
 # ----------------------------------------------------------------------------------------------
@@ -156,12 +207,22 @@ def sample_pairs(inp, n, seed):
     return sorted(pairs)
 
 
+def sample_rows(inp, n, seed):
+    """(b, j, h) triples for workloads with several query rows."""
+    rng = np.random.default_rng(seed)
+    out = {(b, int(rng.integers(inp.q_len)), h) for b, h in sample_pairs(inp, n, seed)}
+    b_long = int(np.argmax(inp.context_lens))
+    out |= {(b_long, 0, 0), (b_long, inp.q_len - 1, inp.num_q_heads - 1)}
+    return sorted(out)
+
+
 @pytest.mark.parametrize("name", ["llama_mha_bf16", "long_gqa_bf16", "ragged_gqa_bf16", "mla_bf16",
-                                  "mla_topk_bf16", "mla_allentries_bf16"])
+                                  "mla_topk_bf16", "mla_allentries_bf16", "llama_mha_q4_bf16",
+                                  "long_gqa_q4_bf16", "mla_q2_bf16"])
 def test_full_size_sampled(name):
     say(f"full {name}: drawing inputs")
     inp = make_config(name)
-    pairs = sample_pairs(inp, 24, 7)
+    pairs = sample_pairs(inp, 24, 7) if inp.q_len == 1 else sample_rows(inp, 24, 7)
     ref_out, ref_lse = oracle.decode_inputs(inp, heads=pairs)
     t = to_device(inp, "cuda", poison=True)
     say(f"full {name}: running")

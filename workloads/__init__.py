@@ -99,11 +99,16 @@ class PagedDecodeInputs:
     context_lens: np.ndarray  # int32 [B]
     block_table: np.ndarray   # int32 [B][max_blocks_per_seq], physical ids
     page_ids: np.ndarray      # int32 [n_used]: physical id of compact row i
-    q: np.ndarray             # [B][Hq][Dqk] float32 or uint16 bf16 bits
+    q: np.ndarray             # [B][Hq][Dqk] (or [B][q_len][Hq][Dqk]) float32 or uint16 bf16 bits
     k_pages: np.ndarray | None = None   # [n_used][Hkv][bs][D]
     v_pages: np.ndarray | None = None   # [n_used][Hkv][D][bs]
     c_pages: np.ndarray | None = None   # [n_used][bs][Dqk] (MLA latent)
     meta: dict = field(default_factory=dict)
+
+    @property
+    def q_len(self) -> int:
+        """Query rows per sequence (the last q_len tokens, causal)."""
+        return int(self.q.shape[1]) if self.q.ndim == 4 else 1
 
     @property
     def max_blocks_per_seq(self) -> int:
@@ -161,7 +166,7 @@ def make_paged_inputs(*, name: str = "custom", kind: str = "mha", dtype: str = "
                       context_lens, num_blocks: int | None = None,
                       max_blocks_per_seq: int | None = None, scale: float | None = None,
                       seed: int = 0, poison: bool = True, values: bool = True,
-                      meta: dict | None = None) -> PagedDecodeInputs:
+                      meta: dict | None = None, q_len: int = 1) -> PagedDecodeInputs:
     """Draw a paged decode workload.
 
     ``context_lens`` is an int sequence (or a callable ``rng -> array`` drawn
@@ -169,7 +174,9 @@ def make_paged_inputs(*, name: str = "custom", kind: str = "mha", dtype: str = "
     permutation of a pool of ``num_blocks`` pages.  With ``poison`` the slots
     past each context's end in its last page are NaN; the device pool's
     unassigned pages are to be NaN-filled by the caller as well.  With
-    ``values=False`` only the shapes, lengths and tables are drawn.
+    ``values=False`` only the shapes, lengths and tables are drawn.  With
+    ``q_len`` > 1, q is [B][q_len][Hq][Dqk]: the sequences' last q_len tokens
+    as query rows.
     """
     if kind not in ("mha", "mla"):
         raise ValueError(kind)
@@ -198,7 +205,11 @@ def make_paged_inputs(*, name: str = "custom", kind: str = "mha", dtype: str = "
         scale = 1.0 / math.sqrt(head_dim)
 
     dq = head_dim
-    q = _Draw(q_seq).normal(batch * num_q_heads * dq, dtype).reshape(batch, num_q_heads, dq)
+    if q_len > 1:
+        q = _Draw(q_seq).normal(batch * q_len * num_q_heads * dq, dtype).reshape(
+            batch, q_len, num_q_heads, dq)
+    else:
+        q = _Draw(q_seq).normal(batch * num_q_heads * dq, dtype).reshape(batch, num_q_heads, dq)
     inp = PagedDecodeInputs(name=name, kind=kind, dtype=dtype, batch=batch,
                             num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                             head_dim=head_dim, head_dim_v=head_dim_v, block_size=block_size,
@@ -291,10 +302,32 @@ CONFIGS = {
         scale=1.0 / math.sqrt(192), seed=7,
         meta=dict(desc="MLA latent bf16 over token-index lists: B32, 128 heads, 8192 entries "
                        "per sequence (every entry), bs1, 262144-row pool")),
+    # Several query rows per sequence (the last q_len tokens, causal): draft
+    # verification / chunked prefill over the same caches as the decode
+    # workloads above (same seeds for lengths and pages, own query rows).
+    "llama_mha_q4_bf16": dict(
+        kind="mha", dtype="bf16", batch=16, num_q_heads=32, num_kv_heads=32, head_dim=128,
+        block_size=16, context_lens=_uniform_ctx(1024, 4096, 16), num_blocks=65536,
+        max_blocks_per_seq=256, scale=1.0 / math.sqrt(128), seed=2, q_len=4,
+        meta=dict(desc="Llama-style MHA bf16, 4 query rows per sequence (causal): B16, 32 heads, "
+                       "D128, ctx U[1024,4096], bs16")),
+    "long_gqa_q4_bf16": dict(
+        kind="mha", dtype="bf16", batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        block_size=16, context_lens=[131072], num_blocks=8192, scale=1.0 / math.sqrt(128), seed=3,
+        q_len=4,
+        meta=dict(desc="long-context GQA bf16, 4 query rows (causal): B1, 32 q / 8 kv heads, "
+                       "D128, ctx 131072, bs16")),
+    "mla_q2_bf16": dict(
+        kind="mla", dtype="bf16", batch=32, num_q_heads=128, num_kv_heads=1, head_dim=576,
+        head_dim_v=512, block_size=64, context_lens=[8192] * 32, num_blocks=4096,
+        scale=1.0 / math.sqrt(192), seed=5, q_len=2,
+        meta=dict(desc="MLA latent bf16, 2 query rows per sequence (causal): B32, 128 heads, "
+                       "latent 576, ctx 8192, bs64")),
 }
 
 CONFIG_ORDER = ["tiny_mha_f32", "llama_mha_bf16", "long_gqa_bf16", "ragged_gqa_bf16", "mla_bf16",
-                "mla_topk_bf16", "mla_allentries_bf16"]
+                "mla_topk_bf16", "mla_allentries_bf16", "llama_mha_q4_bf16", "long_gqa_q4_bf16",
+                "mla_q2_bf16"]
 
 
 def make_config(name: str, *, poison: bool = True, values: bool = True, seed: int | None = None,
