@@ -17,6 +17,7 @@ from .decode_ref import (  # noqa: F401
     bf16_bits_to_f64,
     chunk_partial,
     decode_inputs,
+    fp8_e4m3_bits_to_f64,
     gather_kv,
     gather_latent,
     kv_head_of,

@@ -40,6 +40,11 @@ scaled scores; GQA head h reads KV head h // (Hq/Hkv); an empty context gives
 out = 0 and lse = -inf; slots past the context and table entries past the
 last page are never read.  bf16 inputs are widened bit-exactly (bits << 16).
 
+An FP8 KV cache (the "llms-attention" post names FP8 only as hardware low
+precision FlashAttention-3 uses) is read as OCP E4M3 codes with one scale per
+tensor: a key is k_scale times its code's value, a value v_scale times its
+code's value; queries and outputs keep their own dtype.
+
 Pool layouts (the library's documented layouts):
     k_pool [num_blocks][Hkv][bs][D]
     v_pool [num_blocks][Hkv][Dv][bs]
@@ -61,9 +66,23 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
+def fp8_e4m3_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen FP8 E4M3 codes (OCP layout) exactly: 1 sign, 4 exponent (bias 7)
+    and 3 mantissa bits; exponent 0 is subnormal (m * 2^-9); S.1111.111 is
+    NaN; there is no infinity."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign, e, m = b >> 7, (b >> 3) & 15, b & 7
+    # normal: (1 + m/8) 2^(e-7) = (8 + m) 2^(e-10)
+    mag = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.exp2(e - 10.0))
+    v = np.where(sign == 1, -mag, mag)
+    return np.where((e == 15) & (m == 7), np.nan, v)
+
+
 def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return bf16_bits_to_f64(x)
+    if dtype == "fp8":
+        return fp8_e4m3_bits_to_f64(x)
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
     if dtype == "f64":
@@ -202,13 +221,16 @@ def _check_common(q, block_table, context_lens, bs):
 
 
 def paged_decode(q, k_pool, v_pool, block_table, context_lens, scale, dtype="bf16",
-                 heads=None):
+                 heads=None, kv_dtype=None, k_scale=1.0, v_scale=1.0):
     """Reference decode attention over paged K/V (MHA and GQA).
 
     Returns (out [B][Hq][Dv], lse [B][Hq]) in float64.  ``heads`` optionally
     restricts the work to a list of (b, h) pairs (others stay NaN), which lets
-    a test sample outputs of a large batch one by one.
+    a test sample outputs of a large batch one by one.  ``kv_dtype`` is the
+    caches' dtype when it differs from the query's ("fp8": E4M3 codes, read
+    as k_scale / v_scale times their values).
     """
+    kvd = dtype if kv_dtype is None else kv_dtype
     qf = as_f64(q, dtype)
     B, Hq, _ = qf.shape
     nb, Hkv, bs, _ = k_pool.shape
@@ -227,8 +249,8 @@ def paged_decode(q, k_pool, v_pool, block_table, context_lens, scale, dtype="bf1
             continue
         pages, slots = token_locations(block_table[b], int(ctx[b]), bs)
         k, v = gather_kv(k_pool, v_pool, pages, slots)
-        k = as_f64(k, dtype)
-        v = as_f64(v, dtype)
+        k = as_f64(k, kvd) * k_scale
+        v = as_f64(v, kvd) * v_scale
         for h in (range(Hq) if want is None else want[b]):
             g = kv_head_of(h, Hq, Hkv)
             out[b, h], lse[b, h] = attend(qf[b, h], k[:, g, :], v[:, g, :], scale)
@@ -329,7 +351,7 @@ def _rows_by_j(rows, q_len):
 
 
 def paged_decode_rows(q, k_pool, v_pool, block_table, context_lens, scale, dtype="bf16",
-                      rows=None):
+                      rows=None, kv_dtype=None, k_scale=1.0, v_scale=1.0):
     """Reference attention of q_len query rows per sequence over paged K/V.
 
     q [B][q_len][Hq][D]; returns (out [B][q_len][Hq][Dv], lse [B][q_len][Hq]).
@@ -347,7 +369,8 @@ def paged_decode_rows(q, k_pool, v_pool, block_table, context_lens, scale, dtype
     for j, heads in _rows_by_j(rows, L).items():
         ctx_j = np.array([row_context(c, L, j) for c in ctx], dtype=np.int64)
         out[:, j], lse[:, j] = paged_decode(np.ascontiguousarray(q[:, j]), k_pool, v_pool,
-                                            block_table, ctx_j, scale, dtype=dtype, heads=heads)
+                                            block_table, ctx_j, scale, dtype=dtype, heads=heads,
+                                            kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale)
     return out, lse
 
 
@@ -378,12 +401,20 @@ def decode_inputs(inp, heads=None):
             return paged_decode_mla_rows(inp.q, inp.c_pages, bt, inp.context_lens, inp.scale,
                                          dv=inp.head_dim_v, dtype=inp.dtype, rows=heads)
         return paged_decode_rows(inp.q, inp.k_pages, inp.v_pages, bt, inp.context_lens,
-                                 inp.scale, dtype=inp.dtype, rows=heads)
+                                 inp.scale, dtype=inp.dtype, rows=heads, **_kv_args(inp))
     if inp.kind == "mla":
         return paged_decode_mla(inp.q, inp.c_pages, bt, inp.context_lens, inp.scale,
                                 dv=inp.head_dim_v, dtype=inp.dtype, heads=heads)
     return paged_decode(inp.q, inp.k_pages, inp.v_pages, bt, inp.context_lens, inp.scale,
-                        dtype=inp.dtype, heads=heads)
+                        dtype=inp.dtype, heads=heads, **_kv_args(inp))
+
+
+def _kv_args(inp):
+    """Cache dtype and scales of a workload (none for caches in the query dtype)."""
+    kvd = getattr(inp, "kv_dtype", None)
+    if kvd is None or kvd == inp.dtype:
+        return {}
+    return dict(kv_dtype=kvd, k_scale=inp.k_scale, v_scale=inp.v_scale)
 
 
 # ---------------------------------------------------------------------------

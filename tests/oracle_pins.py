@@ -587,6 +587,61 @@ def pin_mla_rows_bruteforce(o):
         _close(lse, ref_l, what=f"mla rows lse bs{bs}")
 
 
+# --------------------------------------------------------------------------
+# FP8 (E4M3) KV caches with one scale per tensor
+# --------------------------------------------------------------------------
+
+def pin_fp8_widening(o):
+    """E4M3 codes widen to the values the format defines: known codes, and all
+    256 codes against torch's float8_e4m3fn conversion."""
+    import torch
+    known = {0x00: 0.0, 0x80: -0.0, 0x38: 1.0, 0xB8: -1.0, 0x40: 2.0, 0x30: 0.5, 0x3C: 1.5,
+             0x7E: 448.0, 0xFE: -448.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6,
+             0x0F: 1.875 * 2.0 ** -6, 0x77: 240.0}
+    codes = np.array(sorted(known), dtype=np.uint8)
+    got = o.as_f64(codes, "fp8")
+    for c, g in zip(codes.tolist(), got.tolist()):
+        w = known[c]
+        assert g == w and math.copysign(1, g) == math.copysign(1, w), (hex(c), g, w)
+    for c in (0x7F, 0xFF):
+        assert np.isnan(o.as_f64(np.array([c], dtype=np.uint8), "fp8")).all()
+    allc = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(allc).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = o.as_f64(allc, "fp8")
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin]) and np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+
+
+def _fp8_codes(rng, shape):
+    """Random E4M3 codes, NaN codes excluded."""
+    c = rng.integers(0, 256, size=shape).astype(np.uint8)
+    return np.where((c & 0x7F) == 0x7F, np.uint8(0x3A), c)
+
+
+def pin_fp8_decode(o):
+    """Decode over FP8 caches equals the brute force on the dequantized values
+    (codes widened by torch, times their tensor's scale), one and several rows."""
+    import torch
+    widen = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for seed, L in ((60, 1), (61, 3)):
+        _, k, v, bt, ctx, scale = tiny_paged(seed, 2, 4, 2, 8, 8, 4, [9, 5])
+        rng = np.random.default_rng(seed)
+        kc, vc = _fp8_codes(rng, k.shape), _fp8_codes(rng, v.shape)
+        ks, vs = 0.037, 1.9
+        q = rng.standard_normal((2, L, 4, 8))
+        out, lse = o.paged_decode_rows(q, kc, vc, bt, ctx, scale, dtype="f64", kv_dtype="fp8",
+                                       k_scale=ks, v_scale=vs)
+        ref_o, ref_l = brute_force_rows(q, widen(kc) * ks, widen(vc) * vs, bt, ctx, scale)
+        _close(out, ref_o, what=f"fp8 rows out L{L}")
+        _close(lse, ref_l, what=f"fp8 rows lse L{L}")
+        if L == 1:
+            o1, l1 = o.paged_decode(np.ascontiguousarray(q[:, 0]), kc, vc, bt, ctx, scale,
+                                    dtype="f64", kv_dtype="fp8", k_scale=ks, v_scale=vs)
+            _close(o1, ref_o[:, 0], what="fp8 out")
+            _close(l1, ref_l[:, 0], what="fp8 lse")
+
+
 ALL_PINS = [
     pin_bruteforce, pin_mla_bruteforce, pin_mla_token_index_list, pin_bf16_widening, pin_sdpa,
     pin_ctx_one,
@@ -595,5 +650,5 @@ ALL_PINS = [
     pin_gqa_equals_mha, pin_mla_equals_mqa, pin_batch_independence, pin_sampled_heads,
     pin_append_then_decode, pin_append_out_of_range, pin_append_latent,
     pin_rows_bruteforce, pin_rows_sdpa, pin_rows_single_is_decode, pin_rows_causality,
-    pin_mla_rows_bruteforce,
+    pin_mla_rows_bruteforce, pin_fp8_widening, pin_fp8_decode,
 ]

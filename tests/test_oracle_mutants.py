@@ -222,6 +222,37 @@ def _row_context_one_past(ctx, q_len, j):
     return min(int(ctx), max(0, int(ctx) - q_len + 2 + j))
 
 
+def _fp8_bias8(bits):
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    s, e, m = b >> 7, (b >> 3) & 15, b & 7
+    mag = np.where(e == 0, m * 2.0 ** -10, (8 + m) * np.exp2(e - 11.0))
+    v = np.where(s == 1, -mag, mag)
+    return np.where((e == 15) & (m == 7), np.nan, v)
+
+
+def _fp8_no_subnormals(bits):
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    s, e, m = b >> 7, (b >> 3) & 15, b & 7
+    mag = (8 + m) * np.exp2(e - 10.0)
+    v = np.where(s == 1, -mag, mag)
+    return np.where((e == 15) & (m == 7), np.nan, v)
+
+
+def _fp8_unsigned(bits):
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    e, m = (b >> 3) & 15, b & 7
+    v = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.exp2(e - 10.0))
+    return np.where((e == 15) & (m == 7), np.nan, v)
+
+
+def _decode_scales_swapped(*a, k_scale=1.0, v_scale=1.0, **kw):
+    return ref._orig_paged_decode(*a, k_scale=v_scale, v_scale=k_scale, **kw)
+
+
+def _decode_v_unscaled(*a, k_scale=1.0, v_scale=1.0, **kw):
+    return ref._orig_paged_decode(*a, k_scale=k_scale, v_scale=1.0, **kw)
+
+
 MUTANTS = {
     "scores_noscale": ("scores", _scores_noscale),
     "scores_negated": ("scores", _scores_negated),
@@ -254,6 +285,11 @@ MUTANTS = {
     "rows_unmasked": ("row_context", _row_context_no_mask),
     "rows_reversed": ("row_context", _row_context_reversed),
     "rows_see_one_ahead": ("row_context", _row_context_one_past),
+    "fp8_exponent_bias_8": ("fp8_e4m3_bits_to_f64", _fp8_bias8),
+    "fp8_no_subnormals": ("fp8_e4m3_bits_to_f64", _fp8_no_subnormals),
+    "fp8_sign_dropped": ("fp8_e4m3_bits_to_f64", _fp8_unsigned),
+    "fp8_scales_swapped": ("paged_decode", _decode_scales_swapped),
+    "fp8_v_scale_dropped": ("paged_decode", _decode_v_unscaled),
 }
 
 
@@ -263,6 +299,7 @@ def test_mutant_is_caught(name, monkeypatch):
     monkeypatch.setitem(ref.__dict__, "_orig_attend", ref.attend)
     monkeypatch.setitem(ref.__dict__, "_orig_gather_kv", ref.gather_kv)
     monkeypatch.setitem(ref.__dict__, "_orig_append_kv", ref.append_kv)
+    monkeypatch.setitem(ref.__dict__, "_orig_paged_decode", ref.paged_decode)
     monkeypatch.setattr(ref, attr, fn)
     caught = []
     for pin in ALL_PINS:
