@@ -113,7 +113,8 @@ class Case:
             head_dim=inp.head_dim, head_dim_v=inp.head_dim_v, block_size=inp.block_size,
             max_blocks_per_seq=inp.max_blocks_per_seq, num_blocks=inp.num_blocks,
             max_context_len=inp.max_context_len, scale=inp.scale, dtype=torch_dtype(inp.dtype),
-            q_len=inp.q_len)
+            q_len=inp.q_len, kv_dtype=torch_dtype(inp.kv_dtype) if inp.kv_dtype else 0,
+            k_scale=inp.k_scale, v_scale=inp.v_scale)
         self.S = pa.choose_num_splits(self.shape, 0, self.mla)
         nbytes = pa.workspace_size(self.shape, self.S, self.mla)
         # zero-filled: the fused reduction's arrival counters start at 0

@@ -30,6 +30,8 @@ __all__ = [
 ]
 
 _DTYPES = {torch.float32: _lib.PA_F32, torch.bfloat16: _lib.PA_BF16}
+# cache dtypes: the query's, or FP8 E4M3 codes (with bf16 queries and per-tensor scales)
+_FP8 = getattr(torch, "float8_e4m3fn", None)
 
 
 def library_path() -> str:
@@ -66,11 +68,25 @@ def _need(t, name, dtype=None, ndim=None, device=None):
 
 
 def make_shape(*, batch, num_q_heads, num_kv_heads, head_dim, head_dim_v, block_size,
-               max_blocks_per_seq, num_blocks, max_context_len, scale, dtype, q_len=1) -> PaShape:
+               max_blocks_per_seq, num_blocks, max_context_len, scale, dtype, q_len=1,
+               kv_dtype=0, k_scale=1.0, v_scale=1.0) -> PaShape:
     code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    if isinstance(kv_dtype, torch.dtype):
+        kv_dtype = _lib.PA_FP8_E4M3 if kv_dtype == _FP8 else _DTYPES[kv_dtype]
     return PaShape(batch, num_q_heads, num_kv_heads, head_dim, head_dim_v, block_size,
                    max_blocks_per_seq, num_blocks, int(max_context_len), float(scale), code,
-                   int(q_len))
+                   int(q_len), int(kv_dtype), float(k_scale), float(v_scale))
+
+
+def _kv_dtype(cache, q_dtype, k_scale, v_scale):
+    """(kv_dtype code, k_scale, v_scale) for a cache tensor."""
+    if _FP8 is not None and cache.dtype == _FP8:
+        if k_scale is None or v_scale is None:
+            raise ValueError("FP8 caches need k_scale and v_scale")
+        return _lib.PA_FP8_E4M3, float(k_scale), float(v_scale)
+    if cache.dtype != q_dtype:
+        raise ValueError(f"cache dtype {cache.dtype} differs from the query's {q_dtype}")
+    return 0, 1.0, 1.0
 
 
 def _q_dims(q):
@@ -83,13 +99,15 @@ def _q_dims(q):
     raise ValueError("q must be [B][Hq][D] or [B][q_len][Hq][D]")
 
 
-def _mha_shape(q, k_cache, v_cache, block_table, context_lens, max_context_len, scale):
+def _mha_shape(q, k_cache, v_cache, block_table, context_lens, max_context_len, scale,
+               k_scale=None, v_scale=None):
     _need(q, "q")
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
     dev = q.device
-    _need(k_cache, "k_cache", q.dtype, 4, dev)
-    _need(v_cache, "v_cache", q.dtype, 4, dev)
+    _need(k_cache, "k_cache", None, 4, dev)
+    _need(v_cache, "v_cache", k_cache.dtype, 4, dev)
+    kvd, ks, vs = _kv_dtype(k_cache, q.dtype, k_scale, v_scale)
     _need(block_table, "block_table", torch.int32, 2, dev)
     _need(context_lens, "context_lens", torch.int32, 1, dev)
     B, L, Hq, D = _q_dims(q)
@@ -107,7 +125,8 @@ def _mha_shape(q, k_cache, v_cache, block_table, context_lens, max_context_len, 
     return make_shape(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
                       head_dim_v=v_cache.shape[2], block_size=bs,
                       max_blocks_per_seq=block_table.shape[1], num_blocks=nb,
-                      max_context_len=max_context_len, scale=scale, dtype=q.dtype, q_len=L)
+                      max_context_len=max_context_len, scale=scale, dtype=q.dtype, q_len=L,
+                      kv_dtype=kvd, k_scale=ks, v_scale=vs)
 
 
 def _mla_shape(q, kv_cache, block_table, context_lens, max_context_len, scale, head_dim_v):
@@ -171,12 +190,16 @@ def _outputs(shape, q, out, lse, workspace, num_splits, mla):
 
 
 def decode(q, k_cache, v_cache, block_table, context_lens, *, max_context_len=None, scale=None,
-           num_splits=0, out=None, lse=None, workspace=None, stream=None):
+           num_splits=0, out=None, lse=None, workspace=None, stream=None, k_scale=None,
+           v_scale=None):
     """Decode attention over a paged K/V cache (MHA/GQA).  Returns (out, lse).
 
     num_splits <= 0 lets the library choose.  Pass lse=False to skip it.
+    FP8 caches (torch.float8_e4m3fn, bf16 q) need k_scale and v_scale: a key
+    is k_scale times its code's value, a value v_scale times its code's.
     """
-    shape = _mha_shape(q, k_cache, v_cache, block_table, context_lens, max_context_len, scale)
+    shape = _mha_shape(q, k_cache, v_cache, block_table, context_lens, max_context_len, scale,
+                       k_scale, v_scale)
     out, lse, ws = _outputs(shape, q, out, lse, workspace, num_splits, False)
     st = _lib.load().pa_decode(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                _ptr(block_table), _ptr(context_lens), int(num_splits), _ptr(out),
@@ -239,12 +262,14 @@ def reduce(shape: PaShape, context_lens, num_splits, workspace, out, lse, mla=Fa
 def append_kv(k_new, v_new, k_cache, v_cache, block_table, context_lens, stream=None):
     """Write one new token per sequence into the paged K/V cache.
 
-    k_new [B][Hkv][D], v_new [B][Hkv][Dv]; the token goes to position
+    k_new [B][Hkv][D], v_new [B][Hkv][Dv] (in the caches' dtype: FP8 codes for
+    FP8 caches, quantised by the caller); the token goes to position
     context_lens[b] (the length before the append).  context_lens is not
     changed: the caller increments it before decoding the new token.
     """
     _need(k_new, "k_new", ndim=3)
-    if k_new.dtype not in _DTYPES:
+    fp8 = _FP8 is not None and k_new.dtype == _FP8
+    if k_new.dtype not in _DTYPES and not fp8:
         raise ValueError(f"unsupported dtype {k_new.dtype}")
     dev = k_new.device
     _need(v_new, "v_new", k_new.dtype, 3, dev)
@@ -261,9 +286,12 @@ def append_kv(k_new, v_new, k_cache, v_cache, block_table, context_lens, stream=
         raise ValueError("v_cache must be [num_blocks][Hkv][Dv][bs]")
     if block_table.shape[0] != B or context_lens.shape[0] != B:
         raise ValueError("block_table / context_lens batch differs from k_new")
+    # FP8 rows are moved as codes (a bf16 shape with FP8 caches: one byte per element)
     shape = make_shape(batch=B, num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=D, head_dim_v=Dv,
                        block_size=bs, max_blocks_per_seq=block_table.shape[1], num_blocks=nb,
-                       max_context_len=0, scale=1.0, dtype=k_new.dtype)
+                       max_context_len=0, scale=1.0,
+                       dtype=torch.bfloat16 if fp8 else k_new.dtype,
+                       kv_dtype=_lib.PA_FP8_E4M3 if fp8 else 0)
     st = _lib.load().pa_append_kv(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                                   _ptr(v_cache), _ptr(block_table), _ptr(context_lens),
                                   _stream(stream))

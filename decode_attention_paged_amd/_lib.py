@@ -15,6 +15,7 @@ PA_ERR_HIP = 4
 
 PA_F32 = 0
 PA_BF16 = 1
+PA_FP8_E4M3 = 2
 
 
 class PaShape(ctypes.Structure):
@@ -31,6 +32,9 @@ class PaShape(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
         ("q_len", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 

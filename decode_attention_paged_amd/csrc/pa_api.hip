@@ -20,6 +20,9 @@ constexpr int kMaxQLen = 16;                         // query rows per sequence
 // Query rows per sequence (0 and 1 both mean one row).
 int rows_of(const pa_shape& s) { return s.q_len > 1 ? s.q_len : 1; }
 
+// Whether the caches hold FP8 E4M3 codes (kv_dtype 0 means the query dtype).
+bool fp8_kv(const pa_shape& s) { return s.kv_dtype == PA_FP8_E4M3; }
+
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 enum class Kernel { None, MhaValu, GqaMfma, MlaMfma };
@@ -28,6 +31,7 @@ enum class Kernel { None, MhaValu, GqaMfma, MlaMfma };
 Kernel pick_kernel(const pa_shape& s, bool mla) {
   const bool bf16 = s.dtype == PA_BF16;
   if (mla) {
+    if (fp8_kv(s)) return Kernel::None;
     return pa::mla_mfma_supported(bf16, s.head_dim, s.head_dim_v, s.block_size, s.num_q_heads)
                ? Kernel::MlaMfma
                : Kernel::None;
@@ -35,6 +39,12 @@ Kernel pick_kernel(const pa_shape& s, bool mla) {
   if (s.head_dim_v != s.head_dim) return Kernel::None;
   const int G = s.num_q_heads / s.num_kv_heads;
   const int ql = rows_of(s);
+  if (fp8_kv(s)) {
+    if (!bf16) return Kernel::None;
+    if (pa::gqa_mfma_fp8_supported(s.head_dim, s.block_size, G, ql)) return Kernel::GqaMfma;
+    if (ql == 1 && pa::mha_valu_fp8_supported(s.head_dim, s.block_size)) return Kernel::MhaValu;
+    return Kernel::None;
+  }
   if (pa::gqa_mfma_supported(bf16, s.head_dim, s.head_dim_v, s.block_size, G, ql))
     return Kernel::GqaMfma;
   if (ql == 1 && pa::mha_valu_supported(bf16, s.head_dim, s.block_size)) return Kernel::MhaValu;
@@ -51,6 +61,11 @@ pa_status check_shape(const pa_shape* s, bool mla) {
     return PA_ERR_INVALID;
   if (s->num_q_heads % s->num_kv_heads != 0) return PA_ERR_INVALID;
   if (s->q_len < 0) return PA_ERR_INVALID;
+  if (s->kv_dtype != 0 && s->kv_dtype != s->dtype && s->kv_dtype != PA_FP8_E4M3)
+    return PA_ERR_INVALID;
+  if (fp8_kv(*s) && (!std::isfinite(s->k_scale) || !(s->k_scale > 0.f) ||
+                     !std::isfinite(s->v_scale) || !(s->v_scale > 0.f)))
+    return PA_ERR_INVALID;
   if (s->q_len > kMaxQLen) return PA_ERR_UNSUPPORTED;
   if ((int64_t)s->max_context_len > (int64_t)s->max_blocks_per_seq * s->block_size)
     return PA_ERR_INVALID;
@@ -99,7 +114,7 @@ int heuristic_splits(const pa_shape& s, int cus, bool mla) {
   if (P <= 1) return 1;
   if (cus <= 0) cus = 256;
   const Kernel k = pick_kernel(s, mla);
-  const int esz = s.dtype == PA_BF16 ? 2 : 4;
+  const int esz = fp8_kv(s) ? 1 : (s.dtype == PA_BF16 ? 2 : 4);   // bytes per cache element
   long S;
   if (k == Kernel::MlaMfma) {
     // one workgroup per (head group, sequence, split): fill the CUs once
@@ -190,7 +205,8 @@ pa::Params make_params(const pa_shape& s, int S, const void* q, const void* k, c
   p.S = S;
   const int P = max_pages(s);
   p.c = P > 0 ? (P + S - 1) / S : 1;
-  p.scale_log2 = s.scale * 1.4426950408889634f;
+  p.scale_log2 = s.scale * 1.4426950408889634f * (fp8_kv(s) ? s.k_scale : 1.f);
+  p.v_scale = fp8_kv(s) ? s.v_scale : 1.f;
   p.final_write = S == 1 ? 1 : 0;
   if (S > 1) {
     p.o_part = static_cast<float*>(ws);
@@ -246,8 +262,8 @@ pa_status run_partial(const pa_shape* shape, const void* q, const void* k, const
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (kern) {
-    case Kernel::MhaValu: e = pa::launch_mha_valu(p, shape->dtype == PA_BF16, hs); break;
-    case Kernel::GqaMfma: e = pa::launch_gqa_mfma(p, hs); break;
+    case Kernel::MhaValu: e = pa::launch_mha_valu(p, shape->dtype == PA_BF16, fp8_kv(*shape), hs); break;
+    case Kernel::GqaMfma: e = pa::launch_gqa_mfma(p, fp8_kv(*shape), hs); break;
     case Kernel::MlaMfma: e = pa::launch_mla_mfma(p, hs); break;
     default: return PA_ERR_UNSUPPORTED;
   }
@@ -395,8 +411,16 @@ static pa_status check_append_shape(const pa_shape* s, bool mla) {
     return PA_ERR_INVALID;
   if (s->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;   // grid x limit
   if (s->dtype != PA_F32 && s->dtype != PA_BF16) return PA_ERR_INVALID;
+  if (s->kv_dtype != 0 && s->kv_dtype != s->dtype && s->kv_dtype != PA_FP8_E4M3)
+    return PA_ERR_INVALID;
   if (mla && s->num_kv_heads != 1) return PA_ERR_INVALID;
   return PA_OK;
+}
+
+// Bytes per cache element of an append (the cache dtype).
+static int cache_esize(const pa_shape& s) {
+  if (s.kv_dtype == PA_FP8_E4M3) return 1;
+  return s.dtype == PA_BF16 ? 2 : 4;
 }
 
 pa_status pa_append_kv(const pa_shape* shape, const void* k_new, const void* v_new, void* k_cache,
@@ -410,8 +434,7 @@ pa_status pa_append_kv(const pa_shape* shape, const void* k_new, const void* v_n
   pa::AppendParams a{k_new, v_new, k_cache, v_cache, block_table, context_lens,
                      s.batch, s.num_kv_heads, s.head_dim, s.head_dim_v, s.block_size,
                      s.max_blocks_per_seq, s.num_blocks};
-  const hipError_t e =
-      pa::launch_append(a, s.dtype == PA_BF16, false, static_cast<hipStream_t>(stream));
+  const hipError_t e = pa::launch_append(a, cache_esize(s), false, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -425,8 +448,7 @@ pa_status pa_append_latent(const pa_shape* shape, const void* c_new, void* kv_ca
   pa::AppendParams a{c_new, nullptr, kv_cache, nullptr, block_table, context_lens,
                      s.batch, 1, s.head_dim, 0, s.block_size, s.max_blocks_per_seq,
                      s.num_blocks};
-  const hipError_t e =
-      pa::launch_append(a, s.dtype == PA_BF16, true, static_cast<hipStream_t>(stream));
+  const hipError_t e = pa::launch_append(a, cache_esize(s), true, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

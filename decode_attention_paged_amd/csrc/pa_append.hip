@@ -47,21 +47,24 @@ __global__ __launch_bounds__(256) void append_latent_kernel(AppendParams a) {
   for (int d = threadIdx.x; d < a.D; d += blockDim.x) cc[d] = cn[d];
 }
 
+template <typename T>
+hipError_t launch_typed(const AppendParams& a, bool mla, hipStream_t st) {
+  if (mla)
+    hipLaunchKernelGGL(append_latent_kernel<T>, dim3(a.B), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(append_kv_kernel<T>, dim3(a.Hkv, a.B), dim3(128), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_append(const AppendParams& a, bool bf16, bool mla, hipStream_t st) {
-  if (mla) {
-    if (bf16)
-      hipLaunchKernelGGL(append_latent_kernel<uint16_t>, dim3(a.B), dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL(append_latent_kernel<uint32_t>, dim3(a.B), dim3(256), 0, st, a);
-  } else {
-    if (bf16)
-      hipLaunchKernelGGL(append_kv_kernel<uint16_t>, dim3(a.Hkv, a.B), dim3(128), 0, st, a);
-    else
-      hipLaunchKernelGGL(append_kv_kernel<uint32_t>, dim3(a.Hkv, a.B), dim3(128), 0, st, a);
+hipError_t launch_append(const AppendParams& a, int esize, bool mla, hipStream_t st) {
+  switch (esize) {
+    case 1: return launch_typed<uint8_t>(a, mla, st);    // FP8 codes
+    case 2: return launch_typed<uint16_t>(a, mla, st);   // bfloat16
+    case 4: return launch_typed<uint32_t>(a, mla, st);   // float32
+    default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace pa

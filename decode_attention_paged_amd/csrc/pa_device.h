@@ -9,6 +9,7 @@ namespace pa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -32,6 +33,22 @@ __device__ __forceinline__ u32x4 ld128(const void* p) {
 // ~13% more read bandwidth from HBM on MI355X than the default policy.
 __device__ __forceinline__ u32x4 ld128_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+// 64-bit streaming load (8-byte aligned pointer), same policy.
+__device__ __forceinline__ u32x2 ld64_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+
+// Two FP8 E4M3 codes (bytes 0-1 of w, or 2-3 with HI) as a bfloat16 pair:
+// exact, every E4M3 value is a bfloat16 value.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+// Eight FP8 codes (two words) as eight bfloat16 values, in order.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  return u32x4{fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
+               fp8x2_to_bf16x2<true>(w1)};
 }
 
 // Reinterpret a 32-bit lane value as float.  Takes the value (not a vector

@@ -23,6 +23,8 @@
 //   dim, i.e. the A operand of O^T = V^T P^T as stored.
 //   Both outputs put head n in lane column n, so the running max, the
 //   rescale factor and the accumulator of a head live in the same lanes.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 #include "pa_merge.h"
@@ -40,6 +42,45 @@ struct PairTile {
   u32x4 k[2][4];   // [chain][k-step]
   u32x4 v[8];      // [dim block]
 };
+
+// The same pair of pages with FP8 E4M3 caches (rows of 128 bytes), as
+// loaded.  The contraction order over dims is free as long as K and Q use
+// the same one, so a lane loads 16 contiguous dims of its K row at once:
+// k[c][kb2] holds dims (kb2*4 + quad)*16 .. +15, which become the A operands
+// of k-steps 2*kb2 (first 8) and 2*kb2 + 1; the query operands follow the
+// same order.  v[nb] holds the lane's 8 tokens of one dim (8 bytes).
+constexpr int kRowB8 = kD;              // bytes per FP8 K row
+constexpr int kTile8 = kBS * kRowB8;    // bytes per FP8 (page, head) tile
+struct PairTile8 {
+  u32x4 k[2][2];
+  u32x2 v[8];
+};
+
+__device__ __forceinline__ void load_pair(PairTile8& t, const char* ka, const char* kb_,
+                                          const char* va, const char* vb, int koff, int voff,
+                                          bool ksel, bool vsel) {
+  const char* kp = (ksel ? kb_ : ka) + koff;
+  const char* vp = (vsel ? vb : va) + voff;
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) t.k[c][kb2] = ld128_stream(kp + c * 4 * kRowB8 + kb2 * 64);
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) t.v[nb] = ld64_stream(vp + nb * 16 * kBS);
+}
+
+// Widen an FP8 pair tile to the bf16 operands consume_pair takes (exact).
+__device__ __forceinline__ void widen(const PairTile8& f, PairTile& t) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const u32x4& w = f.k[c][kb >> 1];
+      t.k[c][kb] = (kb & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
+    }
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) t.v[nb] = fp8x8_to_bf16x8(f.v[nb][0], f.v[nb][1]);
+}
 
 __device__ __forceinline__ void load_pair(PairTile& t, const char* ka, const char* kb_,
                                           const char* va, const char* vb, int koff, int voff,
@@ -127,8 +168,22 @@ __device__ __forceinline__ void consume_pair(PairTile& t, const u32x4 (&qf)[4], 
   }
 }
 
-template <int NW>
+// The bf16 operands of a loaded tile: the tile itself, or its FP8 codes widened into tw.
+template <bool F8, typename Tile>
+__device__ __forceinline__ PairTile& bf16_tile(Tile& tin, PairTile& tw) {
+  if constexpr (F8) {
+    widen(tin, tw);
+    return tw;
+  } else {
+    return tin;
+  }
+}
+
+template <int NW, bool F8>
 __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
+  using Tile = typename std::conditional<F8, PairTile8, PairTile>::type;
+  constexpr int kT = F8 ? kTile8 : kTile;               // bytes per (page, head) tile
+  constexpr int kR = F8 ? kRowB8 : kRowB;               // bytes per K row
   const int kvh = blockIdx.x, b = blockIdx.z;
   const int s = split_of_block(blockIdx.y, b, p.S);
   const int lane = threadIdx.x & 63;
@@ -155,20 +210,25 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
     const char* qr =
         static_cast<const char*>(p.q) + (((size_t)b * ql + cj) * p.Hq + kvh * G + cg) * kRowB;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) qf[kb] = ld128(qr + kb * 64 + quad * 16);
+    for (int kb = 0; kb < 4; ++kb) {
+      // k-step kb: dims kb*32 + quad*8 (bf16 caches), or, in the FP8 tile's
+      // order, (kb/2*4 + quad)*16 + (kb%2)*8
+      const int qo = F8 ? (kb >> 1) * 128 + quad * 32 + (kb & 1) * 16 : kb * 64 + quad * 16;
+      qf[kb] = ld128(qr + qo);
+    }
   } else {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) qf[kb] = u32x4{0u, 0u, 0u, 0u};
   }
 
   const int* bt = p.block_table + (size_t)b * p.maxb;
-  const size_t pstride = (size_t)p.Hkv * kTile;   // bytes per page, K and V pools alike
-  const char* kbase = static_cast<const char*>(p.k) + (size_t)kvh * kTile;
-  const char* vbase = static_cast<const char*>(p.v) + (size_t)kvh * kTile;
+  const size_t pstride = (size_t)p.Hkv * kT;      // bytes per page, K and V pools alike
+  const char* kbase = static_cast<const char*>(p.k) + (size_t)kvh * kT;
+  const char* vbase = static_cast<const char*>(p.v) + (size_t)kvh * kT;
   const bool ksel = (n >> 3) != 0;
-  const int koff = (((n >> 2) & 1) * 8 + (n & 3)) * kRowB + quad * 16;
+  const int koff = (((n >> 2) & 1) * 8 + (n & 3)) * kR + quad * 16;
   const bool vsel = (quad >> 1) != 0;
-  const int voff = n * 32 + (quad & 1) * 16;
+  const int voff = F8 ? n * kBS + (quad & 1) * 8 : n * 32 + (quad & 1) * 16;
 
   f32x4 acc[8];
 #pragma unroll
@@ -177,7 +237,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
 
   const int npairs = (p1 - p0 + 1) >> 1;
   int k = w;
-  auto issue = [&](PairTile& t, int kk) {
+  auto issue = [&](Tile& t, int kk) {
     if (kk >= npairs) {                              // past the split: read zeros (L2)
       const char* z = reinterpret_cast<const char*>(g_zero_tile);
       load_pair(t, z, z, z, z, koff, voff, ksel, vsel);
@@ -190,12 +250,14 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
     load_pair(t, kbase + ida * pstride, kbase + idb * pstride, vbase + ida * pstride,
               vbase + idb * pstride, koff, voff, ksel, vsel);
   };
-  auto consume = [&](PairTile& t, int kk) {
+  auto consume = [&](Tile& tin, int kk) {
     const int pa_ = p0 + 2 * kk;
     const bool hasb = pa_ + 1 < p1;
     const bool partial = !hasb || (pa_ + 2) * kBS > ctx_lo;
     const int mypage = vsel ? pa_ + 1 : pa_;
     const int tok0 = (vsel && !hasb) ? -1 : mypage * kBS + (quad & 1) * 8;
+    PairTile tw;
+    PairTile& t = bf16_tile<F8>(tin, tw);
     if (partial)
       consume_pair<true>(t, qf, acc, m, l, p.scale_log2, tok0, ctx_col, ctx);
     else
@@ -206,7 +268,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
   // copy between tiles at the loop edge would wait for all of them).  Every
   // step issues its loads, past the split's end from the zero tile, so the
   // wait counts are the same on every path.
-  PairTile t0, t1;
+  Tile t0, t1;
   issue(t0, k);
   issue(t1, k + NW);
   for (; k < npairs; k += 2 * NW) {
@@ -246,7 +308,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
       L = fmaf(f, sm_l[i][hn], L);
       o = fmaf(f, sm_o[i][hn][d], o);
     }
-    o = empty ? 0.f : o / L;
+    o = empty ? 0.f : o * (F8 ? p.v_scale : 1.f) / L;   // FP8 caches: values carry v_scale
     const float lse = empty ? kNegInf : (M + fast_log2(L)) * kLn2;
     const size_t row = ((size_t)b * ql + rj) * p.Hq + kvh * G + rg;
     if (direct) {
@@ -271,14 +333,22 @@ constexpr int kGqaWaves = 4;
 
 }  // namespace
 
+bool gqa_mfma_fp8_supported(int D, int bs, int G, int ql) {
+  const int cols = G * ql;
+  return D == kD && bs == kBS && G >= 1 && cols >= 2 && cols <= 16;
+}
+
 bool gqa_mfma_supported(bool bf16, int D, int Dv, int bs, int G, int ql) {
   const int cols = G * ql;
   return bf16 && D == kD && Dv == kD && bs == kBS && G >= 1 && cols >= 2 && cols <= 16;
 }
 
-hipError_t launch_gqa_mfma(const Params& p, hipStream_t st) {
+hipError_t launch_gqa_mfma(const Params& p, bool fp8kv, hipStream_t st) {
   dim3 grid(p.Hkv, p.S, p.B);
-  hipLaunchKernelGGL(gqa_mfma_partial<kGqaWaves>, grid, dim3(kGqaWaves * 64), 0, st, p);
+  if (fp8kv)
+    hipLaunchKernelGGL((gqa_mfma_partial<kGqaWaves, true>), grid, dim3(kGqaWaves * 64), 0, st, p);
+  else
+    hipLaunchKernelGGL((gqa_mfma_partial<kGqaWaves, false>), grid, dim3(kGqaWaves * 64), 0, st, p);
   return hipGetLastError();
 }
 

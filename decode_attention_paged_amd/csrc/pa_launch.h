@@ -23,14 +23,15 @@ struct Params {
   int32_t ql;                // query rows per sequence (>= 1): rows are (b, j, h), j < ql
   int32_t S;                 // splits in the grid
   int32_t c;                 // pages per split
-  float scale_log2;          // scale * log2(e)
+  float scale_log2;          // scale * log2(e) (* k_scale for FP8 caches)
+  float v_scale;             // FP8 caches: factor of every value (1 otherwise)
   int32_t final_write;       // 1: S == 1, write out/lse directly
   int32_t fused;             // 1: the last workgroup of a unit merges the splits
 };
 
 // Each returns hipSuccess or the launch error.  Shapes are validated by the caller.
-hipError_t launch_mha_valu(const Params& p, bool bf16, hipStream_t st);
-hipError_t launch_gqa_mfma(const Params& p, hipStream_t st);
+hipError_t launch_mha_valu(const Params& p, bool bf16, bool fp8kv, hipStream_t st);
+hipError_t launch_gqa_mfma(const Params& p, bool fp8kv, hipStream_t st);
 hipError_t launch_mla_mfma(const Params& p, hipStream_t st);
 hipError_t launch_reduce(const Params& p, bool bf16, hipStream_t st);
 hipError_t launch_zero_i32(int32_t* dst, size_t n, hipStream_t st);
@@ -46,13 +47,17 @@ struct AppendParams {
   const int32_t* context_lens;
   int B, Hkv, D, Dv, bs, maxb, nblocks;
 };
-hipError_t launch_append(const AppendParams& a, bool bf16, bool mla, hipStream_t st);
+// esize: bytes per cache element (4 float32, 2 bfloat16, 1 FP8 code).
+hipError_t launch_append(const AppendParams& a, int esize, bool mla, hipStream_t st);
 
 // Which kernels exist (host-side predicates used by validation and dispatch).
 bool mha_valu_supported(bool bf16, int D, int bs);
 // G query heads per KV head, ql query rows: the kernel's 16 MFMA columns hold
 // the G * ql (row, head) pairs of a KV head.
 bool gqa_mfma_supported(bool bf16, int D, int Dv, int bs, int G, int ql);
+// FP8 E4M3 caches (bf16 queries): which shapes each kernel takes.
+bool gqa_mfma_fp8_supported(int D, int bs, int G, int ql);
+bool mha_valu_fp8_supported(int D, int bs);
 bool mla_mfma_supported(bool bf16, int Dqk, int Dv, int bs, int Hq);
 // Query heads one MLA workgroup holds (the grid has Hq / this head groups).
 int mla_heads_per_workgroup(int Hq, int bs);

@@ -24,10 +24,16 @@
 namespace pa {
 namespace {
 
-template <bool BF16, int D, int BS>
+// F8: the caches hold FP8 E4M3 codes (BF16 queries); ES is the cache
+// element size, QES the query's.
+template <bool BF16, int D, int BS, bool F8 = false>
 struct MhaCfg {
-  static constexpr int ES = BF16 ? 2 : 4;
+  static constexpr int ES = F8 ? 1 : (BF16 ? 2 : 4);
+  static constexpr int QES = BF16 ? 2 : 4;
   static constexpr int ROWB = D * ES;      // bytes per K row
+  static constexpr int QROWB = D * QES;    // bytes per query row
+  static constexpr int QPL = 16 / ES;      // dims of a K row per lane (one 16-byte load)
+  static constexpr int QV = QPL * QES / 16;   // 16-byte query loads per lane
   static constexpr int LPR = ROWB / 16;    // lanes per K row
   static constexpr int RPI = 64 / LPR;     // K rows per load instruction
   static constexpr int KI = BS / RPI;      // K loads per page
@@ -36,6 +42,7 @@ struct MhaCfg {
   static constexpr int DPL = D / 64;       // output dims per lane
   static constexpr int VI = DPL * CPD;     // V loads per page
   static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row width");
+  static_assert(!F8 || BF16, "FP8 caches take bf16 queries");
   static_assert(BS % RPI == 0 && BS % TPC == 0 && D % 64 == 0, "tile shape");
 };
 
@@ -65,16 +72,16 @@ __device__ __forceinline__ float across_rows_sum(float x) {
   return sum_xor32(x);
 }
 
-template <bool BF16, int D, int BS>
+template <bool BF16, int D, int BS, bool F8>
 struct MhaTile {
-  u32x4 k[MhaCfg<BF16, D, BS>::KI];
-  u32x4 v[MhaCfg<BF16, D, BS>::VI];
+  u32x4 k[MhaCfg<BF16, D, BS, F8>::KI];
+  u32x4 v[MhaCfg<BF16, D, BS, F8>::VI];
 };
 
-template <bool BF16, int D, int BS>
-__device__ __forceinline__ void load_tile(MhaTile<BF16, D, BS>& t, const char* kp, const char* vp,
-                                          int lane) {
-  using C = MhaCfg<BF16, D, BS>;
+template <bool BF16, int D, int BS, bool F8>
+__device__ __forceinline__ void load_tile(MhaTile<BF16, D, BS, F8>& t, const char* kp,
+                                          const char* vp, int lane) {
+  using C = MhaCfg<BF16, D, BS, F8>;
   const char* kl = kp + (lane / C::LPR) * C::ROWB + (lane % C::LPR) * 16;
 #pragma unroll
   for (int i = 0; i < C::KI; ++i) t.k[i] = ld128_stream(kl + i * C::RPI * C::ROWB);
@@ -94,19 +101,29 @@ struct MhaState {
   float acc[DPL];
 };
 
-template <bool BF16, int D, int BS, bool PARTIAL>
-__device__ __forceinline__ void consume_tile(const MhaTile<BF16, D, BS>& t, MhaState<D / 64>& st,
-                                             const u32x4& qv, const float (&qf)[4], float scale_log2,
-                                             int lane, int nvalid) {
-  using C = MhaCfg<BF16, D, BS>;
+template <bool BF16, int D, int BS, bool F8, bool PARTIAL>
+__device__ __forceinline__ void consume_tile(const MhaTile<BF16, D, BS, F8>& t,
+                                             MhaState<D / 64>& st,
+                                             const u32x4 (&qv)[MhaCfg<BF16, D, BS, F8>::QV],
+                                             const float (&qf)[4], float scale_log2, int lane,
+                                             int nvalid) {
+  using C = MhaCfg<BF16, D, BS, F8>;
   const int row = lane / C::LPR;
   float sc[C::KI];
 #pragma unroll
   for (int i = 0; i < C::KI; ++i) {
     float d = 0.f;
-    if constexpr (BF16) {
+    if constexpr (F8) {
+      // 16 dims: word e holds dims 4e .. 4e+3, matched by query words 2e, 2e+1
 #pragma unroll
-      for (int e = 0; e < 4; ++e) d = dot2_bf16(qv[e], t.k[i][e], d);
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = t.k[i][e];
+        d = dot2_bf16(qv[e >> 1][(2 * e) & 3], fp8x2_to_bf16x2<false>(w), d);
+        d = dot2_bf16(qv[e >> 1][(2 * e + 1) & 3], fp8x2_to_bf16x2<true>(w), d);
+      }
+    } else if constexpr (BF16) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d = dot2_bf16(qv[0][e], t.k[i][e], d);
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) d = fmaf(qf[e], as_f32(t.k[i][e]), d);
@@ -140,7 +157,21 @@ __device__ __forceinline__ void consume_tile(const MhaTile<BF16, D, BS>& t, MhaS
 #pragma unroll
     for (int h = 0; h < C::CPD; ++h) {
       const u32x4 vv = t.v[j * C::CPD + h];
-      if constexpr (BF16) {
+      if constexpr (F8) {
+        // 16 tokens of one dim: word e holds tokens 4e .. 4e+3
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(vv[e], false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(vv[e], true);
+          const float v4[4] = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int t0 = h * 16 + 4 * e + k;
+            const float v0 = (PARTIAL && t0 >= nvalid) ? 0.f : v4[k];
+            a = fmaf(ps[t0], v0, a);
+          }
+        }
+      } else if constexpr (BF16) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t0 = h * 8 + 2 * e;
@@ -166,9 +197,9 @@ __device__ __forceinline__ void consume_tile(const MhaTile<BF16, D, BS>& t, MhaS
   }
 }
 
-template <bool BF16, int D, int BS, int NW>
+template <bool BF16, int D, int BS, bool F8, int NW>
 __global__ __launch_bounds__(NW * 64) void mha_valu_partial(Params p) {
-  using C = MhaCfg<BF16, D, BS>;
+  using C = MhaCfg<BF16, D, BS, F8>;
   // head fastest: consecutive workgroups land on different XCDs with equal work
   const int h = blockIdx.x, b = blockIdx.z;
   const int s = split_of_block(blockIdx.y, b, p.S);
@@ -182,12 +213,14 @@ __global__ __launch_bounds__(NW * 64) void mha_valu_partial(Params p) {
   const int p0 = s * p.c;
   const int p1 = min(pages, p0 + p.c);
 
-  // this lane's 16 bytes of the query row
-  const char* qrow = static_cast<const char*>(p.q) + ((size_t)b * p.Hq + h) * C::ROWB;
-  const u32x4 qv = ld128(qrow + (lane % C::LPR) * 16);
+  // the query dims matching this lane's part of a K row
+  const char* qrow = static_cast<const char*>(p.q) + ((size_t)b * p.Hq + h) * C::QROWB;
+  u32x4 qv[C::QV];
+#pragma unroll
+  for (int i = 0; i < C::QV; ++i) qv[i] = ld128(qrow + (lane % C::LPR) * C::QV * 16 + i * 16);
   float qf[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) qf[e] = as_f32(qv[e]);
+  for (int e = 0; e < 4; ++e) qf[e] = as_f32(qv[0][e]);
 
   const int* bt = p.block_table + (size_t)b * p.maxb;
   const size_t kstride = (size_t)p.Hkv * BS * C::ROWB;      // bytes per K page
@@ -201,7 +234,7 @@ __global__ __launch_bounds__(NW * 64) void mha_valu_partial(Params p) {
 #pragma unroll
   for (int j = 0; j < C::DPL; ++j) st.acc[j] = 0.f;
 
-  auto issue = [&](MhaTile<BF16, D, BS>& t, int pg) {
+  auto issue = [&](MhaTile<BF16, D, BS, F8>& t, int pg) {
     if (pg >= p1) {                                  // past the split: read zeros (L2)
       const char* z = reinterpret_cast<const char*>(g_zero_tile);
       load_tile(t, z, z, lane);
@@ -210,17 +243,17 @@ __global__ __launch_bounds__(NW * 64) void mha_valu_partial(Params p) {
     const int id = clampi(bt[pg], 0, p.nblocks - 1);
     load_tile(t, kbase + id * kstride, vbase + id * vstride, lane);
   };
-  auto consume = [&](MhaTile<BF16, D, BS>& t, int pg) {
+  auto consume = [&](MhaTile<BF16, D, BS, F8>& t, int pg) {
     const int nvalid = ctx - pg * BS;
     if (nvalid >= BS)
-      consume_tile<BF16, D, BS, false>(t, st, qv, qf, p.scale_log2, lane, BS);
+      consume_tile<BF16, D, BS, F8, false>(t, st, qv, qf, p.scale_log2, lane, BS);
     else
-      consume_tile<BF16, D, BS, true>(t, st, qv, qf, p.scale_log2, lane, nvalid);
+      consume_tile<BF16, D, BS, F8, true>(t, st, qv, qf, p.scale_log2, lane, nvalid);
   };
   // Two register tiles in turn (see the grouped-query kernel): each consume
   // waits only for its own tile's loads; tiles past the split read zeros.
   int pg = p0 + w;
-  MhaTile<BF16, D, BS> t0, t1;
+  MhaTile<BF16, D, BS, F8> t0, t1;
   issue(t0, pg);
   issue(t1, pg + NW);
   for (; pg < p1; pg += 2 * NW) {
@@ -254,7 +287,8 @@ __global__ __launch_bounds__(NW * 64) void mha_valu_partial(Params p) {
     L = fmaf(f[i], sm_l[i], L);
   }
   const bool empty = (M == kNegInf);
-  const float inv = empty ? 0.f : 1.f / L;
+  // FP8 caches: every value carries v_scale, applied once here
+  const float inv = empty ? 0.f : (F8 ? p.v_scale : 1.f) / L;
   const float lse = empty ? kNegInf : (M + fast_log2(L)) * kLn2;
   const size_t row = (size_t)b * p.Hq + h;
   const bool direct = split_is_direct(p, nsplit);
@@ -288,10 +322,11 @@ __global__ __launch_bounds__(NW * 64) void mha_valu_partial(Params p) {
 
 constexpr int kMhaWaves = 4;
 
-template <bool BF16, int D, int BS>
+template <bool BF16, int D, int BS, bool F8 = false>
 hipError_t launch_one(const Params& p, hipStream_t st) {
   dim3 grid(p.Hq, p.S, p.B);
-  hipLaunchKernelGGL((mha_valu_partial<BF16, D, BS, kMhaWaves>), grid, dim3(kMhaWaves * 64), 0, st, p);
+  hipLaunchKernelGGL((mha_valu_partial<BF16, D, BS, F8, kMhaWaves>), grid, dim3(kMhaWaves * 64), 0,
+                     st, p);
   return hipGetLastError();
 }
 
@@ -302,8 +337,16 @@ bool mha_valu_supported(bool bf16, int D, int bs) {
   return (D == 64 || D == 128) && (bs == 16 || bs == 32);
 }
 
-hipError_t launch_mha_valu(const Params& p, bool bf16, hipStream_t st) {
+bool mha_valu_fp8_supported(int D, int bs) { return D == 128 && (bs == 16 || bs == 32); }
+
+hipError_t launch_mha_valu(const Params& p, bool bf16, bool fp8kv, hipStream_t st) {
   const int D = p.D, bs = p.bs;
+  if (fp8kv) {
+    if (!bf16) return hipErrorInvalidValue;
+    if (D == 128 && bs == 16) return launch_one<true, 128, 16, true>(p, st);
+    if (D == 128 && bs == 32) return launch_one<true, 128, 32, true>(p, st);
+    return hipErrorInvalidValue;
+  }
   if (bf16) {
     if (D == 128 && bs == 16) return launch_one<true, 128, 16>(p, st);
     if (D == 128 && bs == 32) return launch_one<true, 128, 32>(p, st);

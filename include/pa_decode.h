@@ -45,7 +45,11 @@
  *   lse          [batch][q_len][num_q_heads]                        float32
  *   (q_len = 1 drops that axis: q [batch][num_q_heads][head_dim] etc.)
  *   dtype PA_F32 = float32, PA_BF16 = bfloat16 (accumulation is float32;
- *   bf16 outputs are rounded to nearest even).
+ *   bf16 outputs are rounded to nearest even).  The caches may instead hold
+ *   FP8 E4M3 codes (kv_dtype, one byte per element, same layouts) with one
+ *   scale per cache tensor; q and out stay bfloat16.  The pages name FP8 only
+ *   as the hardware low precision FlashAttention-3 uses (the "llms-attention"
+ *   post); this per-tensor-scale reading is the library's.
  *
  * Splits: with S = num_splits and P = ceil(max_context_len / block_size),
  *   every split covers c = ceil(P / S) pages; sequence b uses
@@ -83,7 +87,11 @@ typedef enum pa_status {
   PA_ERR_HIP = 4          /* the HIP runtime reported an error (device query or launch) */
 } pa_status;
 
-typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+/* PA_FP8_E4M3 is a cache dtype only (pa_shape.kv_dtype): OCP FP8 E4M3 codes
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; subnormals;
+ * S.1111.111 is NaN; no infinity), each read as its tensor's scale times the
+ * code's value. */
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
 
 typedef struct pa_shape {
   int32_t batch;              /* B >= 1 */
@@ -98,6 +106,9 @@ typedef struct pa_shape {
   float scale;                /* score scale, finite and > 0, e.g. 1/sqrt(head_dim) */
   int32_t dtype;              /* pa_dtype of q, caches and out */
   int32_t q_len;              /* query rows per sequence, 0..16 (0 and 1: one row) */
+  int32_t kv_dtype;           /* dtype of the caches: 0 = dtype, or PA_FP8_E4M3 (with PA_BF16 q) */
+  float k_scale;              /* FP8 caches: a key is k_scale times its code's value (finite, > 0) */
+  float v_scale;              /* FP8 caches: a value is v_scale times its code's value (finite, > 0) */
 } pa_shape;
 
 /* Human-readable name of a status code.  Never NULL. */
@@ -163,7 +174,10 @@ pa_status pa_workspace_init(const pa_shape* shape, int32_t num_splits, int32_t m
  * head_dim_v == head_dim; block_size 16 or 32.  With q_len > 1: PA_BF16,
  * head_dim 128, block_size 16 and (num_q_heads / num_kv_heads) * q_len <= 16
  * (each KV tile is then read once for all rows and heads of its group); the
- * splits are merged by a reduction launch.
+ * splits are merged by a reduction launch.  FP8 caches (kv_dtype
+ * PA_FP8_E4M3): PA_BF16 q, head_dim 128, block_size 16, any q_len the
+ * bf16 path takes; codes are widened to bfloat16 exactly, k_scale folds into
+ * the score scale and v_scale into the outputs.
  */
 pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
                     const void* v_cache, const int32_t* block_table,

@@ -69,7 +69,7 @@ def test_shape_struct_matches_header(tmp_path):
     compiling the header with the host C compiler)."""
     import shutil
     import subprocess
-    assert ctypes.sizeof(PaShape) == 12 * 4       # 11 int32 fields + one float, no padding
+    assert ctypes.sizeof(PaShape) == 15 * 4       # 12 int32 fields + three floats, no padding
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
         pytest.skip("no host C compiler")
@@ -94,6 +94,8 @@ def test_shape_struct_matches_header(tmp_path):
     ("max_context_len", 8 * 16 + 1),  # longer than the block table allows
     ("scale", math.inf), ("scale", 0.0), ("scale", -0.125), ("scale", math.nan),
     ("q_len", -1),
+    ("kv_dtype", 7),                # not a cache dtype
+    ("kv_dtype", -1),
 ])
 def test_invalid_shapes(lib, field, value):
     assert decode(lib, shape(**{field: value})) == _lib.PA_ERR_INVALID
@@ -114,9 +116,32 @@ def test_null_shape_and_pointers(lib):
     dict(q_len=2, dtype=_lib.PA_F32),                   # several rows: bf16 MFMA kernel only
     dict(q_len=2, head_dim=64, head_dim_v=64),          # several rows: head_dim 128 only
     dict(q_len=5, num_kv_heads=2),                      # G = 4 heads x 5 rows: 20 > 16 columns
+    dict(kv_dtype=_lib.PA_FP8_E4M3, k_scale=0.1, v_scale=0.1, dtype=_lib.PA_F32),   # FP8: bf16 q
+    dict(kv_dtype=_lib.PA_FP8_E4M3, k_scale=0.1, v_scale=0.1, head_dim=64, head_dim_v=64),
 ])
+
 def test_unsupported(lib, kw):
     assert decode(lib, shape(**kw)) == _lib.PA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("ks,vs", [(0.0, 1.0), (1.0, -1.0), (math.nan, 1.0), (1.0, math.inf)])
+def test_fp8_scales_checked(lib, ks, vs):
+    s = shape(kv_dtype=_lib.PA_FP8_E4M3, k_scale=ks, v_scale=vs)
+    assert decode(lib, s) == _lib.PA_ERR_INVALID
+
+
+def test_fp8_shapes_pass_validation(lib):
+    """FP8 caches with bf16 queries validate (the workspace check fails first,
+    so nothing launches); an explicit cache dtype equal to the query's is the
+    default; the latent (MLA) path has no FP8 kernel."""
+    for kw in (dict(), dict(num_kv_heads=2), dict(q_len=2), dict(block_size=32, max_context_len=200)):
+        s = shape(kv_dtype=_lib.PA_FP8_E4M3, k_scale=0.02, v_scale=3.0, **kw)
+        assert decode(lib, s, splits=4) == _lib.PA_ERR_WORKSPACE, kw
+    assert decode(lib, shape(kv_dtype=_lib.PA_BF16), splits=4) == _lib.PA_ERR_WORKSPACE
+    m = shape(num_q_heads=128, num_kv_heads=1, head_dim=576, head_dim_v=512, block_size=64,
+              max_context_len=300, kv_dtype=_lib.PA_FP8_E4M3, k_scale=0.1, v_scale=0.1)
+    assert lib.pa_decode_mla(ctypes.byref(m), FAKE, FAKE, FAKE, FAKE, 1, FAKE, NULL, NULL, 0,
+                             NULL) == _lib.PA_ERR_UNSUPPORTED
 
 
 def test_several_rows_supported(lib):

@@ -25,6 +25,9 @@ CASES = {
                     block_size=16, context_lens=[17, 16, 1, 40], num_blocks=20),
     "gqa_bf16": dict(kind="mha", dtype="bf16", batch=4, num_q_heads=16, num_kv_heads=2,
                      head_dim=128, block_size=16, context_lens=[33, 1, 300, 16], num_blocks=40),
+    "gqa_fp8": dict(kind="mha", dtype="bf16", batch=4, num_q_heads=16, num_kv_heads=2,
+                    head_dim=128, block_size=16, context_lens=[33, 1, 300, 16], num_blocks=40,
+                    kv_dtype="fp8", k_scale=0.05, v_scale=0.3),
     "mla_bf16": dict(kind="mla", dtype="bf16", batch=3, num_q_heads=16, num_kv_heads=1,
                      head_dim=576, head_dim_v=512, block_size=64, context_lens=[65, 64, 1],
                      num_blocks=12, scale=192 ** -0.5),
@@ -33,7 +36,17 @@ CASES = {
 
 def _bits(t: torch.Tensor) -> torch.Tensor:
     """Raw element bits (NaN-safe equality)."""
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def _poison(t: torch.Tensor, idx):
+    """Set t[idx] to NaN (the FP8 NaN code for FP8 caches)."""
+    if t.dtype == torch.float8_e4m3fn:
+        t.view(torch.uint8)[idx] = 0x7F
+    else:
+        t[idx] = float("nan")
 
 
 def _rows(inp, b, n):
@@ -46,6 +59,9 @@ def _rows(inp, b, n):
 
 
 def _dev(a: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "fp8":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda().view(
+            torch.float8_e4m3fn)
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
@@ -69,8 +85,8 @@ def test_append_then_decode(name):
         if full.kind == "mla":
             t_before["kv_cache"][page, slot, :] = float("nan")
         else:
-            t_before["k_cache"][page, :, slot, :] = float("nan")
-            t_before["v_cache"][page, :, :, slot] = float("nan")
+            _poison(t_before["k_cache"], (page, slice(None), slot, slice(None)))
+            _poison(t_before["v_cache"], (page, slice(None), slice(None), slot))
     if full.kind == "mla":
         c_new = _dev(np.stack([r[0] for r in rows]), full.dtype)
         pa.append_latent(c_new, t_before["kv_cache"], t_before["block_table"],
@@ -78,8 +94,9 @@ def test_append_then_decode(name):
         torch.cuda.synchronize()
         assert torch.equal(_bits(t_before["kv_cache"]), _bits(t_full["kv_cache"]))
     else:
-        k_new = _dev(np.stack([r[0] for r in rows]), full.dtype)
-        v_new = _dev(np.stack([r[1] for r in rows]), full.dtype)
+        kvd = full.kv_dtype or full.dtype
+        k_new = _dev(np.stack([r[0] for r in rows]), kvd)
+        v_new = _dev(np.stack([r[1] for r in rows]), kvd)
         pa.append_kv(k_new, v_new, t_before["k_cache"], t_before["v_cache"],
                      t_before["block_table"], t_before["context_lens"])
         torch.cuda.synchronize()
@@ -92,9 +109,10 @@ def test_append_then_decode(name):
         out, lse = pa.decode_mla(t_before["q"], t_before["kv_cache"], t_before["block_table"],
                                  t_before["context_lens"], scale=full.scale, num_splits=2)
     else:
+        fp8 = dict(k_scale=full.k_scale, v_scale=full.v_scale) if full.kv_dtype == "fp8" else {}
         out, lse = pa.decode(t_before["q"], t_before["k_cache"], t_before["v_cache"],
                              t_before["block_table"], t_before["context_lens"],
-                             scale=full.scale, num_splits=2)
+                             scale=full.scale, num_splits=2, **fp8)
     torch.cuda.synchronize()
     tol = 1e-5 if full.dtype == "f32" else 2e-2
     assert np.abs(from_device(out) - ref_out).max() <= tol

@@ -42,9 +42,10 @@ def run(inp, t=None, num_splits=0, poison=True):
                                  max_context_len=inp.max_context_len, scale=inp.scale,
                                  head_dim_v=inp.head_dim_v, num_splits=num_splits)
     else:
+        fp8 = dict(k_scale=inp.k_scale, v_scale=inp.v_scale) if inp.kv_dtype == "fp8" else {}
         out, lse = pa.decode(t["q"], t["k_cache"], t["v_cache"], t["block_table"],
                              t["context_lens"], max_context_len=inp.max_context_len,
-                             scale=inp.scale, num_splits=num_splits)
+                             scale=inp.scale, num_splits=num_splits, **fp8)
     torch.cuda.synchronize()
     return out, lse
 
@@ -193,6 +194,49 @@ def test_several_rows(name):
 
 
 # ----------------------------------------------------------------------------------------------
+# FP8 E4M3 caches with bf16 queries (both kernels, one and several rows): every output compared.
+# Unused pages and tail slots hold the FP8 NaN code.
+# ----------------------------------------------------------------------------------------------
+
+FP8_KV = dict(kv_dtype="fp8", k_scale=0.037, v_scale=1.9)
+FP8 = {
+    "fp8_mha_bs16": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=4, num_kv_heads=4,
+                         head_dim=128, block_size=16, context_lens=[1, 37, 300], num_blocks=64,
+                         **FP8_KV),
+    "fp8_mha_bs32": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=2, num_kv_heads=2,
+                         head_dim=128, block_size=32, context_lens=[100, 31], num_blocks=20,
+                         **FP8_KV),
+    "fp8_gqa_g4": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=8, num_kv_heads=2,
+                       head_dim=128, block_size=16, context_lens=[17, 333], num_blocks=40, **FP8_KV),
+    "fp8_gqa_g8": dict(kind="mha", dtype="bf16", batch=4, num_q_heads=16, num_kv_heads=2,
+                       head_dim=128, block_size=16, context_lens=[1, 16, 1000, 47], num_blocks=90,
+                       **FP8_KV),
+    "fp8_gqa_g16": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=16, num_kv_heads=1,
+                        head_dim=128, block_size=16, context_lens=[15, 515], num_blocks=40,
+                        **FP8_KV),
+    "fp8_rows_mha_q4": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=4, num_kv_heads=4,
+                            head_dim=128, block_size=16, context_lens=[3, 37, 300], num_blocks=64,
+                            q_len=4, **FP8_KV),
+    "fp8_rows_gqa_g4_q4": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=8, num_kv_heads=2,
+                               head_dim=128, block_size=16, context_lens=[2, 17, 333],
+                               num_blocks=60, q_len=4, **FP8_KV),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8))
+def test_fp8_kv(name):
+    inp = make_paged_inputs(name=name, seed=400 + sorted(FP8).index(name), **FP8[name])
+    ref_out, ref_lse = oracle.decode_inputs(inp)
+    t = to_device(inp, "cuda", poison=True)
+    assert t["k_cache"].dtype == torch.float8_e4m3fn
+    P = -(-inp.max_context_len // inp.block_size)
+    for S in [0, 1, 2, 3, 7, P + 5]:
+        say(f"{name} S={S}")
+        out, lse = run(inp, t, num_splits=S)
+        compare(inp, out, lse, ref_out, ref_lse, f"{name} S={S}")
+
+
+# ----------------------------------------------------------------------------------------------
 # Full-size workloads in the launch configuration the benchmark times (heuristic split count):
 # sampled (sequence, head) rows against the oracle, every output finite.
 # ----------------------------------------------------------------------------------------------
@@ -218,7 +262,8 @@ def sample_rows(inp, n, seed):
 
 @pytest.mark.parametrize("name", ["llama_mha_bf16", "long_gqa_bf16", "ragged_gqa_bf16", "mla_bf16",
                                   "mla_topk_bf16", "mla_allentries_bf16", "llama_mha_q4_bf16",
-                                  "long_gqa_q4_bf16", "mla_q2_bf16"])
+                                  "long_gqa_q4_bf16", "mla_q2_bf16", "llama_mha_fp8",
+                                  "long_gqa_fp8", "ragged_gqa_fp8"])
 def test_full_size_sampled(name):
     say(f"full {name}: drawing inputs")
     inp = make_config(name)

@@ -33,6 +33,7 @@ import numpy as np
 
 CHUNK = 1 << 22
 BF16_NAN_BITS = 0x7FC0
+FP8_NAN_CODE = 0x7F          # E4M3 NaN (S.1111.111)
 
 
 def _threads() -> int:
@@ -59,6 +60,15 @@ class _Draw:
 
     def __init__(self, seed_seq: np.random.SeedSequence):
         self.seq = seed_seq
+
+    def normal_fp8(self, n: int, scale: float) -> np.ndarray:
+        """n N(0,1) values as FP8 E4M3 codes (uint8) of value / scale: rounded to
+        nearest even by torch's float8_e4m3fn cast, after clipping to the
+        format's largest finite magnitude, 448."""
+        import torch
+        f = self.normal(n, "f32")
+        x = np.clip(f / np.float32(scale), -448.0, 448.0).astype(np.float32)
+        return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
     def normal(self, n: int, dtype: str) -> np.ndarray:
         """n values in the workload dtype (float32, or bf16 bits as uint16)."""
@@ -104,6 +114,9 @@ class PagedDecodeInputs:
     v_pages: np.ndarray | None = None   # [n_used][Hkv][D][bs]
     c_pages: np.ndarray | None = None   # [n_used][bs][Dqk] (MLA latent)
     meta: dict = field(default_factory=dict)
+    kv_dtype: str | None = None         # cache dtype when not the query's: "fp8" (E4M3 codes)
+    k_scale: float = 1.0                # FP8: a key is k_scale times its code's value
+    v_scale: float = 1.0
 
     @property
     def q_len(self) -> int:
@@ -120,6 +133,9 @@ class PagedDecodeInputs:
 
     @property
     def esize(self) -> int:
+        """Bytes per cache element."""
+        if self.kv_dtype == "fp8":
+            return 1
         return 4 if self.dtype == "f32" else 2
 
     def compact_block_table(self) -> np.ndarray:
@@ -166,7 +182,8 @@ def make_paged_inputs(*, name: str = "custom", kind: str = "mha", dtype: str = "
                       context_lens, num_blocks: int | None = None,
                       max_blocks_per_seq: int | None = None, scale: float | None = None,
                       seed: int = 0, poison: bool = True, values: bool = True,
-                      meta: dict | None = None, q_len: int = 1) -> PagedDecodeInputs:
+                      meta: dict | None = None, q_len: int = 1, kv_dtype: str | None = None,
+                      k_scale: float = 1.0, v_scale: float = 1.0) -> PagedDecodeInputs:
     """Draw a paged decode workload.
 
     ``context_lens`` is an int sequence (or a callable ``rng -> array`` drawn
@@ -176,12 +193,16 @@ def make_paged_inputs(*, name: str = "custom", kind: str = "mha", dtype: str = "
     unassigned pages are to be NaN-filled by the caller as well.  With
     ``values=False`` only the shapes, lengths and tables are drawn.  With
     ``q_len`` > 1, q is [B][q_len][Hq][Dqk]: the sequences' last q_len tokens
-    as query rows.
+    as query rows.  With ``kv_dtype="fp8"`` (bf16 queries) the caches hold
+    FP8 E4M3 codes of the same N(0,1) draws divided by k_scale / v_scale.
     """
     if kind not in ("mha", "mla"):
         raise ValueError(kind)
     if dtype not in ("f32", "bf16"):
         raise ValueError(dtype)
+    fp8 = kv_dtype == "fp8"
+    if kv_dtype not in (None, dtype, "fp8") or (fp8 and (dtype != "bf16" or kind == "mla")):
+        raise ValueError(f"cache dtype {kv_dtype} with {dtype} queries / {kind}")
     if kind == "mla":
         num_kv_heads = 1
     head_dim_v = head_dim if head_dim_v is None else head_dim_v
@@ -214,7 +235,10 @@ def make_paged_inputs(*, name: str = "custom", kind: str = "mha", dtype: str = "
                             num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                             head_dim=head_dim, head_dim_v=head_dim_v, block_size=block_size,
                             num_blocks=nb, scale=float(scale), context_lens=ctx,
-                            block_table=bt, page_ids=page_ids, q=q, meta=dict(meta or {}))
+                            block_table=bt, page_ids=page_ids, q=q, meta=dict(meta or {}),
+                            kv_dtype="fp8" if fp8 else None,
+                            k_scale=float(k_scale) if fp8 else 1.0,
+                            v_scale=float(v_scale) if fp8 else 1.0)
     if not values:
         return inp
 
@@ -238,12 +262,21 @@ def make_paged_inputs(*, name: str = "custom", kind: str = "mha", dtype: str = "
 
     hkv, dv = num_kv_heads, head_dim_v
     # Drawn token-major ([page][slot][head][dim], logical order), then laid out.
-    k = _Draw(k_seq).normal(total * block_size * hkv * dq, dtype).reshape(total, block_size, hkv, dq)
+    if fp8:
+        nan = np.uint8(FP8_NAN_CODE)
+        k = _Draw(k_seq).normal_fp8(total * block_size * hkv * dq, k_scale)
+    else:
+        k = _Draw(k_seq).normal(total * block_size * hkv * dq, dtype)
+    k = k.reshape(total, block_size, hkv, dq)
     if poison:
         k[tail] = nan
     inp.k_pages = np.ascontiguousarray(k.transpose(0, 2, 1, 3))   # [n][Hkv][bs][D]
     del k
-    v = _Draw(v_seq).normal(total * block_size * hkv * dv, dtype).reshape(total, block_size, hkv, dv)
+    if fp8:
+        v = _Draw(v_seq).normal_fp8(total * block_size * hkv * dv, v_scale)
+    else:
+        v = _Draw(v_seq).normal(total * block_size * hkv * dv, dtype)
+    v = v.reshape(total, block_size, hkv, dv)
     if poison:
         v[tail] = nan
     inp.v_pages = np.ascontiguousarray(v.transpose(0, 2, 3, 1))   # [n][Hkv][Dv][bs]
@@ -323,11 +356,33 @@ CONFIGS = {
         scale=1.0 / math.sqrt(192), seed=5, q_len=2,
         meta=dict(desc="MLA latent bf16, 2 query rows per sequence (causal): B32, 128 heads, "
                        "latent 576, ctx 8192, bs64")),
+    # FP8 E4M3 caches (bf16 queries, one scale per cache tensor) over the decode
+    # workloads' lengths and pages: the same N(0,1) draws, quantised.
+    "llama_mha_fp8": dict(
+        kind="mha", dtype="bf16", batch=16, num_q_heads=32, num_kv_heads=32, head_dim=128,
+        block_size=16, context_lens=_uniform_ctx(1024, 4096, 16), num_blocks=65536,
+        max_blocks_per_seq=256, scale=1.0 / math.sqrt(128), seed=2, kv_dtype="fp8",
+        k_scale=0.017, v_scale=0.019,
+        meta=dict(desc="Llama-style MHA, FP8 E4M3 KV (bf16 q): B16, 32 heads, D128, "
+                       "ctx U[1024,4096], bs16")),
+    "long_gqa_fp8": dict(
+        kind="mha", dtype="bf16", batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        block_size=16, context_lens=[131072], num_blocks=8192, scale=1.0 / math.sqrt(128), seed=3,
+        kv_dtype="fp8", k_scale=0.017, v_scale=0.019,
+        meta=dict(desc="long-context GQA, FP8 E4M3 KV (bf16 q): B1, 32 q / 8 kv heads, D128, "
+                       "ctx 131072, bs16")),
+    "ragged_gqa_fp8": dict(
+        kind="mha", dtype="bf16", batch=64, num_q_heads=64, num_kv_heads=8, head_dim=128,
+        block_size=16, context_lens=_loguniform_ctx(128, 32768, 64), num_blocks=65536,
+        max_blocks_per_seq=2048, scale=1.0 / math.sqrt(128), seed=4, kv_dtype="fp8",
+        k_scale=0.017, v_scale=0.019,
+        meta=dict(desc="ragged GQA, FP8 E4M3 KV (bf16 q): 64 seqs, ctx log-U[128,32768], "
+                       "64 q / 8 kv heads, D128, bs16")),
 }
 
 CONFIG_ORDER = ["tiny_mha_f32", "llama_mha_bf16", "long_gqa_bf16", "ragged_gqa_bf16", "mla_bf16",
                 "mla_topk_bf16", "mla_allentries_bf16", "llama_mha_q4_bf16", "long_gqa_q4_bf16",
-                "mla_q2_bf16"]
+                "mla_q2_bf16", "llama_mha_fp8", "long_gqa_fp8", "ragged_gqa_fp8"]
 
 
 def make_config(name: str, *, poison: bool = True, values: bool = True, seed: int | None = None,
