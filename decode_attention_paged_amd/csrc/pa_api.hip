@@ -138,7 +138,10 @@ int heuristic_splits(const pa_shape& s, int cus, bool mla) {
       heads_per_wg = 1;
       target_bytes = kSplitBytesValu;
     }
-    const double page_bytes = (double)s.block_size * (s.head_dim + s.head_dim_v) * esz;
+    // split sizes are measured in bf16 bytes: FP8 caches (half the bytes per
+    // token) get the same tokens per split, which measured better on the
+    // ragged batch (186 against 201 us) and within 3% elsewhere
+    const double page_bytes = (double)s.block_size * (s.head_dim + s.head_dim_v) * (esz < 2 ? 2 : esz);
     const double part_bytes = 2.0 * heads_per_wg * (s.head_dim_v + 1) * 4.0;
     int c_min = (int)std::ceil(part_bytes / (0.03 * page_bytes));
     if (c_min < 1) c_min = 1;
