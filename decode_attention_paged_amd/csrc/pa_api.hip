@@ -16,6 +16,9 @@ constexpr long kFusedMergeBytes = 4 * 1024;   // largest per-unit partial set me
 constexpr double kSplitBytesValu = 128.0 * 1024.0;   // KV bytes per workgroup, VALU kernel
 constexpr double kSplitBytesMfma = 1024.0 * 1024.0;  // KV bytes per workgroup, MFMA kernel
 constexpr int kMaxQLen = 16;                         // query rows per sequence
+// Longest context: token indices, split ends ((s + 1) * c * bs) and page
+// counts stay in int32 arithmetic inside the kernels.
+constexpr int32_t kMaxContext = 1 << 29;
 
 // Query rows per sequence (0 and 1 both mean one row).
 int rows_of(const pa_shape& s) { return s.q_len > 1 ? s.q_len : 1; }
@@ -69,6 +72,10 @@ pa_status check_shape(const pa_shape* s, bool mla) {
   if (s->q_len > kMaxQLen) return PA_ERR_UNSUPPORTED;
   if ((int64_t)s->max_context_len > (int64_t)s->max_blocks_per_seq * s->block_size)
     return PA_ERR_INVALID;
+  if (s->max_context_len > kMaxContext) return PA_ERR_UNSUPPORTED;
+  // rows (sequence, query row, head) are counted in int32 (grids, row indices)
+  if ((int64_t)s->batch * (s->q_len > 1 ? s->q_len : 1) * s->num_q_heads > 0x7fffffffLL)
+    return PA_ERR_UNSUPPORTED;
   if (s->dtype != PA_F32 && s->dtype != PA_BF16) return PA_ERR_INVALID;
   if (!std::isfinite(s->scale) || !(s->scale > 0.f)) return PA_ERR_INVALID;
   if (mla && (s->num_kv_heads != 1 || s->head_dim_v > s->head_dim)) return PA_ERR_INVALID;
@@ -76,7 +83,9 @@ pa_status check_shape(const pa_shape* s, bool mla) {
   return PA_OK;
 }
 
-int max_pages(const pa_shape& s) { return (s.max_context_len + s.block_size - 1) / s.block_size; }
+int max_pages(const pa_shape& s) {
+  return (int)(((int64_t)s.max_context_len + s.block_size - 1) / s.block_size);
+}
 
 // Number of compute units of the current device, cached per device.
 int device_cus() {

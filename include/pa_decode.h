@@ -65,7 +65,9 @@
  *   workspace.
  *
  * Errors: a status is returned, nothing is thrown.  Arguments are checked on
- *   the host before any HIP call; on failure nothing is launched.  Device-side
+ *   the host before any HIP call; on failure nothing is launched.  Limits
+ *   (PA_ERR_UNSUPPORTED beyond them): batch <= 65535, max_context_len <= 2^29,
+ *   batch * q_len * num_q_heads < 2^31, at most 65535 splits.  Device-side
  *   context_lens are clamped to [0, max_context_len] and block ids to
  *   [0, num_blocks), so malformed tables cannot read outside the pools.
  */

@@ -116,6 +116,8 @@ def test_null_shape_and_pointers(lib):
     dict(q_len=2, dtype=_lib.PA_F32),                   # several rows: bf16 MFMA kernel only
     dict(q_len=2, head_dim=64, head_dim_v=64),          # several rows: head_dim 128 only
     dict(q_len=5, num_kv_heads=2),                      # G = 4 heads x 5 rows: 20 > 16 columns
+    dict(max_context_len=(1 << 29) + 16, max_blocks_per_seq=(1 << 25) + 1),  # past 2^29 tokens
+    dict(num_q_heads=1 << 16, num_kv_heads=1 << 16, batch=65535),             # rows past 2^31
     dict(kv_dtype=_lib.PA_FP8_E4M3, k_scale=0.1, v_scale=0.1, dtype=_lib.PA_F32),   # FP8: bf16 q
     dict(kv_dtype=_lib.PA_FP8_E4M3, k_scale=0.1, v_scale=0.1, head_dim=64, head_dim_v=64),
 ])
