@@ -70,8 +70,6 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
-typedef __attribute__((address_space(3))) float lds_float;
 
 // 16 zero bytes in global memory: the load source for token slots past the
 // context, so no NaN or stale data reaches the value product.
@@ -374,6 +372,8 @@ struct RoleCfg {
 constexpr int kVoteOff = 0;        // int votes[NS]
 constexpr int kMtopOff = 64;       // float mtop[2][NH]: largest chunk max per token half
 constexpr int kStatOff = 2048;     // float stat_m[NH], stat_l[2][NH]
+static_assert(kMtopOff + 2 * 64 * 4 <= kStatOff && kStatOff + 3 * 64 * 4 <= kChunkB,
+              "end-of-pass regions fit the ring's first slot for up to 64 heads");
 
 template <int HH, int HBW>
 struct RoleShared {
