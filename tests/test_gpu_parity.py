@@ -127,6 +127,16 @@ SMALL = {
     "mla_bf16_bs1_h32": dict(kind="mla", dtype="bf16", batch=2, num_q_heads=32, num_kv_heads=1,
                              head_dim=576, head_dim_v=512, block_size=1, context_lens=[47, 65],
                              num_blocks=200, scale=192 ** -0.5),
+    # two 128-head groups (wide workgroups paired on an XCD), three 64-head groups
+    "mla_bf16_h256": dict(kind="mla", dtype="bf16", batch=2, num_q_heads=256, num_kv_heads=1,
+                          head_dim=576, head_dim_v=512, block_size=64, context_lens=[100, 257],
+                          num_blocks=12, scale=192 ** -0.5),
+    "mla_bf16_h192": dict(kind="mla", dtype="bf16", batch=2, num_q_heads=192, num_kv_heads=1,
+                          head_dim=576, head_dim_v=512, block_size=64, context_lens=[33, 190],
+                          num_blocks=10, scale=192 ** -0.5),
+    # grouped heads on 32-token pages run on the VALU kernel
+    "gqa_bf16_g4_bs32": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=8, num_kv_heads=2,
+                             head_dim=128, block_size=32, context_lens=[40, 300], num_blocks=20),
 }
 
 
@@ -172,6 +182,9 @@ ROWS = {
     "rows_mla_h16_q4": dict(kind="mla", dtype="bf16", batch=2, num_q_heads=16, num_kv_heads=1,
                             head_dim=576, head_dim_v=512, block_size=64, context_lens=[1, 700],
                             num_blocks=20, scale=192 ** -0.5, q_len=4),
+    "rows_mla_h32_q3": dict(kind="mla", dtype="bf16", batch=2, num_q_heads=32, num_kv_heads=1,
+                            head_dim=576, head_dim_v=512, block_size=64, context_lens=[66, 3],
+                            num_blocks=8, scale=192 ** -0.5, q_len=3),
     "rows_mla_bs1_h128_q2": dict(kind="mla", dtype="bf16", batch=3, num_q_heads=128,
                                  num_kv_heads=1, head_dim=576, head_dim_v=512, block_size=1,
                                  context_lens=[1, 100, 333], num_blocks=600, scale=192 ** -0.5,
