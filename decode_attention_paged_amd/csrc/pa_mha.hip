@@ -12,11 +12,13 @@
 //   K rows are D*esize bytes; LPR lanes cover a row with 16-byte loads and a
 //   wave loads RPI = 64/LPR rows per instruction.  The score of token
 //   i*RPI + r ends up in every lane of row group r after a DPP reduction.
-//   V is stored [D][bs]: lane l reads 16 contiguous bytes = TPC tokens of
-//   dim j*64 + l, so all lanes of one load share the same tokens and the
-//   token weights can be wave-uniform scalars (v_readlane into SGPRs).
-//   Each lane therefore owns whole output dims; no cross-lane sum of the
-//   accumulator is needed.
+//   V is stored [D][bs] (a row of bs tokens per dim).  Each V load reads 1 KiB
+//   of the tile contiguously: lane l takes 16 bytes, TPL tokens of one dim,
+//   so LPD lanes share a dim and each keeps a partial sum over its tokens;
+//   the LPD partials are added once, after the loop.  Token weights are
+//   read into SGPRs (v_readlane) and each lane selects its TPL of them.
+//   (Loads that each cover a full 1 KiB run measurably faster than loads
+//   of 16 bytes at a 32-byte stride, which read every cache line twice.)
 #include "pa_device.h"
 #include "pa_launch.h"
 #include "pa_merge.h"
@@ -37,13 +39,15 @@ struct MhaCfg {
   static constexpr int LPR = ROWB / 16;    // lanes per K row
   static constexpr int RPI = 64 / LPR;     // K rows per load instruction
   static constexpr int KI = BS / RPI;      // K loads per page
-  static constexpr int TPC = 16 / ES;      // tokens per 16-byte V chunk
-  static constexpr int CPD = BS / TPC;     // V chunks per dim
-  static constexpr int DPL = D / 64;       // output dims per lane
-  static constexpr int VI = DPL * CPD;     // V loads per page
+  static constexpr int VROWB = BS * ES;    // bytes per V row (one dim's bs tokens)
+  static constexpr int LPD = VROWB / 16;   // lanes per V row in a load
+  static constexpr int DPI = 64 / LPD;     // dims per V load (1 KiB)
+  static constexpr int VI = D / DPI;       // V loads per page = partial sums per lane
+  static constexpr int TPL = BS / LPD;     // tokens per lane in a V load (16 / ES)
   static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row width");
   static_assert(!F8 || BF16, "FP8 caches take bf16 queries");
-  static_assert(BS % RPI == 0 && BS % TPC == 0 && D % 64 == 0, "tile shape");
+  static_assert(BS % RPI == 0 && VROWB % 16 == 0 && LPD <= 8 && D % DPI == 0, "tile shape");
+  static_assert(TPL == 16 / ES, "a V load holds whole tokens");
 };
 
 // Sum over the LPR lanes of one K row.
@@ -86,24 +90,22 @@ __device__ __forceinline__ void load_tile(MhaTile<BF16, D, BS, F8>& t, const cha
 #pragma unroll
   for (int i = 0; i < C::KI; ++i) t.k[i] = ld128_stream(kl + i * C::RPI * C::ROWB);
 #pragma unroll
-  for (int j = 0; j < C::DPL; ++j)
-#pragma unroll
-    for (int h = 0; h < C::CPD; ++h)
-      t.v[j * C::CPD + h] = ld128_stream(vp + (size_t)(j * 64 + lane) * BS * C::ES + h * 16);
+  for (int k = 0; k < C::VI; ++k) t.v[k] = ld128_stream(vp + k * 1024 + lane * 16);
 }
 
 // Running state of one wave: max (log2 domain, wave-uniform), this lane's
-// row-group share of the sum, and the lane's output dims.
-template <int DPL>
+// row-group share of the sum, and the lane's partial sums of VI output dims
+// (dim k*DPI + lane/LPD over its TPL tokens of each page).
+template <int VI>
 struct MhaState {
   float m;
   float l;
-  float acc[DPL];
+  float acc[VI];
 };
 
 template <bool BF16, int D, int BS, bool F8, bool PARTIAL>
 __device__ __forceinline__ void consume_tile(const MhaTile<BF16, D, BS, F8>& t,
-                                             MhaState<D / 64>& st,
+                                             MhaState<MhaCfg<BF16, D, BS, F8>::VI>& st,
                                              const u32x4 (&qv)[MhaCfg<BF16, D, BS, F8>::QV],
                                              const float (&qf)[4], float scale_log2, int lane,
                                              int nvalid) {
@@ -151,50 +153,66 @@ __device__ __forceinline__ void consume_tile(const MhaTile<BF16, D, BS, F8>& t,
   float ps[BS];
 #pragma unroll
   for (int t2 = 0; t2 < BS; ++t2) ps[t2] = readlane(pr[t2 / C::RPI], (t2 % C::RPI) * C::LPR);
+  // this lane's tokens in every V load: tb .. tb + TPL - 1
+  const int sub = lane % C::LPD;
+  const int tb = sub * C::TPL;
+  float wt[C::TPL];
 #pragma unroll
-  for (int j = 0; j < C::DPL; ++j) {
-    float a = st.acc[j] * alpha;
+  for (int e = 0; e < C::TPL; ++e) {
+    float x = ps[e];
 #pragma unroll
-    for (int h = 0; h < C::CPD; ++h) {
-      const u32x4 vv = t.v[j * C::CPD + h];
-      if constexpr (F8) {
-        // 16 tokens of one dim: word e holds tokens 4e .. 4e+3
+    for (int g = 1; g < C::LPD; ++g) x = (sub == g) ? ps[g * C::TPL + e] : x;
+    wt[e] = x;
+  }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(vv[e], false);
-          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(vv[e], true);
-          const float v4[4] = {lo[0], lo[1], hi[0], hi[1]};
+  for (int k = 0; k < C::VI; ++k) {
+    float a = st.acc[k] * alpha;
+    const u32x4 vv = t.v[k];
+    if constexpr (F8) {
+      // 16 tokens: word e holds tokens 4e .. 4e+3
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int t0 = h * 16 + 4 * e + k;
-            const float v0 = (PARTIAL && t0 >= nvalid) ? 0.f : v4[k];
-            a = fmaf(ps[t0], v0, a);
-          }
-        }
-      } else if constexpr (BF16) {
+      for (int e = 0; e < 4; ++e) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(vv[e], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(vv[e], true);
+        const float v4[4] = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t0 = h * 8 + 2 * e;
-          float v0 = bf16lo(vv[e]), v1 = bf16hi(vv[e]);
-          if constexpr (PARTIAL) {
-            v0 = (t0 < nvalid) ? v0 : 0.f;
-            v1 = (t0 + 1 < nvalid) ? v1 : 0.f;
-          }
-          a = fmaf(ps[t0], v0, a);
-          a = fmaf(ps[t0 + 1], v1, a);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t0 = h * 4 + e;
-          float v0 = as_f32(vv[e]);
-          if constexpr (PARTIAL) v0 = (t0 < nvalid) ? v0 : 0.f;
-          a = fmaf(ps[t0], v0, a);
+        for (int j = 0; j < 4; ++j) {
+          const int te = 4 * e + j;
+          const float v0 = (PARTIAL && tb + te >= nvalid) ? 0.f : v4[j];
+          a = fmaf(wt[te], v0, a);
         }
       }
+    } else if constexpr (BF16) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int te = 2 * e;
+        float v0 = bf16lo(vv[e]), v1 = bf16hi(vv[e]);
+        if constexpr (PARTIAL) {
+          v0 = (tb + te < nvalid) ? v0 : 0.f;
+          v1 = (tb + te + 1 < nvalid) ? v1 : 0.f;
+        }
+        a = fmaf(wt[te], v0, a);
+        a = fmaf(wt[te + 1], v1, a);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v0 = as_f32(vv[e]);
+        if constexpr (PARTIAL) v0 = (tb + e < nvalid) ? v0 : 0.f;
+        a = fmaf(wt[e], v0, a);
+      }
     }
-    st.acc[j] = a;
+    st.acc[k] = a;
   }
+}
+
+// Add the LPD partial sums of each dim (lanes l ^ 1, l ^ 2, l ^ 4 within a row).
+template <int LPD>
+__device__ __forceinline__ float dim_sum(float x) {
+  if constexpr (LPD >= 2) x += dpp<kDppQuadXor1>(x);
+  if constexpr (LPD >= 4) x += dpp<kDppQuadXor2>(x);
+  if constexpr (LPD >= 8) x += dpp<kDppRowHalfMirror>(x);
+  return x;
 }
 
 template <bool BF16, int D, int BS, bool F8, int NW>
@@ -228,11 +246,11 @@ __global__ __launch_bounds__(NW * 64) void mha_valu_partial(Params p) {
   const char* kbase = static_cast<const char*>(p.k) + (size_t)g * BS * C::ROWB;
   const char* vbase = static_cast<const char*>(p.v) + (size_t)g * D * BS * C::ES;
 
-  MhaState<C::DPL> st;
+  MhaState<C::VI> st;
   st.m = kNegInf;
   st.l = 0.f;
 #pragma unroll
-  for (int j = 0; j < C::DPL; ++j) st.acc[j] = 0.f;
+  for (int k = 0; k < C::VI; ++k) st.acc[k] = 0.f;
 
   auto issue = [&](MhaTile<BF16, D, BS, F8>& t, int pg) {
     if (pg >= p1) {                                  // past the split: read zeros (L2)
@@ -273,7 +291,10 @@ __global__ __launch_bounds__(NW * 64) void mha_valu_partial(Params p) {
     sm_l[w] = ltot;
   }
 #pragma unroll
-  for (int j = 0; j < C::DPL; ++j) sm_acc[w][j * 64 + lane] = st.acc[j];
+  for (int k = 0; k < C::VI; ++k) {
+    const float a = dim_sum<C::LPD>(st.acc[k]);
+    if (lane % C::LPD == 0) sm_acc[w][k * C::DPI + lane / C::LPD] = a;
+  }
   __syncthreads();
 
   float M = kNegInf;
