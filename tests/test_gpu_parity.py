@@ -101,6 +101,11 @@ SMALL = {
                          head_dim=128, block_size=16, context_lens=[77, 160], num_blocks=30),
     "mha_f32_d64_bs32": dict(kind="mha", dtype="f32", batch=2, num_q_heads=4, num_kv_heads=4,
                              head_dim=64, block_size=32, context_lens=[65, 3], num_blocks=10),
+    # every lanes-per-V-row case of the VALU kernel: bf16 D64 bs32 (4), f32 D128 bs32 (8)
+    "mha_bf16_d64_bs32": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=3, num_kv_heads=3,
+                              head_dim=64, block_size=32, context_lens=[200, 1, 33], num_blocks=20),
+    "mha_f32_d128_bs32": dict(kind="mha", dtype="f32", batch=2, num_q_heads=2, num_kv_heads=2,
+                              head_dim=128, block_size=32, context_lens=[190, 17], num_blocks=12),
     "gqa_f32_g4": dict(kind="mha", dtype="f32", batch=2, num_q_heads=8, num_kv_heads=2,
                        head_dim=64, block_size=16, context_lens=[50, 200], num_blocks=30),
     "gqa_bf16_g4": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=8, num_kv_heads=2,
