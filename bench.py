@@ -39,7 +39,12 @@ DEFAULT_CONFIG = "llama_mha_bf16"
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "decode_attention_paged_amd", "csrc")
 
-KERNEL_OF = {"mha": "pa_mha.hip", "gqa": "pa_gqa.hip", "mla": "pa_mla.hip"}
+# the sources each partial kernel is compiled from (its file and the headers it includes)
+KERNEL_SOURCES = {
+    "mha": ("pa_mha.hip", "pa_device.h", "pa_launch.h", "pa_merge.h"),
+    "gqa": ("pa_gqa.hip", "pa_device.h", "pa_launch.h", "pa_merge.h"),
+    "mla": ("pa_mla.hip", "pa_device.h", "pa_launch.h"),
+}
 
 
 def kernel_family(inp) -> str:
@@ -54,7 +59,7 @@ def kernel_family(inp) -> str:
 
 def kernel_source_hash(family: str) -> str:
     h = hashlib.sha256()
-    for f in (KERNEL_OF[family], "pa_device.h", "pa_launch.h"):
+    for f in KERNEL_SOURCES[family]:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -315,8 +315,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
       store_out<true>(p, row, d, o);
       if (d == 0 && p.lse) p.lse[row] = lse;
     } else {
-      store_coherent(p.o_part + (row * p.S + s) * kD + d, o);
-      if (d == 0) store_coherent(p.lse_part + row * p.S + s, lse);
+      store_partial(p, p.o_part + (row * p.S + s) * kD + d, o);
+      if (d == 0) store_partial(p, p.lse_part + row * p.S + s, lse);
     }
   }
   if (!direct && p.fused) {

@@ -34,6 +34,17 @@ __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// One value of a split partial.  Read back in this launch (the fused merge):
+// a coherent store.  Read by a separate reduction launch: a plain store, made
+// visible by the kernel boundary; the coherent store writes through to memory
+// and measured 2.5-4.5 % slower on the MHA partial kernel.
+__device__ __forceinline__ void store_partial(const Params& p, float* dst, float v) {
+  if (p.fused)
+    store_coherent(dst, v);
+  else
+    *dst = v;
+}
+
 template <bool BF16>
 __device__ __forceinline__ void store_out(const Params& p, size_t row, int d, float o) {
   if constexpr (BF16)

@@ -321,13 +321,13 @@ __global__ __launch_bounds__(NW * 64) void mha_valu_partial(Params p) {
     if (direct)
       store_out<BF16>(p, row, d, o);
     else
-      store_coherent(p.o_part + (row * p.S + s) * D + d, o);
+      store_partial(p, p.o_part + (row * p.S + s) * D + d, o);
   }
   if (threadIdx.x == 0) {
     if (direct) {
       if (p.lse) p.lse[row] = lse;
     } else {
-      store_coherent(p.lse_part + row * p.S + s, lse);
+      store_partial(p, p.lse_part + row * p.S + s, lse);
     }
   }
   if (!direct && p.fused) {
