@@ -1,0 +1,38 @@
+"""Benchmark command line on the CPU: the one-GPU contract and the source hash
+that keys the committed profile counters."""
+import os
+import re
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
+
+
+def test_kernel_sources_cover_every_local_include():
+    """A profile's counters stay valid only while every source its kernel is built from is unchanged."""
+    for family, files in bench.KERNEL_SOURCES.items():
+        main = os.path.join(bench.CSRC, files[0])
+        includes = set(re.findall(r'#include "(pa_[a-z_]+\.h)"', open(main).read()))
+        assert includes <= set(files[1:]), (family, includes - set(files[1:]))
+        assert len(bench.kernel_source_hash(family)) == 16
+
+
+def test_committed_profiles_name_a_known_workload_and_family():
+    from workloads import CONFIG_ORDER, make_config
+    names = [f[len("pmc_"):-len(".md")] for f in os.listdir(bench.PROFILES) if f.startswith("pmc_")]
+    assert names
+    for name in names:
+        assert name in CONFIG_ORDER, name
+        text = open(os.path.join(bench.PROFILES, f"pmc_{name}.md")).read()
+        assert re.search(r"kernel_source_sha256: [0-9a-f]{16}", text), name
+        assert bench.kernel_family(make_config(name, poison=False)) in bench.KERNEL_SOURCES
