@@ -147,10 +147,14 @@ int heuristic_splits(const pa_shape& s, int cus, bool mla) {
       heads_per_wg = 1;
       target_bytes = kSplitBytesValu;
     }
-    // split sizes are measured in bf16 bytes: FP8 caches (half the bytes per
-    // token) get the same tokens per split, which measured better on the
-    // ragged batch (186 against 201 us) and within 3% elsewhere
-    const double page_bytes = (double)s.block_size * (s.head_dim + s.head_dim_v) * (esz < 2 ? 2 : esz);
+    // FP8 caches hold half the bytes per token.  With at least one unit per
+    // CU, splits keep the bf16 token count (the ragged batch: 186 against
+    // 201 us with splits of the same bytes); when the CU count sizes the grid
+    // instead, splits of the same bytes pay each workgroup's fixed cost half
+    // as often (long-context GQA at 32 splits: 44 against 46 us at 64).
+    const bool bf16_geometry = esz < 2 && units >= cus;
+    const double page_bytes =
+        (double)s.block_size * (s.head_dim + s.head_dim_v) * (bf16_geometry ? 2 : esz);
     const double part_bytes = 2.0 * heads_per_wg * (s.head_dim_v + 1) * 4.0;
     int c_min = (int)std::ceil(part_bytes / (0.03 * page_bytes));
     if (c_min < 1) c_min = 1;
