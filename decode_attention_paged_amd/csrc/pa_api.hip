@@ -15,6 +15,7 @@ constexpr int kMaxSplits = 65535;          // grid y limit
 constexpr long kFusedMergeBytes = 4 * 1024;   // largest per-unit partial set merged in-kernel
 constexpr double kSplitBytesValu = 128.0 * 1024.0;   // KV bytes per workgroup, VALU kernel
 constexpr double kSplitBytesMfma = 1024.0 * 1024.0;  // KV bytes per workgroup, MFMA kernel
+constexpr int kMinSplitsLong = 8;                    // splits of the longest sequence (MFMA kernel, full grid)
 constexpr int kMaxQLen = 16;                         // query rows per sequence
 // Longest context: token indices, split ends ((s + 1) * c * bs) and page
 // counts stay in int32 arithmetic inside the kernels.
@@ -159,6 +160,15 @@ int heuristic_splits(const pa_shape& s, int cus, bool mla) {
     int c_min = (int)std::ceil(part_bytes / (0.03 * page_bytes));
     if (c_min < 1) c_min = 1;
     int c = (int)(target_bytes / page_bytes);
+    // A batch with a unit per CU or more runs its workgroups in rounds; the
+    // units differ in length, and workgroups as long as a whole short-batch
+    // sequence leave a tail: the longest sequence gets at least kMinSplitsLong
+    // splits (Llama-style MHA with 4 query rows on the MFMA kernel: 8 splits,
+    // 110 us against 116 at 2; the ragged batch keeps its 16).
+    if (k == Kernel::GqaMfma && units >= cus) {
+      const int c_long = (P + kMinSplitsLong - 1) / kMinSplitsLong;
+      if (c > c_long) c = c_long;
+    }
     if (c < c_min) c = c_min;
     S = (P + c - 1) / c;
     const long s_fill = (cus + units - 1) / units;
