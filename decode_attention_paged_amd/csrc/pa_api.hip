@@ -142,7 +142,9 @@ int heuristic_splits(const pa_shape& s, int cus, bool mla) {
     if (k == Kernel::GqaMfma) {
       units = (long)s.batch * s.num_kv_heads;
       heads_per_wg = s.num_q_heads / s.num_kv_heads * rows_of(s);   // partial rows per workgroup
-      target_bytes = kSplitBytesMfma;
+      // fewer units than CUs: one 8-wave workgroup per CU (gqa_waves) with
+      // twice the bytes
+      target_bytes = units < cus ? 2 * kSplitBytesMfma : kSplitBytesMfma;
     } else {
       units = (long)s.batch * s.num_q_heads;
       heads_per_wg = 1;
@@ -242,6 +244,17 @@ pa::Params make_params(const pa_shape& s, int S, const void* q, const void* k, c
   return p;
 }
 
+// Waves per workgroup of the grouped-query kernel: 8 when the grid holds at
+// most one workgroup per CU (then every CU runs one; measured on the
+// long-context workload at 32 splits: 82.3 us against 84.6 us for 4-wave
+// workgroups at 64 splits, two per CU), else 4 (two workgroups per CU; 8
+// waves measured 6 % slower on the ragged batch).
+int gqa_waves(const pa_shape& s, int S) {
+  const int cus = device_cus();
+  const long wgs = (long)s.batch * s.num_kv_heads * S;
+  return cus > 0 && wgs <= cus ? 8 : 4;
+}
+
 // Whether pa_decode merges in-kernel for this shape and split count.  The
 // fused merge costs every workgroup a device-scope arrival atomic (a round
 // trip it waits for) and leaves the merge to the last workgroup of each unit
@@ -285,6 +298,7 @@ pa_status run_partial(const pa_shape* shape, const void* q, const void* k, const
   // serial tail when they are large.  Above kFusedMergeBytes per unit the
   // separate reduction launch (all units in parallel) is faster.
   p.fused = (fused && fuses(*shape, S, kern)) ? 1 : 0;
+  p.wg_waves = kern == Kernel::GqaMfma ? gqa_waves(*shape, S) : 0;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (kern) {

@@ -8,7 +8,9 @@
 // pairs of pages round-robin (a pair is 32 tokens, the MFMA contraction
 // depth of the value product) and merge their running states in LDS at the
 // end, which yields the split's (o_s, lse_s) of Flash-Decoding's second step
-// (the "flash decoding ++" entry, its three-steps snippet).
+// (the "flash decoding ++" entry, its three-steps snippet).  NW is 4 (two
+// workgroups per CU), or 8 when the grid holds one workgroup per CU: a
+// batch too small to fill the CUs, split so that every CU gets one.
 //
 // Operand layouts (MFMA 16x16x32 bf16: A[i][k] in lane i + 16*(k/8), element
 // k%8; B[k][j] in lane j + 16*(k/8); D[i][j] in lane j + 16*(i/4), reg i%4):
@@ -329,7 +331,14 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
   }
 }
 
-constexpr int kGqaWaves = 4;
+template <int NW>
+void launch_waves(const Params& p, bool fp8kv, hipStream_t st) {
+  dim3 grid(p.Hkv, p.S, p.B);
+  if (fp8kv)
+    hipLaunchKernelGGL((gqa_mfma_partial<NW, true>), grid, dim3(NW * 64), 0, st, p);
+  else
+    hipLaunchKernelGGL((gqa_mfma_partial<NW, false>), grid, dim3(NW * 64), 0, st, p);
+}
 
 }  // namespace
 
@@ -344,11 +353,12 @@ bool gqa_mfma_supported(bool bf16, int D, int Dv, int bs, int G, int ql) {
 }
 
 hipError_t launch_gqa_mfma(const Params& p, bool fp8kv, hipStream_t st) {
-  dim3 grid(p.Hkv, p.S, p.B);
-  if (fp8kv)
-    hipLaunchKernelGGL((gqa_mfma_partial<kGqaWaves, true>), grid, dim3(kGqaWaves * 64), 0, st, p);
+  if (p.wg_waves == 8)
+    launch_waves<8>(p, fp8kv, st);
+  else if (p.wg_waves == 4)
+    launch_waves<4>(p, fp8kv, st);
   else
-    hipLaunchKernelGGL((gqa_mfma_partial<kGqaWaves, false>), grid, dim3(kGqaWaves * 64), 0, st, p);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -27,6 +27,7 @@ struct Params {
   float v_scale;             // FP8 caches: factor of every value (1 otherwise)
   int32_t final_write;       // 1: S == 1, write out/lse directly
   int32_t fused;             // 1: the last workgroup of a unit merges the splits
+  int32_t wg_waves;          // grouped-query kernel: waves per workgroup, 4 or 8
 };
 
 // Each returns hipSuccess or the launch error.  Shapes are validated by the caller.

@@ -139,6 +139,13 @@ SMALL = {
     "mla_bf16_h192": dict(kind="mla", dtype="bf16", batch=2, num_q_heads=192, num_kv_heads=1,
                           head_dim=576, head_dim_v=512, block_size=64, context_lens=[33, 190],
                           num_blocks=10, scale=192 ** -0.5),
+    # 24 x 8 (sequence, KV head) units: grids above one workgroup per CU take the 4-wave
+    # grouped-query workgroups, smaller ones the 8-wave ones
+    "gqa_bf16_g4_b24": dict(kind="mha", dtype="bf16", batch=24, num_q_heads=32, num_kv_heads=8,
+                            head_dim=128, block_size=16,
+                            context_lens=[1, 300, 17, 64, 65, 250, 3, 129, 200, 31, 32, 33,
+                                          280, 90, 7, 160, 161, 15, 16, 100, 45, 222, 2, 199],
+                            num_blocks=400),
     # grouped heads on 32-token pages run on the VALU kernel
     "gqa_bf16_g4_bs32": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=8, num_kv_heads=2,
                              head_dim=128, block_size=32, context_lens=[40, 300], num_blocks=20),
