@@ -112,7 +112,8 @@ int device_cus() {
 // from measurements on MI355X (bf16, 128-dim heads, 16-token pages):
 //  * a split should carry a fixed amount of KV per workgroup: ~128 KiB for
 //    the VALU kernel (one head per workgroup, 4 workgroups per CU), ~1 MiB for
-//    the MFMA kernel (a whole head group, 2 workgroups per CU).  Longer splits
+//    the MFMA kernel (a whole head group, 2 workgroups per CU; 2 MiB when a
+//    batch with fewer units than CUs gets one 8-wave workgroup per CU).  Longer splits
 //    leave a long tail on ragged batches; shorter ones pay each workgroup's
 //    fixed prologue/epilogue more often;
 //  * the grid must still hold at least one workgroup per CU if every sequence
