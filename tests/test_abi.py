@@ -214,10 +214,11 @@ def _splits(lib, mla=False, **kw):
 
 
 def test_split_heuristic_fills_the_gpu(lib):
-    # long context, 8 KV heads, one sequence: must split
+    # long context, 8 KV heads, one sequence: must split, one workgroup per CU
+    # (fewer units than CUs: 8-wave workgroups with 2 MiB splits)
     S = _splits(lib, batch=1, num_q_heads=32, num_kv_heads=8, max_context_len=131072,
                 max_blocks_per_seq=8192, num_blocks=8192)
-    assert 64 <= S <= 8192
+    assert 32 <= S <= 8192
     assert S * 8 >= 256                        # at least one workgroup per CU
     # Llama-style MHA batch of 16 x 32 heads, contexts up to 4096
     S2 = _splits(lib, batch=16, num_q_heads=32, num_kv_heads=32, max_context_len=4096,
