@@ -55,6 +55,16 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 // element lvalue): bit-casting an ext_vector element directly reads element 0.
 __device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 
+// Wait until every vector-memory access this thread issued has completed
+// (s_waitcnt vmcnt(0); gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8]
+// | vmcnt_hi[15:14], the other counters left at their maxima).  The signal
+// fences keep the compiler from moving memory accesses across the wait.
+__device__ __forceinline__ void wait_stores_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---------------------------------------------------------------- bf16
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }

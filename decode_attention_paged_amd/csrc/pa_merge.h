@@ -23,10 +23,10 @@ __device__ __forceinline__ bool split_is_direct(const Params& p, int nsplit) {
 
 // Split partials cross workgroups (and XCDs, whose L2 caches are not coherent
 // with each other) only through device-scope coherent accesses: agent-scope
-// atomic stores and loads (global_store/global_load with sc1).  Together with
-// the barrier's wait for this thread's stores before the counter atomic, this
-// orders partials before the arrival without writing back or invalidating
-// whole L2 caches.
+// atomic stores and loads (global_store/global_load with sc1), which complete
+// at the device-coherent level.  arrive_last orders them before the arrival
+// (each thread waits for its own stores) and after it (the last workgroup
+// acquires before it reads), without writing back whole L2 caches.
 __device__ __forceinline__ void store_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -55,17 +55,26 @@ __device__ __forceinline__ void store_out(const Params& p, size_t row, int d, fl
 
 // Arrive at the unit's counter after this workgroup's partials are written
 // (with store_coherent).  Returns true (in every thread) when this workgroup
-// is the last of the unit's `nsplit` splits.  __syncthreads() waits until every
-// thread's stores have completed before thread 0's counter atomic; the last
-// workgroup reads the partials with load_coherent after the second barrier.
+// is the last of the unit's `nsplit` splits.
+//
+// Release: a barrier alone does not wait for outstanding vector-memory
+// stores, so every thread first waits until its own partial stores have
+// completed (vmcnt(0)); they are coherent stores, so completed means visible
+// to every CU.  Only then does the barrier let thread 0 bump the counter.
+// Acquire: the workgroup that takes the last arrival invalidates its
+// non-coherent cached lines (an agent-scope acquire fence, once per unit)
+// before the barrier that releases its threads to read the partials.
 // The last workgroup resets the counter, leaving the workspace ready for the
 // next call.
 __device__ __forceinline__ bool arrive_last(const Params& p, int unit, int nsplit, int* sm_flag) {
+  wait_stores_done();
   __syncthreads();
   if (threadIdx.x == 0) {
     const int old =
         __hip_atomic_fetch_add(p.counters + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *sm_flag = (old == nsplit - 1) ? 1 : 0;
+    const int last = (old == nsplit - 1) ? 1 : 0;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *sm_flag = last;
   }
   __syncthreads();
   return *sm_flag != 0;

@@ -35,4 +35,4 @@ def test_committed_profiles_name_a_known_workload_and_family():
         assert name in CONFIG_ORDER, name
         text = open(os.path.join(bench.PROFILES, f"pmc_{name}.md")).read()
         assert re.search(r"kernel_source_sha256: [0-9a-f]{16}", text), name
-        assert bench.kernel_family(make_config(name, poison=False)) in bench.KERNEL_SOURCES
+        assert bench.kernel_family(make_config(name, values=False)) in bench.KERNEL_SOURCES

@@ -5,11 +5,15 @@ assignments, the query and the paged key/value (or latent) cache.  It holds
 none of the attention arithmetic, so that the CPU oracle and the HIP path can
 both be fed from it without sharing any of the method.
 
-Every value is drawn as float32 N(0, 1) and, for bf16 workloads, rounded to
-bfloat16 with round-to-nearest-even; bf16 arrays are carried as their uint16
-bit patterns.  Draws come in fixed chunks of ``CHUNK`` values, chunk ``i``
-from the ``i``-th child of ``numpy.random.SeedSequence(seed)``; the result is
-therefore independent of how many threads fill it.
+One generator, ``numpy.random.default_rng(seed)`` (PCG64), draws everything
+in this order: the context lengths, the page assignment (a permutation of
+the pool, whose prefix is handed out sequence by sequence in logical page
+order), q, then K and V (or the latent) in logical token order (page, slot,
+head, dim).  Every value is drawn as float32 N(0, 1) and, for bf16
+workloads, rounded to bfloat16 with round-to-nearest-even; bf16 arrays are
+carried as their uint16 bit patterns.  Large tensors are drawn in sequential
+chunks of ``CHUNK`` values from the same generator, which yields the same
+stream as one draw.
 
 Pool layouts (physical page ``p``):
 
@@ -25,8 +29,6 @@ arrays, row ``i`` holding physical page ``page_ids[i]``); a device pool of
 from __future__ import annotations
 
 import math
-import os
-from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -34,14 +36,6 @@ import numpy as np
 CHUNK = 1 << 22
 BF16_NAN_BITS = 0x7FC0
 FP8_NAN_CODE = 0x7F          # E4M3 NaN (S.1111.111)
-
-
-def _threads() -> int:
-    try:
-        n = len(os.sched_getaffinity(0))
-    except AttributeError:  # pragma: no cover
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -56,10 +50,10 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 class _Draw:
-    """Chunked, thread-count independent N(0,1) stream for one tensor."""
+    """N(0,1) values from the workload's one generator, drawn in sequence."""
 
-    def __init__(self, seed_seq: np.random.SeedSequence):
-        self.seq = seed_seq
+    def __init__(self, rng: np.random.Generator):
+        self.rng = rng
 
     def normal_fp8(self, n: int, scale: float) -> np.ndarray:
         """n N(0,1) values as FP8 E4M3 codes (uint8) of value / scale: rounded to
@@ -72,22 +66,11 @@ class _Draw:
 
     def normal(self, n: int, dtype: str) -> np.ndarray:
         """n values in the workload dtype (float32, or bf16 bits as uint16)."""
-        nchunks = max(1, (n + CHUNK - 1) // CHUNK)
-        children = self.seq.spawn(nchunks)
         out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
-
-        def fill(i: int) -> None:
-            lo, hi = i * CHUNK, min(n, (i + 1) * CHUNK)
-            if hi <= lo:
-                return
-            vals = np.random.default_rng(children[i]).standard_normal(hi - lo, dtype=np.float32)
+        for lo in range(0, n, CHUNK):
+            hi = min(n, lo + CHUNK)
+            vals = self.rng.standard_normal(hi - lo, dtype=np.float32)
             out[lo:hi] = vals if dtype == "f32" else f32_to_bf16_bits(vals)
-
-        if nchunks == 1:
-            fill(0)
-        else:
-            with ThreadPoolExecutor(_threads()) as ex:
-                list(ex.map(fill, range(nchunks)))
         return out
 
 
@@ -206,11 +189,9 @@ def make_paged_inputs(*, name: str = "custom", kind: str = "mha", dtype: str = "
     if kind == "mla":
         num_kv_heads = 1
     head_dim_v = head_dim if head_dim_v is None else head_dim_v
-    root = np.random.SeedSequence(seed)
-    ctl_seq, page_seq, q_seq, k_seq, v_seq = root.spawn(5)
-    rng_ctx = np.random.default_rng(ctl_seq)
+    rng = np.random.default_rng(seed)
     if callable(context_lens):
-        ctx = np.asarray(context_lens(rng_ctx), dtype=np.int64)
+        ctx = np.asarray(context_lens(rng), dtype=np.int64)
     else:
         ctx = np.asarray(context_lens, dtype=np.int64)
     ctx = ctx.reshape(batch).astype(np.int32)
@@ -221,16 +202,16 @@ def make_paged_inputs(*, name: str = "custom", kind: str = "mha", dtype: str = "
         raise ValueError("max_blocks_per_seq too small for the context lengths")
     total = int(n_pages.sum())
     nb = max(1, total) if num_blocks is None else num_blocks
-    bt, page_ids = _assign_pages(np.random.default_rng(page_seq), n_pages, nb, max_blocks)
+    bt, page_ids = _assign_pages(rng, n_pages, nb, max_blocks)
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
 
     dq = head_dim
     if q_len > 1:
-        q = _Draw(q_seq).normal(batch * q_len * num_q_heads * dq, dtype).reshape(
+        q = _Draw(rng).normal(batch * q_len * num_q_heads * dq, dtype).reshape(
             batch, q_len, num_q_heads, dq)
     else:
-        q = _Draw(q_seq).normal(batch * num_q_heads * dq, dtype).reshape(batch, num_q_heads, dq)
+        q = _Draw(rng).normal(batch * num_q_heads * dq, dtype).reshape(batch, num_q_heads, dq)
     inp = PagedDecodeInputs(name=name, kind=kind, dtype=dtype, batch=batch,
                             num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                             head_dim=head_dim, head_dim_v=head_dim_v, block_size=block_size,
@@ -254,7 +235,7 @@ def make_paged_inputs(*, name: str = "custom", kind: str = "mha", dtype: str = "
         off += n
 
     if kind == "mla":
-        c = _Draw(k_seq).normal(total * block_size * dq, dtype).reshape(total, block_size, dq)
+        c = _Draw(rng).normal(total * block_size * dq, dtype).reshape(total, block_size, dq)
         if poison:
             c[tail] = nan
         inp.c_pages = c
@@ -264,18 +245,18 @@ def make_paged_inputs(*, name: str = "custom", kind: str = "mha", dtype: str = "
     # Drawn token-major ([page][slot][head][dim], logical order), then laid out.
     if fp8:
         nan = np.uint8(FP8_NAN_CODE)
-        k = _Draw(k_seq).normal_fp8(total * block_size * hkv * dq, k_scale)
+        k = _Draw(rng).normal_fp8(total * block_size * hkv * dq, k_scale)
     else:
-        k = _Draw(k_seq).normal(total * block_size * hkv * dq, dtype)
+        k = _Draw(rng).normal(total * block_size * hkv * dq, dtype)
     k = k.reshape(total, block_size, hkv, dq)
     if poison:
         k[tail] = nan
     inp.k_pages = np.ascontiguousarray(k.transpose(0, 2, 1, 3))   # [n][Hkv][bs][D]
     del k
     if fp8:
-        v = _Draw(v_seq).normal_fp8(total * block_size * hkv * dv, v_scale)
+        v = _Draw(rng).normal_fp8(total * block_size * hkv * dv, v_scale)
     else:
-        v = _Draw(v_seq).normal(total * block_size * hkv * dv, dtype)
+        v = _Draw(rng).normal(total * block_size * hkv * dv, dtype)
     v = v.reshape(total, block_size, hkv, dv)
     if poison:
         v[tail] = nan
@@ -336,8 +317,9 @@ CONFIGS = {
         meta=dict(desc="MLA latent bf16 over token-index lists: B32, 128 heads, 8192 entries "
                        "per sequence (every entry), bs1, 262144-row pool")),
     # Several query rows per sequence (the last q_len tokens, causal): draft
-    # verification / chunked prefill over the same caches as the decode
-    # workloads above (same seeds for lengths and pages, own query rows).
+    # verification / chunked prefill over caches shaped like the decode
+    # workloads above (same seeds, so the same lengths and pages; the query
+    # rows take more draws, so the K/V values that follow them differ).
     "llama_mha_q4_bf16": dict(
         kind="mha", dtype="bf16", batch=16, num_q_heads=32, num_kv_heads=32, head_dim=128,
         block_size=16, context_lens=_uniform_ctx(1024, 4096, 16), num_blocks=65536,
