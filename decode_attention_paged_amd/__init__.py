@@ -17,6 +17,7 @@ Layouts (see include/pa_decode.h):
 from __future__ import annotations
 
 import ctypes
+import weakref
 
 import torch
 
@@ -25,8 +26,8 @@ from ._lib import PaError, PaShape  # noqa: F401
 
 __all__ = [
     "decode", "decode_mla", "decode_partial", "decode_mla_partial", "reduce",
-    "append_kv", "append_latent", "choose_num_splits", "decode_launches", "workspace_size", "workspace_init", "make_shape", "PaError",
-    "library_path",
+    "append_kv", "append_latent", "choose_num_splits", "decode_launches", "workspace_size",
+    "workspace_init", "make_shape", "PaError", "library_path", "stream_read",
 ]
 
 _DTYPES = {torch.float32: _lib.PA_F32, torch.bfloat16: _lib.PA_BF16}
@@ -167,6 +168,30 @@ def workspace_size(shape: PaShape, num_splits: int = 0, mla: bool = False) -> in
     return int(_lib.load().pa_decode_workspace_size(ctypes.byref(shape), int(num_splits), int(mla)))
 
 
+# Arrival counters of the in-kernel merge: the first 4 bytes per row (R = B x
+# q_len x Hq rows) of a workspace, which must be zero when a pa_decode call
+# that merges in-kernel starts.  Each completed call leaves its own counters
+# zero, but its partials follow its own R counters and may overwrite the
+# counters of a larger R.  For each workspace tensor this binding has used:
+# (weak reference, rows whose counters are known to be zero).
+_WS_ZERO_ROWS = {}
+
+
+def _rows(shape):
+    return shape.batch * max(1, shape.q_len) * shape.num_q_heads
+
+
+def _zero_rows(ws):
+    ent = _WS_ZERO_ROWS.get(id(ws))
+    return ent[1] if ent is not None and ent[0]() is ws else 0
+
+
+def _note_workspace(ws, rows):
+    """Record that a call with `rows` rows used `ws` (counters past them may be overwritten)."""
+    if ws is not None:
+        _WS_ZERO_ROWS[id(ws)] = (weakref.ref(ws), min(rows, _zero_rows(ws)))
+
+
 def _outputs(shape, q, out, lse, workspace, num_splits, mla):
     B, Hq, Dv = shape.batch, shape.num_q_heads, shape.head_dim_v
     rows = (B, Hq) if q.dim() == 3 else (B, q.shape[1], Hq)
@@ -186,6 +211,7 @@ def _outputs(shape, q, out, lse, workspace, num_splits, mla):
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         # zero-filled: the fused reduction's arrival counters must start at 0
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        _WS_ZERO_ROWS[id(workspace)] = (weakref.ref(workspace), _rows(shape))
     return out, (None if lse is False else lse), workspace
 
 
@@ -201,6 +227,12 @@ def decode(q, k_cache, v_cache, block_table, context_lens, *, max_context_len=No
     shape = _mha_shape(q, k_cache, v_cache, block_table, context_lens, max_context_len, scale,
                        k_scale, v_scale)
     out, lse, ws = _outputs(shape, q, out, lse, workspace, num_splits, False)
+    rows = _rows(shape)
+    if (ws is not None and _zero_rows(ws) < rows and workspace_size(shape, num_splits) > 0
+            and decode_launches(shape, num_splits) == 1):
+        # an in-kernel merge over counters not known to be zero: zero them first
+        workspace_init(shape, ws, num_splits, False, stream)
+    _note_workspace(ws, rows)
     st = _lib.load().pa_decode(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                _ptr(block_table), _ptr(context_lens), int(num_splits), _ptr(out),
                                _ptr(lse), _ptr(ws), _nbytes(ws),
@@ -216,6 +248,7 @@ def decode_mla(q, kv_cache, block_table, context_lens, *, max_context_len=None, 
         raise ValueError("MLA needs an explicit scale")
     shape = _mla_shape(q, kv_cache, block_table, context_lens, max_context_len, scale, head_dim_v)
     out, lse, ws = _outputs(shape, q, out, lse, workspace, num_splits, True)
+    _note_workspace(ws, _rows(shape))
     st = _lib.load().pa_decode_mla(ctypes.byref(shape), _ptr(q), _ptr(kv_cache), _ptr(block_table),
                                    _ptr(context_lens), int(num_splits), _ptr(out), _ptr(lse),
                                    _ptr(ws), _nbytes(ws), _stream(stream))
@@ -228,11 +261,14 @@ def workspace_init(shape: PaShape, workspace, num_splits: int = 0, mla: bool = F
     st = _lib.load().pa_workspace_init(ctypes.byref(shape), int(num_splits), int(mla),
                                        _ptr(workspace), _nbytes(workspace), _stream(stream))
     _lib.check(st, "pa_workspace_init")
+    if workspace is not None:
+        _WS_ZERO_ROWS[id(workspace)] = (weakref.ref(workspace), _rows(shape))
 
 
 def decode_partial(shape: PaShape, q, k_cache, v_cache, block_table, context_lens, num_splits,
                    out, lse, workspace, stream=None):
     """Only the per-split partial step (writes out/lse directly when S == 1)."""
+    _note_workspace(workspace, _rows(shape))
     st = _lib.load().pa_decode_partial(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                        _ptr(block_table), _ptr(context_lens), int(num_splits),
                                        _ptr(out), _ptr(lse), _ptr(workspace),
@@ -243,6 +279,7 @@ def decode_partial(shape: PaShape, q, k_cache, v_cache, block_table, context_len
 
 def decode_mla_partial(shape: PaShape, q, kv_cache, block_table, context_lens, num_splits, out,
                        lse, workspace, stream=None):
+    _note_workspace(workspace, _rows(shape))
     st = _lib.load().pa_decode_mla_partial(ctypes.byref(shape), _ptr(q), _ptr(kv_cache),
                                            _ptr(block_table), _ptr(context_lens), int(num_splits),
                                            _ptr(out), _ptr(lse), _ptr(workspace),
@@ -319,3 +356,16 @@ def append_latent(c_new, kv_cache, block_table, context_lens, stream=None):
     st = _lib.load().pa_append_latent(ctypes.byref(shape), _ptr(c_new), _ptr(kv_cache),
                                       _ptr(block_table), _ptr(context_lens), _stream(stream))
     _lib.check(st, "pa_append_latent")
+
+
+def stream_read(src, sink, stream=None):
+    """Measurement helper: stream-read every byte of the device tensor `src`
+    (size a multiple of 16) with the KV gather's load form; `sink` is a
+    one-word device tensor (int32/uint32), written only in a practically
+    impossible case."""
+    _need(src, "src")
+    _need(sink, "sink", device=src.device)
+    if _nbytes(sink) < 4:
+        raise ValueError("sink must hold one 32-bit word")
+    st = _lib.load().pa_stream_read(_ptr(src), _nbytes(src), _ptr(sink), _stream(stream))
+    _lib.check(st, "pa_stream_read")

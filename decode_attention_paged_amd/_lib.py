@@ -58,6 +58,7 @@ SIGNATURES = {
     "pa_reduce": (_I32, [_SH, _P, _I32, _I32, _P, _SZ, _P, _P, _P]),
     "pa_append_kv": (_I32, [_SH, _P, _P, _P, _P, _P, _P, _P]),
     "pa_append_latent": (_I32, [_SH, _P, _P, _P, _P, _P]),
+    "pa_stream_read": (_I32, [_P, _SZ, _P, _P]),
 }
 
 _lib = None

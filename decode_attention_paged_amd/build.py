@@ -9,6 +9,7 @@ decode_attention_paged_amd/libpa_decode.so next to this file.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -33,7 +34,8 @@ COMMON_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
-SOURCES = ["pa_api.hip", "pa_mha.hip", "pa_gqa.hip", "pa_mla.hip", "pa_reduce.hip", "pa_append.hip"]
+SOURCES = ["pa_api.hip", "pa_mha.hip", "pa_gqa.hip", "pa_mla.hip", "pa_reduce.hip", "pa_append.hip",
+           "pa_probe.hip"]
 
 
 def hipcc() -> str:
@@ -47,12 +49,46 @@ def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
-                    if "packed-fp32-ops" not in l and l.strip())
+    lines = [l for l in (r.stdout + r.stderr).splitlines()
+             if "packed-fp32-ops" not in l and l.strip()]
     if r.returncode != 0:
-        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
-    if verbose and out:
-        print(out, flush=True)
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n" + "\n".join(lines))
+    remarks = [l for l in lines if "kernel-resource-usage" in l]
+    other = [l for l in lines if "kernel-resource-usage" not in l]
+    if verbose and other:
+        print("\n".join(other), flush=True)
+    return remarks
+
+
+def resource_usage(remarks):
+    """Per-kernel figures from the compiler's kernel-resource-usage remarks:
+    {kernel: {"VGPRs": n, "AGPRs": n, "ScratchSize": n, "VGPRs Spill": n, ...}}."""
+    usage, name = {}, None
+    for line in remarks:
+        m = re.search(r"remark:\s+Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            usage[name] = {}
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^\]]*\])?: (\d+)", line)
+        if m and name is not None:
+            usage[name][m.group(1).strip()] = int(m.group(2))
+    return usage
+
+
+def check_usage(usage):
+    """Refuse kernels that spill vector registers or use scratch memory.
+
+    The kernels count their own vector-memory waits around asm loads (the
+    latent kernels) and size their register tiles to the register file; a
+    spill adds memory operations the hand-counted waits do not know about,
+    and scratch traffic the bandwidth figures do not account for.
+    """
+    bad = {k: v for k, v in usage.items()
+           if v.get("ScratchSize", 0) > 0 or v.get("VGPRs Spill", 0) > 0}
+    if bad:
+        raise RuntimeError("kernels spill or use scratch: " +
+                           "; ".join(f"{k}: {v}" for k, v in sorted(bad.items())))
 
 
 def build(verbose: bool = False, save_temps: bool = False) -> str:
@@ -63,14 +99,21 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *COMMON_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if save_temps:
             cmd += ["-save-temps=obj"]
-        _run(cmd, verbose)
-        return obj
+        return obj, _run(cmd, verbose)
 
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+        results = list(ex.map(compile_one, SOURCES))
+    objs = [o for o, _ in results]
+    usage = {}
+    for _, remarks in results:
+        usage.update(resource_usage(remarks))
+    if not usage:
+        raise RuntimeError("the compiler reported no kernel resource usage")
+    check_usage(usage)
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)

@@ -16,6 +16,8 @@ constexpr long kFusedMergeBytes = 4 * 1024;   // largest per-unit partial set me
 constexpr double kSplitBytesValu = 128.0 * 1024.0;   // KV bytes per workgroup, VALU kernel
 constexpr double kSplitBytesMfma = 1024.0 * 1024.0;  // KV bytes per workgroup, MFMA kernel
 constexpr int kMinSplitsLong = 8;                    // splits of the longest sequence (MFMA kernel, full grid)
+constexpr double kMinSplitBytesValu = 32.0 * 1024.0;  // fewest KV bytes per workgroup, VALU kernel
+constexpr double kMinSplitBytesMfma = 64.0 * 1024.0;  // fewest KV bytes per workgroup, MFMA kernel
 constexpr int kMaxQLen = 16;                         // query rows per sequence
 // Longest context: token indices, split ends ((s + 1) * c * bs) and page
 // counts stay in int32 arithmetic inside the kernels.
@@ -176,6 +178,15 @@ int heuristic_splits(const pa_shape& s, int cus, bool mla) {
     S = (P + c - 1) / c;
     const long s_fill = (cus + units - 1) / units;
     if (S < s_fill) S = s_fill;
+    // A problem too small to fill the CUs with useful work: filling them
+    // anyway gives workgroups that read a few KiB each and a reduction launch
+    // of the same cost as the work.  No split reads less than a minimum (the
+    // launch is then bound by latency, not by how many CUs it occupies), so
+    // tiny problems use few splits and merge them in-kernel, in one launch.
+    const double unit_bytes = (double)P * s.block_size * (s.head_dim + s.head_dim_v) * esz;
+    const double min_bytes = k == Kernel::GqaMfma ? kMinSplitBytesMfma : kMinSplitBytesValu;
+    const long s_small = (long)(unit_bytes / min_bytes);
+    if (S > s_small) S = s_small;
   }
   if (S > P) S = P;
   if (S > kMaxSplits) S = kMaxSplits;
@@ -197,18 +208,20 @@ int resolve_splits(const pa_shape& s, int32_t num_splits, bool mla) {
   return S;
 }
 
-// Workspace layout (S > 1), R = B * q_len * Hq rows: o_part f32 [R][S][Dv] |
-// lse_part f32 [R][S] | counters i32 [R], each 256-byte aligned.
+// Workspace layout (S > 1), R = B * q_len * Hq rows, each region 256-byte
+// aligned: counters i32 [R] | o_part f32 [R][S][Dv] | lse_part f32 [R][S].
+// The counters come first, at an offset that does not depend on S: calls with
+// the same R find them where the previous call left them (zero), whatever
+// their split counts, and the partials never overwrite them.
 size_t ws_rows(const pa_shape& s) { return (size_t)s.batch * rows_of(s) * s.num_q_heads; }
+size_t ws_counter_bytes(const pa_shape& s) { return align_up(ws_rows(s) * sizeof(int32_t)); }
+size_t ws_opart_offset(const pa_shape& s) { return ws_counter_bytes(s); }
 size_t ws_lse_offset(const pa_shape& s, int S) {
-  return align_up(ws_rows(s) * S * s.head_dim_v * sizeof(float));
-}
-size_t ws_counter_offset(const pa_shape& s, int S) {
-  return ws_lse_offset(s, S) + align_up(ws_rows(s) * S * sizeof(float));
+  return ws_opart_offset(s) + align_up(ws_rows(s) * S * s.head_dim_v * sizeof(float));
 }
 size_t workspace_bytes_for(const pa_shape& s, int S) {
   if (S <= 1) return 0;
-  return ws_counter_offset(s, S) + align_up(ws_rows(s) * sizeof(int32_t));
+  return ws_lse_offset(s, S) + align_up(ws_rows(s) * S * sizeof(float));
 }
 
 pa::Params make_params(const pa_shape& s, int S, const void* q, const void* k, const void* v,
@@ -238,9 +251,10 @@ pa::Params make_params(const pa_shape& s, int S, const void* q, const void* k, c
   p.v_scale = fp8_kv(s) ? s.v_scale : 1.f;
   p.final_write = S == 1 ? 1 : 0;
   if (S > 1) {
-    p.o_part = static_cast<float*>(ws);
-    p.lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) + ws_lse_offset(s, S));
-    p.counters = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + ws_counter_offset(s, S));
+    char* base = static_cast<char*>(ws);
+    p.counters = reinterpret_cast<int32_t*>(base);
+    p.o_part = reinterpret_cast<float*>(base + ws_opart_offset(s));
+    p.lse_part = reinterpret_cast<float*>(base + ws_lse_offset(s, S));
   }
   return p;
 }
@@ -376,7 +390,7 @@ pa_status pa_workspace_init(const pa_shape* shape, int32_t num_splits, int32_t m
   if (S < 1) return PA_ERR_HIP;
   if (S <= 1) return PA_OK;
   if (!workspace || workspace_bytes < workspace_bytes_for(*shape, S)) return PA_ERR_WORKSPACE;
-  int32_t* cnt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ws_counter_offset(*shape, S));
+  int32_t* cnt = static_cast<int32_t*>(workspace);
   const size_t n = ws_rows(*shape);
   return pa::launch_zero_i32(cnt, n, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK
                                                                                     : PA_ERR_HIP;
@@ -486,10 +500,21 @@ pa_status pa_append_latent(const pa_shape* shape, const void* c_new, void* kv_ca
   if (st != PA_OK) return st;
   if (!c_new || !kv_cache || !block_table || !context_lens) return PA_ERR_INVALID;
   const pa_shape& s = *shape;
+  // no latent decode reads FP8 codes: refuse to write caches nothing can read
+  if (s.kv_dtype == PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
   pa::AppendParams a{c_new, nullptr, kv_cache, nullptr, block_table, context_lens,
                      s.batch, 1, s.head_dim, 0, s.block_size, s.max_blocks_per_seq,
                      s.num_blocks};
   const hipError_t e = pa::launch_append(a, cache_esize(s), true, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(src) % 16 != 0)
+    return PA_ERR_INVALID;
+  const hipError_t e =
+      pa::launch_stream_read(src, bytes, sink, device_cus(), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -51,6 +51,10 @@ struct AppendParams {
 // esize: bytes per cache element (4 float32, 2 bfloat16, 1 FP8 code).
 hipError_t launch_append(const AppendParams& a, int esize, bool mla, hipStream_t st);
 
+// Streaming-read probe over `bytes` (a multiple of 16) of device memory.
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int cus,
+                              hipStream_t st);
+
 // Which kernels exist (host-side predicates used by validation and dispatch).
 bool mha_valu_supported(bool bf16, int D, int bs);
 // G query heads per KV head, ql query rows: the kernel's 16 MFMA columns hold

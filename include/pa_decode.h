@@ -141,24 +141,28 @@ int32_t pa_choose_num_splits(const pa_shape* shape, int32_t num_cus, int32_t mla
 int32_t pa_decode_launches(const pa_shape* shape, int32_t num_splits, int32_t mla);
 
 /*
- * Bytes of workspace a call with this shape and split count needs: float32
- * partials o[R][S][head_dim_v], float32 lse[R][S] and int32 arrival counters
- * [R], R = batch * q_len * num_q_heads rows, each 256-byte aligned.  0 when
- * S resolves to 1 (the partial kernel then writes out/lse directly).
- * num_splits <= 0 resolves through the heuristic (which may query the device).
- * Returns 0 on an invalid shape.  Host only.
+ * Bytes of workspace a call with this shape and split count needs: int32
+ * arrival counters [R] at offset 0, then float32 partials o[R][S][head_dim_v]
+ * and float32 lse[R][S], R = batch * q_len * num_q_heads rows, each region
+ * 256-byte aligned.  0 when S resolves to 1 (the partial kernel then writes
+ * out/lse directly).  num_splits <= 0 resolves through the heuristic (which
+ * may query the device).  Returns 0 on an invalid shape.  Host only.
  *
- * The counters must be zero when a pa_decode / pa_decode_mla call starts:
- * zero-fill a new workspace (pa_workspace_init, or any memset to 0) once; every
- * call that completes leaves them zero again.  A workspace that a faulted or
- * aborted call may have left dirty must be re-initialised.
+ * The counters (the first 4*R bytes) must be zero when a pa_decode call that
+ * merges in-kernel starts (pa_decode_launches == 1 with S > 1).  Zero them
+ * once for a new workspace (pa_workspace_init, or any memset to 0).  Every
+ * call that completes leaves its counters zero and writes its partials after
+ * them, so any sequence of calls with the same R keeps them zero, whatever
+ * their split counts.  A call with a smaller R writes partials where a larger
+ * R keeps counters: re-initialise before a call with a larger R than the
+ * previous one, and after a faulted or aborted call.
  */
 size_t pa_decode_workspace_size(const pa_shape* shape, int32_t num_splits, int32_t mla);
 
 /*
- * Zero the counter region of `workspace` for this shape and split count, on
- * `stream` (a fill kernel, safe to capture in a graph).  PA_OK when S resolves
- * to 1 (no workspace needed).  Errors as for pa_decode.
+ * Zero the counter region of `workspace` (its first 4*R bytes) for this shape
+ * and split count, on `stream` (a fill kernel, safe to capture in a graph).
+ * PA_OK when S resolves to 1 (no workspace needed).  Errors as for pa_decode.
  */
 pa_status pa_workspace_init(const pa_shape* shape, int32_t num_splits, int32_t mla,
                             void* workspace, size_t workspace_bytes, void* stream);
@@ -260,11 +264,26 @@ pa_status pa_append_kv(const pa_shape* shape, const void* k_new, const void* v_n
 /*
  * MLA variant: kv_cache[page][slot][:] = c_new[b][:], c_new [batch][head_dim]
  * (the whole latent row: keys and values come from the same memory).
- * num_kv_heads must be 1.  Otherwise as pa_append_kv.
+ * num_kv_heads must be 1; kv_dtype PA_FP8_E4M3 gives PA_ERR_UNSUPPORTED (no
+ * latent decode reads FP8 codes).  Otherwise as pa_append_kv.
  */
 pa_status pa_append_latent(const pa_shape* shape, const void* c_new, void* kv_cache,
                            const int32_t* block_table, const int32_t* context_lens,
                            void* stream);
+
+/*
+ * Measurement helper, not part of the method: read `bytes` of device memory
+ * at `src` with the streaming 128-bit loads the KV gather uses, on `stream`,
+ * so a benchmark can report the read bandwidth this device reaches next to
+ * its published HBM peak (the pages' roofline is the time to read the KV
+ * cache from memory: the "flash decoding ++" entry, its upper-bound snippet).
+ * `sink` is one caller-owned device word, written only in the (practically
+ * impossible) case that the folded data equals a fixed constant, so the reads
+ * cannot be optimised away and nothing is written.  `bytes` must be a
+ * positive multiple of 16 and `src` 16-byte aligned (PA_ERR_INVALID
+ * otherwise); PA_ERR_HIP on a failed launch.
+ */
+pa_status pa_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

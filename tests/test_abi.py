@@ -169,8 +169,8 @@ def test_workspace_checks(lib):
     need = lib.pa_decode_workspace_size(ctypes.byref(s), 4, 0)
     rows = 2 * 8 * 4
     up = lambda x: -(-x // 256) * 256
-    # o partials | lse partials | one arrival counter per (sequence, head)
-    assert need == up(rows * 128 * 4) + up(rows * 4) + up(2 * 8 * 4)
+    # one arrival counter per (sequence, head) | o partials | lse partials
+    assert need == up(2 * 8 * 4) + up(rows * 128 * 4) + up(rows * 4)
     assert decode(lib, s, splits=4, ws=FAKE, ws_bytes=need - 1) == _lib.PA_ERR_WORKSPACE
     # one split needs no workspace
     assert lib.pa_decode_workspace_size(ctypes.byref(s), 1, 0) == 0
@@ -238,6 +238,24 @@ def test_split_heuristic_fills_the_gpu(lib):
     assert _splits(lib, max_context_len=0) == 1
 
 
+def test_split_heuristic_tiny_problem_is_one_launch(lib):
+    """A problem far too small to fill the CUs (1 sequence, 8 heads of 64 dims,
+    512 float32 tokens: 2 MiB) is not cut into CU-filling slivers: no split
+    reads less than 32 KiB, and the few splits merge in-kernel (one launch)."""
+    s = shape(batch=1, num_q_heads=8, num_kv_heads=8, head_dim=64, head_dim_v=64,
+              max_context_len=512, max_blocks_per_seq=32, num_blocks=32, scale=0.125,
+              dtype=_lib.PA_F32)
+    S = lib.pa_choose_num_splits(ctypes.byref(s), 256, 0)
+    unit_bytes = 512 * 64 * 2 * 4                # one head's K and V
+    assert S >= 2 and unit_bytes / S >= 32 * 1024
+    assert lib.pa_decode_launches(ctypes.byref(s), S, 0) == 1
+    # grouped heads: no split reads less than 64 KiB
+    g = shape(batch=1, num_q_heads=32, num_kv_heads=8, max_context_len=1024,
+              max_blocks_per_seq=64, num_blocks=64)
+    Sg = lib.pa_choose_num_splits(ctypes.byref(g), 256, 0)
+    assert 1024 * 128 * 2 * 2 / Sg >= 64 * 1024
+
+
 def test_split_heuristic_invalid_shape(lib):
     s = shape(batch=0)
     assert lib.pa_choose_num_splits(ctypes.byref(s), 256, 0) == 0
@@ -275,6 +293,10 @@ def test_append_null_pointers(lib):
         assert append_latent(lib, ms, **{kw: NULL}) == _lib.PA_ERR_INVALID, kw
     # the latent pool has one KV head
     assert append_latent(lib, shape(num_kv_heads=2, num_q_heads=2)) == _lib.PA_ERR_INVALID
+    # no latent decode reads FP8 codes, so the latent append refuses them
+    assert append_latent(lib, shape(num_q_heads=1, num_kv_heads=1, head_dim=576, head_dim_v=576,
+                                    block_size=64, kv_dtype=_lib.PA_FP8_E4M3)) == \
+        _lib.PA_ERR_UNSUPPORTED
 
 
 def test_append_grid_limits(lib):
@@ -313,3 +335,14 @@ def test_token_index_split_limit(lib):
                            NULL)
     assert st == _lib.PA_ERR_UNSUPPORTED              # ceil(5000 / 2) > 2048
     assert lib.pa_choose_num_splits(ctypes.byref(s), 256, 1) >= 3
+
+
+def test_stream_read_checks(lib):
+    """The streaming-read probe validates before launching."""
+    sink = FAKE
+    assert lib.pa_stream_read(NULL, 1024, sink, NULL) == _lib.PA_ERR_INVALID
+    assert lib.pa_stream_read(FAKE, 1024, NULL, NULL) == _lib.PA_ERR_INVALID
+    assert lib.pa_stream_read(FAKE, 0, sink, NULL) == _lib.PA_ERR_INVALID
+    assert lib.pa_stream_read(FAKE, 1000, sink, NULL) == _lib.PA_ERR_INVALID     # not 16-byte rows
+    assert lib.pa_stream_read(ctypes.c_void_p(0x1008), 1024, sink, NULL) == _lib.PA_ERR_INVALID
+
