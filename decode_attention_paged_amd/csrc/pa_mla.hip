@@ -741,142 +741,170 @@ hipError_t launch_roles(const Params& p, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Wide workgroup: all 128 heads of a (sequence, split) in one workgroup of 8
-// waves, two per SIMD, so every CU streams each latent row of its split once.
-// Wave w scores head block w (16 heads, both token halves of a chunk: S^T
-// 32 x 16, queries in 72 registers) and accumulates O^T for dims 64w ..
-// 64w+63 of all 128 heads (accumulators in 128 registers): 200 of the 256
-// registers a wave has at two waves per SIMD.  Each step scores chunk i and
-// then runs the value product of chunk i - 1.  Every wave issues its
-// share of the chunk loads (4 or 5 of the 36 per chunk).  Softmax bookkeeping
-// is per wave as its heads are its own: reference max fixed per pass, restart
-// on overflow, sums per lane.
-constexpr int kWideNW = 8;
+// Wide workgroup: all 128 heads of a (sequence, split) in one workgroup of 4
+// waves, one per SIMD, so every CU streams each latent row of its split once.
+//
+// One wave per SIMD gives each wave the whole register file (256 VGPRs and
+// 256 AGPRs), which lets the larger MFMA shape v_mfma_f32_32x32x16_bf16 serve
+// both products:
+//   scores  wave w: S^T[32 tokens x 32 heads] = C[32 x 576] Q^T for heads
+//           32w .. 32w+31; the queries stay in 144 VGPRs as B operands, and
+//           each latent row is read from LDS once per 32 heads (4 times per
+//           chunk and workgroup, where 16-head blocks read it 8 times);
+//   values  wave w: O^T[128 dims x 128 heads] += V^T[128 x 32] P^T for dims
+//           128w .. 128w+127; the accumulators fill the 256 AGPRs.
+// Each step scores chunk i and then runs the value product of chunk i - 1;
+// every wave issues 9 of the chunk's 36 direct-to-LDS loads.  Softmax
+// bookkeeping is per wave, as its score heads are its own: reference max
+// fixed per pass, restart on overflow, sums per lane.
+//
+// 32x32 MFMA operand layouts (K = 16: A[i][k] in lane i + 32*(k/8), element
+// k%8; B[k][j] in lane j + 32*(k/8); D[i][j] in lane j + 32*((i/4)%2),
+// register 4*(i/8) + i%4):
+//   score A: token (lane & 31), 16-byte chunk 2*kb + (lane >> 5) of its row;
+//   score D: lane holds head (lane & 31), tokens 8g + 4*(lane >> 5) + r in
+//            register 4g + r;
+//   value A: dim (lane & 31) of an M-block, tokens 8*(lane >> 5) .. +7 of a
+//            16-token k-step (two transposed reads);
+//   value B: the 8 weights of those tokens for head (lane & 31) of a head
+//            block: one 16-byte slot, stored so that the read is linear.
+constexpr int kWideNW = 4;
 constexpr int kWideNH = 128;
-constexpr int kWideDW = kDv / kWideNW;   // 64 value dims per wave
-constexpr int kWideMB = kWideDW / 16;    // 4 M-blocks
-constexpr int kWideNB = kWideNH / 16;    // 8 head blocks
+constexpr int kWideHW = kWideNH / kWideNW;   // 32 score heads per wave
+constexpr int kWideDW = kDv / kWideNW;       // 128 value dims per wave
+constexpr int kWideMB = kWideDW / 32;        // 4 M-blocks of 32 dims
+constexpr int kWideNB = kWideNH / 32;        // 4 head blocks of 32
+constexpr int kWideKS = kDqk / 16;           // 36 score k-steps
+constexpr int kWideLook = 4;                 // score operand reads ahead of their MFMAs
+constexpr int kWidePB = kWideNH * kCT * 2;   // bytes of one probability buffer
+static_assert(kDmaInst % kWideNW == 0, "uniform load share");
 
-struct WideOps {
-  const lds_char* ring;
-  const lds_char* pl;
-  int w, lane;
-  __device__ __forceinline__ const lds_char* slot(int ci) const { return ring + (ci % kRing) * kChunkB; }
-  __device__ __forceinline__ const lds_char* pbuf(int ci) const {
-    return pl + (ci & 1) * (kWideNH * kCT * 2);
-  }
-  // V^T A operand of M-block mb: dims 64w + 16mb + (lane & 15), tokens
-  // 8*quad .. +7, two transposed reads.
-  __device__ __forceinline__ u32x4 va(const lds_char* buf, int mb) const {
-    const int quad = lane >> 4, n = lane & 15;
-    const int bc = (kWideDW * w + mb * 16) * 2 + (n & 3) * 8;   // byte column
-    const int r0 = quad * 8 + (n >> 2), r1 = r0 + 4;
-    const lds_char* lo = buf + r0 * kRowB + (((bc >> 4) ^ row_key(r0)) << 4) + (bc & 15);
-    const lds_char* hi = buf + r1 * kRowB + (((bc >> 4) ^ row_key(r1)) << 4) + (bc & 15);
-    const u32x2 vlo = lds_tr16(lo), vhi = lds_tr16(hi);
-    return u32x4{vlo[0], vlo[1], vhi[0], vhi[1]};
-  }
-  // P^T B operand of head block nb: tokens 8*quad .. +7 of head 16nb + (lane & 15).
-  __device__ __forceinline__ u32x4 pb(const lds_char* pbuf, int nb) const {
-    const int quad = lane >> 4, n = lane & 15;
-    return *(const lds_u32x4*)(pbuf + nb * (16 * kCT * 2) + 16 * (quad * 16 + n));
-  }
-};
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 32x32x16 MFMAs as asm (see the 16x16 forms above for the padding): score
+// accumulators in VGPRs, value accumulators in AGPRs.
+__device__ __forceinline__ void mfma32_v_first(f32x16& d, const u32x4& a, const u32x4& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_v(f32x16& d, const u32x4& a, const u32x4& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_a(f32x16& d, const u32x4& a, const u32x4& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+// Drain before VALU reads the score accumulators (an 8-pass MFMA result).
+__device__ __forceinline__ void drain_scores32(f32x16& s0, f32x16& s1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1));
+}
 
 struct WideState {
-  u32x4 qf[kKSteps];                  // Q^T B operands of head block w
-  f32x4 acc[kWideMB][kWideNB];        // O^T: dims 64w + 16mb .., heads 16nb ..
+  u32x4 qf[kWideKS];                  // Q^T B operands of heads 32w .. 32w+31
+  f32x16 acc[kWideMB][kWideNB];       // O^T: dims 128w + 32mb .., heads 32nb ..
   float m, mtop, l;                   // reference max, largest chunk max (log2), lane's sum
   bool bad;
 };
 
-// Scores of chunk ci for head block w, softmax weights, probabilities to LDS.
-__device__ __forceinline__ void wide_scores(WideState& st, const WideOps& op, int ci, int t0, int t1,
-                                            float cs) {
-  const lds_char* buf = op.slot(ci);
-  const int lane = op.lane, quad = lane >> 4, n = lane & 15;
-  // Row n (and 16 + n), 16-byte chunk kb*4 + quad, stored at chunk (kb*4 + quad) ^ (n & 7).
-  const int xb = (n >> 2) & 1;
-  const int sbase = n * kRowB + 16 * (quad ^ (n & 3));
-  const lds_char* se = buf + sbase + 64 * xb;
-  const lds_char* so = buf + sbase - 64 * xb;
-  auto load_a = [&](int kb, u32x4& x0, u32x4& x1) {
-    const lds_char* rp = ((kb & 1) ? so : se) + 64 * kb;
-    x0 = *(const lds_u32x4*)rp;
-    x1 = *(const lds_u32x4*)(rp + 16 * kRowB);
-  };
-  constexpr int L = 1;
-  u32x4 ab[L + 1][2];
-  f32x4 sa[2];
+// Scores of chunk `buf` for heads 32w .. 32w+31, softmax weights,
+// probabilities to `pbuf`.  tok0: the chunk's first token; t1: the split's end.
+__device__ __forceinline__ void wide_scores(WideState& st, const lds_char* buf, lds_char* pbuf,
+                                            int w, int lane, int tok0, int t1, float cs) {
+  const int r = lane & 31, hsel = lane >> 5;
+  // Chunk c of row r sits at c ^ (r & 7); with c = 2kb + hsel that is byte
+  // 16*(hsel ^ (r & 1)) + 32*((kb & 3) ^ ((r >> 1) & 3)) + 128*(kb >> 2).
+  const lds_char* pr[4];
 #pragma unroll
-  for (int kb = 0; kb < L; ++kb) load_a(kb, ab[kb][0], ab[kb][1]);
+  for (int m4 = 0; m4 < 4; ++m4)
+    pr[m4] = buf + r * kRowB + 16 * (hsel ^ (r & 1)) + 32 * (m4 ^ ((r >> 1) & 3));
+  auto load_a = [&](int kb) { return *(const lds_u32x4*)(pr[kb & 3] + 128 * (kb >> 2)); };
+  constexpr int L = kWideLook;
+  u32x4 ab[L + 1];
 #pragma unroll
-  for (int kb = 0; kb < kKSteps; ++kb) {
-    if (kb + L < kKSteps) load_a(kb + L, ab[(kb + L) % (L + 1)][0], ab[(kb + L) % (L + 1)][1]);
-    if (kb == 0) {
-      mfma_v_first(sa[0], ab[0][0], st.qf[0]);
-      mfma_v_first(sa[1], ab[0][1], st.qf[0]);
-    } else {
-      mfma_v(sa[0], ab[kb % (L + 1)][0], st.qf[kb]);
-      mfma_v(sa[1], ab[kb % (L + 1)][1], st.qf[kb]);
-    }
+  for (int kb = 0; kb < L; ++kb) ab[kb] = load_a(kb);
+  f32x16 s0, s1;
+#pragma unroll
+  for (int kb = 0; kb < kWideKS; ++kb) {
+    // the buffer refilled here was consumed one step earlier
+    if (kb + L < kWideKS) ab[(kb + L) % (L + 1)] = load_a(kb + L);
+    const u32x4 a = ab[kb % (L + 1)];
+    // two accumulator chains (even and odd k-steps) keep dependent MFMAs apart
+    if (kb == 0) mfma32_v_first(s0, a, st.qf[kb]);
+    else if (kb == 1) mfma32_v_first(s1, a, st.qf[kb]);
+    else if (kb & 1) mfma32_v(s1, a, st.qf[kb]);
+    else mfma32_v(s0, a, st.qf[kb]);
   }
-  drain_scores<2>(sa);
-  // lane: tokens quad*4 + j (sa[0]) and 16 + quad*4 + j (sa[1]) of head 16w + n
-  float v[8];
+  drain_scores32(s0, s1);
+  float v[16];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    v[j] = sa[0][j];
-    v[4 + j] = sa[1][j];
-  }
-  const int tb = t0 + ci * kCT + quad * 4;
-  if (tb + 16 + 4 > t1) {                            // only a split's last chunk runs past t1
+  for (int i = 0; i < 16; ++i) v[i] = s0[i] + s1[i];
+  // lane: head 32w + r, tokens tok0 + 8g + 4*hsel + j in v[4g + j]
+  const int tb = tok0 + 4 * hsel;
+  if (tok0 + kCT > t1) {                             // only a split's last chunk runs past t1
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (tb + j >= t1) v[j] = kNegInf;
-      if (tb + 16 + j >= t1) v[4 + j] = kNegInf;
-    }
+    for (int i = 0; i < 16; ++i)
+      if (tb + 8 * (i >> 2) + (i & 3) >= t1) v[i] = kNegInf;
   }
-  float mx = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
-                   fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
-  mx = max_xor32(max_xor16(mx)) * cs;                // log2 units, same in the 4 quads
+  float mx = v[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, v[i]);
+  mx = max_xor32(mx) * cs;                           // log2 units, same in both lane halves
   st.mtop = fmaxf(st.mtop, mx);
   if (st.m == kNegInf) st.m = mx;                    // first chunk of the first pass
   st.bad |= mx > st.m + kHeadroom;
+  float ls = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = fast_exp2(fmaf(v[j], cs, -st.m));
-  st.l += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
-  // head block w, 16-byte slot q*16 + n holds tokens 8q .. 8q+7
-  lds_char* prow = (lds_char*)op.pbuf(ci) + op.w * (16 * kCT * 2) + n * 16;
-  u32x2 p0, p1;
-  p0[0] = pack_bf16(v[0], v[1]);
-  p0[1] = pack_bf16(v[2], v[3]);
-  p1[0] = pack_bf16(v[4], v[5]);
-  p1[1] = pack_bf16(v[6], v[7]);
-  ds_store_b64(prow + 256 * (quad >> 1) + 8 * (quad & 1), p0);
-  ds_store_b64(prow + 256 * (2 + (quad >> 1)) + 8 * (quad & 1), p1);
+  for (int i = 0; i < 16; ++i) {
+    v[i] = fast_exp2(fmaf(v[i], cs, -st.m));
+    ls += v[i];
+  }
+  st.l += ls;
+  // tokens 8g + 4*hsel .. +3 of head 32w + r: 16-byte slot (4w + g)*32 + r
+  // (head block w, k-step g/2, half g%2), bytes 8*hsel .. +7
+  lds_char* pw = pbuf + (4 * w * 32 + r) * 16 + 8 * hsel;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    u32x2 pk;
+    pk[0] = pack_bf16(v[4 * g], v[4 * g + 1]);
+    pk[1] = pack_bf16(v[4 * g + 2], v[4 * g + 3]);
+    ds_store_b64(pw + g * 32 * 16, pk);
+  }
 }
 
-// Value product of chunk ci: dims 64w .. 64w+63 of all 128 heads.
-__device__ __forceinline__ void wide_values(WideState& st, const WideOps& op, int ci) {
-  const lds_char* buf = op.slot(ci);
-  const lds_char* pb = op.pbuf(ci);
-  u32x4 va[kWideMB];
+// V^T A operand of M-block mb (dims 128w + 32mb + (lane & 31)) and k-step kb
+// (tokens 16kb + 8*(lane >> 5) .. +7): two transposed reads, each of a
+// 4-token x 16-dim block per 16 lanes.
+__device__ __forceinline__ u32x4 wide_va(const lds_char* buf, int w, int lane, int mb, int kb) {
+  const int gq = lane >> 4, n = lane & 15;
+  const int bc = (kWideDW * w + 32 * mb + 16 * (gq & 1)) * 2 + (n & 3) * 8;   // byte column
+  const int r0 = 16 * kb + 8 * (gq >> 1) + (n >> 2), r1 = r0 + 4;
+  const lds_char* lo = buf + r0 * kRowB + (((bc >> 4) ^ row_key(r0)) << 4) + (bc & 15);
+  const lds_char* hi = buf + r1 * kRowB + (((bc >> 4) ^ row_key(r1)) << 4) + (bc & 15);
+  const u32x2 vlo = lds_tr16(lo), vhi = lds_tr16(hi);
+  return u32x4{vlo[0], vlo[1], vhi[0], vhi[1]};
+}
+
+// Value product of one chunk: dims 128w .. 128w+127 of all 128 heads.
+__device__ __forceinline__ void wide_values(WideState& st, const lds_char* buf, const lds_char* pbuf,
+                                            int w, int lane) {
 #pragma unroll
-  for (int mb = 0; mb < kWideMB; ++mb) va[mb] = op.va(buf, mb);
-  u32x4 b[2];
-  b[0] = op.pb(pb, 0);
+  for (int kb = 0; kb < 2; ++kb) {
+    u32x4 b[kWideNB];
 #pragma unroll
-  for (int nb = 0; nb < kWideNB; ++nb) {
-    if (nb + 1 < kWideNB) b[(nb + 1) & 1] = op.pb(pb, nb + 1);
+    for (int nb = 0; nb < kWideNB; ++nb)
+      b[nb] = *(const lds_u32x4*)(pbuf + (nb * 4 + kb * 2) * 512 + lane * 16);
+    u32x4 a[2];
+    a[0] = wide_va(buf, w, lane, 0, kb);
 #pragma unroll
-    for (int mb = 0; mb < kWideMB; ++mb) mfma_v(st.acc[mb][nb], va[mb], b[nb & 1]);
+    for (int mb = 0; mb < kWideMB; ++mb) {
+      if (mb + 1 < kWideMB) a[(mb + 1) & 1] = wide_va(buf, w, lane, mb + 1, kb);
+#pragma unroll
+      for (int nb = 0; nb < kWideNB; ++nb) mfma32_a(st.acc[mb][nb], a[mb & 1], b[nb]);
+    }
   }
 }
 
 __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
   __shared__ __attribute__((aligned(16))) char ring_lds[kRing * kChunkB];
-  __shared__ __attribute__((aligned(16))) uint16_t pl_lds[2 * kWideNH * kCT];
+  __shared__ __attribute__((aligned(16))) char pl_lds[2 * kWidePB];
 
   const int HG = p.ql * p.Hq / kWideNH;               // head groups (of query rows too)
   int hg, u;
@@ -888,7 +916,7 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
   const int s = u / p.B;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int quad = lane >> 4, n = lane & 15;
+  const int r = lane & 31, hsel = lane >> 5;
   const int head0 = hg * kWideNH;
   const int ctx = clampi(p.context_lens[b], 0, p.max_ctx);
   const int pages = (ctx + 63) / 64;
@@ -899,21 +927,12 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
   const int p1 = min(pages, s * p.c + p.c);
   const int nchunks = t1 > t0 ? (t1 - t0 + kCT - 1) / kCT : 0;
   const float cs = p.scale_log2;                      // > 0, checked by the host
-  const int nwi = (kDmaInst - w + kWideNW - 1) / kWideNW;   // this wave's loads per chunk
+  constexpr int kNwi = kDmaInst / kWideNW;            // this wave's loads per chunk
 
-  WideState st;
-  const size_t row0 = (size_t)b * p.ql * p.Hq + head0;
-  {
-    const char* qr = static_cast<const char*>(p.q) + (row0 + 16 * w + n) * kRowB;
-#pragma unroll
-    for (int kb = 0; kb < kKSteps; ++kb) st.qf[kb] = ld128(qr + kb * 64 + quad * 16);
-  }
-  st.m = kNegInf;
-  st.mtop = kNegInf;
-
-  const WideOps op{(const lds_char*)ring_lds, (const lds_char*)pl_lds, w, lane};
   lds_char* const ring = (lds_char*)ring_lds;
+  lds_char* const pl = (lds_char*)pl_lds;
   auto slot = [&](int ci) { return ring + (ci % kRing) * kChunkB; };
+  auto pbuf = [&](int ci) { return pl + (ci & 1) * kWidePB; };
   ChunkSource<kWideNW, 64> src;
   src.bt = p.block_table + (size_t)b * p.maxb;
   src.cbase = static_cast<const char*>(p.k);
@@ -923,38 +942,60 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
   src.nblocks = p.nblocks;
   src.w = w;
   src.lane = lane;
-  for (;;) {
+  // Chunks 0 and 1 of every pass are issued even past the split's end (those
+  // loads read the zero block), so the count in flight is known.  The first
+  // pass issues them before the query loads and then waits for everything:
+  // the compiler does not see the direct-to-LDS loads, and a partial wait here
+  // would leave it believing query loads are still in flight inside the loop
+  // (where it would then wait for every chunk load in flight).
+  src.begin(s * p.c);
+  src.issue(slot(0), 0);
+  src.issue(slot(1), 1);
+  WideState st;
+  const size_t row0 = (size_t)b * p.ql * p.Hq + head0;
+  {
+    // B operand of k-step kb: head 32w + r, dims 16kb + 8*hsel .. +7
+    const char* qr = static_cast<const char*>(p.q) + (row0 + kWideHW * w + r) * kRowB + hsel * 16;
+#pragma unroll
+    for (int kb = 0; kb < kWideKS; ++kb) st.qf[kb] = ld128(qr + kb * 32);
+  }
+  wait_vm<0>();
+  st.m = kNegInf;
+  st.mtop = kNegInf;
+  for (bool first = true;; first = false) {
     st.l = 0.f;
 #pragma unroll
     for (int mb = 0; mb < kWideMB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < kWideNB; ++nb) st.acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < kWideNB; ++nb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.acc[mb][nb][i] = 0.f;
+      }
     st.bad = false;
-    src.begin(s * p.c);
-    // Chunks 0 and 1 are issued even past the split's end (those loads read
-    // the zero block), so the count in flight is known here: one wait retires
-    // the query loads (older) and chunk 0.
-    src.issue(slot(0), 0);
-    src.issue(slot(1), 1);
-    wait_vm_dyn(nwi);
+    if (!first) {
+      src.begin(s * p.c);
+      src.issue(slot(0), 0);
+      src.issue(slot(1), 1);
+      wait_vm<kNwi>();                                // chunk 0 (chunk 1 may be in flight)
+    }
     lds_barrier();
     if (nchunks > 0) {
       if (2 < nchunks) src.issue(slot(2), 2);
-      wide_scores(st, op, 0, t0, t1, cs);
+      wide_scores(st, slot(0), pbuf(0), w, lane, t0, t1, cs);
     }
     for (int ci = 1; ci < nchunks; ++ci) {
       // chunk ci has landed (this wave's loads, then, after the barrier,
       // every wave's); the probabilities of ci - 1 are complete; the value
-      // product of ci - 2 is done, so its slot can be refilled
-      if (ci + 1 < nchunks) wait_vm_dyn(nwi); else wait_vm<0>();
+      // product of ci - 2 is done, so its slot and probability buffer are free
+      if (ci + 1 < nchunks) wait_vm<kNwi>(); else wait_vm<0>();
       lds_barrier();
       if (ci + 2 < nchunks) src.issue(slot(ci + 2), ci + 2);
-      wide_scores(st, op, ci, t0, t1, cs);
-      wide_values(st, op, ci - 1);
+      wide_scores(st, slot(ci), pbuf(ci), w, lane, t0 + ci * kCT, t1, cs);
+      wide_values(st, slot(ci - 1), pbuf(ci - 1), w, lane);
     }
     if (nchunks > 0) {
       lds_barrier();                                  // the last chunk's probabilities
-      wide_values(st, op, nchunks - 1);
+      wide_values(st, slot(nchunks - 1), pbuf(nchunks - 1), w, lane);
     }
     // Did any head's chunk max overflow the headroom over its reference max?
     wait_vm<0>();                                     // loads issued past the end of a short split
@@ -977,37 +1018,42 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
   float* stat_m = (float*)ring_lds;
   float* stat_l = stat_m + kWideNH;
   {
-    const float lt = sum_xor32(sum_xor16(st.l));
-    if (quad == 0) {
-      stat_m[16 * w + n] = st.m;
-      stat_l[16 * w + n] = lt;
+    const float lt = st.l + __shfl_xor(st.l, 32, 64);
+    if (hsel == 0) {
+      stat_m[kWideHW * w + r] = st.m;
+      stat_l[kWideHW * w + r] = lt;
     }
   }
   lds_barrier();
 #pragma unroll
   for (int nb = 0; nb < kWideNB; ++nb) {
-    const float mm = stat_m[nb * 16 + n];
-    const float lt = stat_l[nb * 16 + n];
-    const float inv = (mm == kNegInf) ? 0.f : 1.f / lt;
-    const size_t row = row0 + nb * 16 + n;
+    const int h = 32 * nb + r;
+    const float mm = stat_m[h];
+    const float inv = (mm == kNegInf) ? 0.f : 1.f / stat_l[h];
+    const size_t row = row0 + h;
 #pragma unroll
     for (int mb = 0; mb < kWideMB; ++mb) {
-      const int d = kWideDW * w + mb * 16 + quad * 4;
-      if (p.final_write) {
-        u32x2 pk;
-        pk[0] = pack_bf16(st.acc[mb][nb][0] * inv, st.acc[mb][nb][1] * inv);
-        pk[1] = pack_bf16(st.acc[mb][nb][2] * inv, st.acc[mb][nb][3] * inv);
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + row * kDv + d) = pk;
-      } else {
-        f32x4 o;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = st.acc[mb][nb][j] * inv;
-        *reinterpret_cast<f32x4*>(p.o_part + (row * p.S + s) * kDv + d) = o;
+      for (int g = 0; g < 4; ++g) {
+        // dims 128w + 32mb + 8g + 4*hsel .. +3
+        const int d = kWideDW * w + 32 * mb + 8 * g + 4 * hsel;
+        const f32x16& a = st.acc[mb][nb];
+        if (p.final_write) {
+          u32x2 pk;
+          pk[0] = pack_bf16(a[4 * g] * inv, a[4 * g + 1] * inv);
+          pk[1] = pack_bf16(a[4 * g + 2] * inv, a[4 * g + 3] * inv);
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + row * kDv + d) = pk;
+        } else {
+          f32x4 o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = a[4 * g + j] * inv;
+          *reinterpret_cast<f32x4*>(p.o_part + (row * p.S + s) * kDv + d) = o;
+        }
       }
     }
   }
-  if (quad == 0) {
-    const int h = 16 * w + n;
+  if (hsel == 0) {
+    const int h = kWideHW * w + r;
     const float mm = stat_m[h];
     const float lt = stat_l[h];
     const float lse = (mm == kNegInf) ? kNegInf : (mm + fast_log2(lt)) * kLn2;
