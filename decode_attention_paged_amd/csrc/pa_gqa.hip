@@ -50,12 +50,18 @@ struct PairTile {
 // the same one, so a lane loads 16 contiguous dims of its K row at once:
 // k[c][kb2] holds dims (kb2*4 + quad)*16 .. +15, which become the A operands
 // of k-steps 2*kb2 (first 8) and 2*kb2 + 1; the query operands follow the
-// same order.  v[nb] holds the lane's 8 tokens of one dim (8 bytes).
+// same order.
+// A V row of one dim is 16 bytes (16 tokens).  Lane (n, quad) loads whole
+// rows: v[j] holds dim 16*(2j + (quad & 1)) + n, all 16 tokens of page
+// quad / 2.  The value operand needs tokens 8*(quad & 1) .. +7 of dims
+// 16*nb + n for every nb, so lanes l and l ^ 16 (rows quad and quad ^ 1 of
+// the same page) each hold half of what the other needs; widen() trades
+// those halves with v_permlane16_swap.
 constexpr int kRowB8 = kD;              // bytes per FP8 K row
 constexpr int kTile8 = kBS * kRowB8;    // bytes per FP8 (page, head) tile
 struct PairTile8 {
   u32x4 k[2][2];
-  u32x2 v[8];
+  u32x4 v[4];
 };
 
 __device__ __forceinline__ void load_pair(PairTile8& t, const char* ka, const char* kb_,
@@ -68,7 +74,15 @@ __device__ __forceinline__ void load_pair(PairTile8& t, const char* ka, const ch
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) t.k[c][kb2] = ld128_stream(kp + c * 4 * kRowB8 + kb2 * 64);
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) t.v[nb] = ld64_stream(vp + nb * 16 * kBS);
+  for (int j = 0; j < 4; ++j) t.v[j] = ld128_stream(vp + j * 32 * kBS);
+}
+
+// Trade words between lanes l and l ^ 16: odd rows of `a` take the even
+// rows' `b`, even rows of `b` take the odd rows' `a` (v_permlane16_swap).
+__device__ __forceinline__ void swap_rows16(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
 }
 
 // Widen an FP8 pair tile to the bf16 operands consume_pair takes (exact).
@@ -80,8 +94,18 @@ __device__ __forceinline__ void widen(const PairTile8& f, PairTile& t) {
       const u32x4& w = f.k[c][kb >> 1];
       t.k[c][kb] = (kb & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
     }
+  // v[j] of an even row holds dim block 2j (its own tokens 0-7, then the
+  // partner's 8-15); of an odd row, dim block 2j + 1 (the partner's tokens
+  // 0-7, then its own 8-15).  After the swap every lane has its 8 tokens of
+  // both blocks: lo = block 2j, hi = block 2j + 1.
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) t.v[nb] = fp8x8_to_bf16x8(f.v[nb][0], f.v[nb][1]);
+  for (int j = 0; j < 4; ++j) {
+    uint32_t lo0 = f.v[j][0], lo1 = f.v[j][1], hi0 = f.v[j][2], hi1 = f.v[j][3];
+    swap_rows16(lo0, hi0);
+    swap_rows16(lo1, hi1);
+    t.v[2 * j] = fp8x8_to_bf16x8(lo0, lo1);
+    t.v[2 * j + 1] = fp8x8_to_bf16x8(hi0, hi1);
+  }
 }
 
 __device__ __forceinline__ void load_pair(PairTile& t, const char* ka, const char* kb_,
@@ -230,7 +254,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
   const bool ksel = (n >> 3) != 0;
   const int koff = (((n >> 2) & 1) * 8 + (n & 3)) * kR + quad * 16;
   const bool vsel = (quad >> 1) != 0;
-  const int voff = F8 ? n * kBS + (quad & 1) * 8 : n * 32 + (quad & 1) * 16;
+  const int voff = F8 ? (16 * (quad & 1) + n) * kBS : n * 32 + (quad & 1) * 16;
 
   f32x4 acc[8];
 #pragma unroll
