@@ -781,20 +781,23 @@ static_assert(kDmaInst % kWideNW == 0, "uniform load share");
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// 32x32x16 MFMAs as asm (see the 16x16 forms above for the padding): score
-// accumulators in VGPRs, value accumulators in AGPRs.
+// Score MFMAs as asm, so their accumulators stay in VGPRs (see the 16x16
+// forms above for the padding); the drain covers an 8-pass result before
+// VALU reads it.
 __device__ __forceinline__ void mfma32_v_first(f32x16& d, const u32x4& a, const u32x4& b) {
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma32_v(f32x16& d, const u32x4& a, const u32x4& b) {
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void mfma32_a(f32x16& d, const u32x4& a, const u32x4& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
-}
-// Drain before VALU reads the score accumulators (an 8-pass MFMA result).
 __device__ __forceinline__ void drain_scores32(f32x16& s0, f32x16& s1) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1));
+}
+// Value MFMA (accumulators in AGPRs: the compiler places them there, as
+// the VGPRs hold the queries).
+__device__ __forceinline__ void mfma32_a(f32x16& d, const u32x4& a, const u32x4& b) {
+  d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                              __builtin_bit_cast(bf16x8, b), d, 0, 0, 0);
 }
 
 struct WideState {
@@ -804,10 +807,13 @@ struct WideState {
   bool bad;
 };
 
-// Scores of chunk `buf` for heads 32w .. 32w+31, softmax weights,
-// probabilities to `pbuf`.  tok0: the chunk's first token; t1: the split's end.
-__device__ __forceinline__ void wide_scores(WideState& st, const lds_char* buf, lds_char* pbuf,
-                                            int w, int lane, int tok0, int t1, float cs) {
+// Score MFMAs of chunk `buf` for heads 32w .. 32w+31 (S^T, 32 tokens x 32
+// heads, in two accumulator chains: even and odd k-steps).  issue(k) runs
+// before k-step 4k (k < 9): this wave's loads of a later chunk go out between
+// the MFMAs, so the matrix core stays busy while the load path accepts them.
+template <typename Issue>
+__device__ __forceinline__ void wide_score_mfma(const WideState& st, const lds_char* buf, int lane,
+                                                f32x16& s0, f32x16& s1, const Issue& issue) {
   const int r = lane & 31, hsel = lane >> 5;
   // Chunk c of row r sits at c ^ (r & 7); with c = 2kb + hsel that is byte
   // 16*(hsel ^ (r & 1)) + 32*((kb & 3) ^ ((r >> 1) & 3)) + 128*(kb >> 2).
@@ -820,23 +826,30 @@ __device__ __forceinline__ void wide_scores(WideState& st, const lds_char* buf, 
   u32x4 ab[L + 1];
 #pragma unroll
   for (int kb = 0; kb < L; ++kb) ab[kb] = load_a(kb);
-  f32x16 s0, s1;
 #pragma unroll
   for (int kb = 0; kb < kWideKS; ++kb) {
+    if ((kb & 3) == 0 && kb / 4 < kDmaInst / kWideNW) issue(kb / 4);
     // the buffer refilled here was consumed one step earlier
     if (kb + L < kWideKS) ab[(kb + L) % (L + 1)] = load_a(kb + L);
     const u32x4 a = ab[kb % (L + 1)];
-    // two accumulator chains (even and odd k-steps) keep dependent MFMAs apart
     if (kb == 0) mfma32_v_first(s0, a, st.qf[kb]);
     else if (kb == 1) mfma32_v_first(s1, a, st.qf[kb]);
     else if (kb & 1) mfma32_v(s1, a, st.qf[kb]);
     else mfma32_v(s0, a, st.qf[kb]);
   }
   drain_scores32(s0, s1);
-  float v[16];
+}
+
+// Softmax of one chunk, first part: the scores (both accumulator chains
+// added), masked past the split's end t1, and their max per head, with the
+// overflow bookkeeping.  tok0: the chunk's first token.
+__device__ __forceinline__ void wide_scores_max(WideState& st, const f32x16& s0, const f32x16& s1,
+                                                float (&v)[16], int lane, int tok0, int t1,
+                                                float cs) {
+  const int hsel = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = s0[i] + s1[i];
-  // lane: head 32w + r, tokens tok0 + 8g + 4*hsel + j in v[4g + j]
+  // lane: head 32w + (lane & 31), tokens tok0 + 8g + 4*hsel + j in v[4g + j]
   const int tb = tok0 + 4 * hsel;
   if (tok0 + kCT > t1) {                             // only a split's last chunk runs past t1
 #pragma unroll
@@ -850,6 +863,12 @@ __device__ __forceinline__ void wide_scores(WideState& st, const lds_char* buf, 
   st.mtop = fmaxf(st.mtop, mx);
   if (st.m == kNegInf) st.m = mx;                    // first chunk of the first pass
   st.bad |= mx > st.m + kHeadroom;
+}
+
+// Second part: the weights, their sum, and the probabilities to `pbuf`.
+__device__ __forceinline__ void wide_weights(WideState& st, float (&v)[16], lds_char* pbuf, int w,
+                                             int lane, float cs) {
+  const int r = lane & 31, hsel = lane >> 5;
   float ls = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -869,22 +888,37 @@ __device__ __forceinline__ void wide_scores(WideState& st, const lds_char* buf, 
   }
 }
 
-// V^T A operand of M-block mb (dims 128w + 32mb + (lane & 31)) and k-step kb
-// (tokens 16kb + 8*(lane >> 5) .. +7): two transposed reads, each of a
-// 4-token x 16-dim block per 16 lanes.
-__device__ __forceinline__ u32x4 wide_va(const lds_char* buf, int w, int lane, int mb, int kb) {
+// Per-lane LDS byte offsets of the transposed V^T reads, relative to a
+// chunk buffer.  The A operand of M-block mb (dims 128w + 32mb + (lane & 31))
+// and k-step kb (tokens 16kb + 8*(lane >> 5) .. +7) is two reads, rows r0
+// and r0 + 4 (r0 = 16kb + 8*(lane >> 5) + (lane & 15) / 4), each of a
+// 4-token x 16-dim block per 16 lanes.  Its 16-byte chunk index within the
+// row is 16w + 4mb + b2 (b2 in 0..3: dim half and lane), stored at that index
+// XOR (row & 7).  Bit 2 of the index is mb & 1 and rows r0 and r0 + 4 differ
+// in bit 2 of the key, so every read address is one of two bases plus an
+// immediate: 128*(mb >> 1) + 18432*kb (+ 4608 for the second row).
+struct WideVaBase {
+  int even, odd;   // bytes: chunk pattern (b2 ^ key) and (b2 ^ key ^ 4) on row r0
+};
+__device__ __forceinline__ WideVaBase wide_va_base(int w, int lane) {
   const int gq = lane >> 4, n = lane & 15;
-  const int bc = (kWideDW * w + 32 * mb + 16 * (gq & 1)) * 2 + (n & 3) * 8;   // byte column
-  const int r0 = 16 * kb + 8 * (gq >> 1) + (n >> 2), r1 = r0 + 4;
-  const lds_char* lo = buf + r0 * kRowB + (((bc >> 4) ^ row_key(r0)) << 4) + (bc & 15);
-  const lds_char* hi = buf + r1 * kRowB + (((bc >> 4) ^ row_key(r1)) << 4) + (bc & 15);
+  const int r0 = 8 * (gq >> 1) + (n >> 2);           // k-step 0
+  const int bc = 2 * (16 * (gq & 1)) + (n & 3) * 8;  // byte column within the 64-byte M-block
+  const int b2 = bc >> 4, lo = bc & 15;
+  const int row = r0 * kRowB + 16 * 16 * w + lo;
+  return WideVaBase{row + 16 * (b2 ^ row_key(r0)), row + 16 * ((b2 ^ row_key(r0)) ^ 4)};
+}
+__device__ __forceinline__ u32x4 wide_va(const lds_char* buf, const WideVaBase& vb, int mb, int kb) {
+  const int imm = 128 * (mb >> 1) + 16 * kRowB * kb;
+  const lds_char* lo = buf + ((mb & 1) ? vb.odd : vb.even) + imm;
+  const lds_char* hi = buf + ((mb & 1) ? vb.even : vb.odd) + imm + 4 * kRowB;
   const u32x2 vlo = lds_tr16(lo), vhi = lds_tr16(hi);
   return u32x4{vlo[0], vlo[1], vhi[0], vhi[1]};
 }
 
 // Value product of one chunk: dims 128w .. 128w+127 of all 128 heads.
 __device__ __forceinline__ void wide_values(WideState& st, const lds_char* buf, const lds_char* pbuf,
-                                            int w, int lane) {
+                                            const WideVaBase& vb, int lane) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     u32x4 b[kWideNB];
@@ -892,10 +926,10 @@ __device__ __forceinline__ void wide_values(WideState& st, const lds_char* buf, 
     for (int nb = 0; nb < kWideNB; ++nb)
       b[nb] = *(const lds_u32x4*)(pbuf + (nb * 4 + kb * 2) * 512 + lane * 16);
     u32x4 a[2];
-    a[0] = wide_va(buf, w, lane, 0, kb);
+    a[0] = wide_va(buf, vb, 0, kb);
 #pragma unroll
     for (int mb = 0; mb < kWideMB; ++mb) {
-      if (mb + 1 < kWideMB) a[(mb + 1) & 1] = wide_va(buf, w, lane, mb + 1, kb);
+      if (mb + 1 < kWideMB) a[(mb + 1) & 1] = wide_va(buf, vb, mb + 1, kb);
 #pragma unroll
       for (int nb = 0; nb < kWideNB; ++nb) mfma32_a(st.acc[mb][nb], a[mb & 1], b[nb]);
     }
@@ -952,6 +986,7 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
   src.issue(slot(0), 0);
   src.issue(slot(1), 1);
   WideState st;
+  const WideVaBase vb = wide_va_base(w, lane);
   const size_t row0 = (size_t)b * p.ql * p.Hq + head0;
   {
     // B operand of k-step kb: head 32w + r, dims 16kb + 8*hsel .. +7
@@ -980,8 +1015,15 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
     }
     lds_barrier();
     if (nchunks > 0) {
-      if (2 < nchunks) src.issue(slot(2), 2);
-      wide_scores(st, slot(0), pbuf(0), w, lane, t0, t1, cs);
+      const bool more = 2 < nchunks;
+      const auto pre = src.prepare(2);
+      f32x16 s0, s1;
+      wide_score_mfma(st, slot(0), lane, s0, s1, [&](int k) {
+        if (more) src.issue_k(pre, slot(2), k);
+      });
+      float v[16];
+      wide_scores_max(st, s0, s1, v, lane, t0, t1, cs);
+      wide_weights(st, v, pbuf(0), w, lane, cs);
     }
     for (int ci = 1; ci < nchunks; ++ci) {
       // chunk ci has landed (this wave's loads, then, after the barrier,
@@ -989,13 +1031,23 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
       // product of ci - 2 is done, so its slot and probability buffer are free
       if (ci + 1 < nchunks) wait_vm<kNwi>(); else wait_vm<0>();
       lds_barrier();
-      if (ci + 2 < nchunks) src.issue(slot(ci + 2), ci + 2);
-      wide_scores(st, slot(ci), pbuf(ci), w, lane, t0 + ci * kCT, t1, cs);
-      wide_values(st, slot(ci - 1), pbuf(ci - 1), w, lane);
+      // scores of ci (with the loads of ci + 2 between them) and their max,
+      // the value product of ci - 1 (independent of them), then the weights
+      // of ci, which the compiler can interleave with that value product
+      const bool more = ci + 2 < nchunks;
+      const auto pre = src.prepare(ci + 2);
+      f32x16 s0, s1;
+      wide_score_mfma(st, slot(ci), lane, s0, s1, [&](int k) {
+        if (more) src.issue_k(pre, slot(ci + 2), k);
+      });
+      float v[16];
+      wide_scores_max(st, s0, s1, v, lane, t0 + ci * kCT, t1, cs);
+      wide_values(st, slot(ci - 1), pbuf(ci - 1), vb, lane);
+      wide_weights(st, v, pbuf(ci), w, lane, cs);
     }
     if (nchunks > 0) {
       lds_barrier();                                  // the last chunk's probabilities
-      wide_values(st, slot(nchunks - 1), pbuf(nchunks - 1), w, lane);
+      wide_values(st, slot(nchunks - 1), pbuf(nchunks - 1), vb, lane);
     }
     // Did any head's chunk max overflow the headroom over its reference max?
     wait_vm<0>();                                     // loads issued past the end of a short split
@@ -1017,17 +1069,23 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
 
   float* stat_m = (float*)ring_lds;
   float* stat_l = stat_m + kWideNH;
+  // The epilogue derives its lane values afresh (an opaque copy of the lane
+  // id), so the compiler keeps nothing from the prologue alive across the
+  // loop for them.
+  int lane_e = lane;
+  asm volatile("" : "+v"(lane_e));
+  const int re = lane_e & 31, he = lane_e >> 5;
   {
     const float lt = st.l + __shfl_xor(st.l, 32, 64);
-    if (hsel == 0) {
-      stat_m[kWideHW * w + r] = st.m;
-      stat_l[kWideHW * w + r] = lt;
+    if (he == 0) {
+      stat_m[kWideHW * w + re] = st.m;
+      stat_l[kWideHW * w + re] = lt;
     }
   }
   lds_barrier();
 #pragma unroll
   for (int nb = 0; nb < kWideNB; ++nb) {
-    const int h = 32 * nb + r;
+    const int h = 32 * nb + re;
     const float mm = stat_m[h];
     const float inv = (mm == kNegInf) ? 0.f : 1.f / stat_l[h];
     const size_t row = row0 + h;
@@ -1036,7 +1094,7 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         // dims 128w + 32mb + 8g + 4*hsel .. +3
-        const int d = kWideDW * w + 32 * mb + 8 * g + 4 * hsel;
+        const int d = kWideDW * w + 32 * mb + 8 * g + 4 * he;
         const f32x16& a = st.acc[mb][nb];
         if (p.final_write) {
           u32x2 pk;
@@ -1052,8 +1110,8 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
       }
     }
   }
-  if (hsel == 0) {
-    const int h = kWideHW * w + r;
+  if (he == 0) {
+    const int h = kWideHW * w + re;
     const float mm = stat_m[h];
     const float lt = stat_l[h];
     const float lse = (mm == kNegInf) ? kNegInf : (mm + fast_log2(lt)) * kLn2;
