@@ -12,6 +12,7 @@ PA_ERR_INVALID = 1
 PA_ERR_UNSUPPORTED = 2
 PA_ERR_WORKSPACE = 3
 PA_ERR_HIP = 4
+PA_ERR_SCRATCH = 5
 
 PA_F32 = 0
 PA_BF16 = 1
@@ -52,6 +53,7 @@ SIGNATURES = {
     "pa_decode_workspace_size": (_SZ, [_SH, _I32, _I32]),
     "pa_workspace_init": (_I32, [_SH, _I32, _I32, _P, _SZ, _P]),
     "pa_decode": (_I32, [_SH, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
+    "pa_decode_static": (_I32, [_SH, _P, _P, _P, _P, _P, _I32, _P, _P, _P]),
     "pa_decode_mla": (_I32, [_SH, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "pa_decode_partial": (_I32, [_SH, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "pa_decode_mla_partial": (_I32, [_SH, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),

@@ -337,6 +337,36 @@ pa_status run_reduce(const pa_shape* shape, const int32_t* ctx, int S, const voi
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// Partials and arrival counters of pa_decode_static: a file-scope device
+// array (each device holds its own copy until the process ends) in place of
+// a caller's workspace.  In host code `scratch` is only a stand-in symbol;
+// its device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+struct ScratchSlot {
+  void* ptr = nullptr;      // device address of this device's `scratch`
+  size_t zero_rows = 0;     // rows whose arrival counters are known to be zero
+};
+std::mutex g_scratch_mu;
+ScratchSlot g_scratch[kMaxDevices];
+
+// This device's scratch slot, its address looked up on first use.
+ScratchSlot* scratch_slot() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  ScratchSlot* slot = &g_scratch[dev];
+  if (slot->ptr == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return nullptr;
+    slot->ptr = ptr;
+    slot->zero_rows = 0;   // nothing known about the array's contents yet
+  }
+  return slot;
+}
+
 }  // namespace
 
 extern "C" {
@@ -348,6 +378,7 @@ const char* pa_status_string(int32_t status) {
     case PA_ERR_UNSUPPORTED: return "unsupported dtype/head_dim/block_size combination";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_SCRATCH: return "partials exceed the library's static scratch (64 MiB)";
     default: return "unknown status";
   }
 }
@@ -440,6 +471,41 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache, c
                                    &reduce);
   if (st != PA_OK) return st;
   return reduce ? run_reduce(shape, context_lens, S, workspace, out, lse, stream) : PA_OK;
+}
+
+pa_status pa_decode_static(const pa_shape* shape, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* block_table,
+                           const int32_t* context_lens, int32_t num_splits, void* out,
+                           float* lse, void* stream) {
+  const pa_status st = check_shape(shape, false);
+  if (st != PA_OK) return st;
+  if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out) return PA_ERR_INVALID;
+  const int S = resolve_splits(*shape, num_splits, false);
+  if (S < 1) return PA_ERR_HIP;
+  const size_t need = workspace_bytes_for(*shape, S);
+  if (need > kScratchBytes) return PA_ERR_SCRATCH;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  ScratchSlot* slot = scratch_slot();
+  if (slot == nullptr) return PA_ERR_HIP;
+  const size_t rows = ws_rows(*shape);
+  const bool merge_in_kernel = S > 1 && fuses(*shape, S, pick_kernel(*shape, false));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (merge_in_kernel && slot->zero_rows < rows) {
+    // counters a previous call may have covered with partials: zero them
+    // (a fill kernel, safe under graph capture)
+    if (pa::launch_zero_i32(static_cast<int32_t*>(slot->ptr), rows, hs) != hipSuccess)
+      return PA_ERR_HIP;
+    slot->zero_rows = rows;
+  }
+  int S_run = 0;
+  bool reduce = false;
+  const pa_status r = run_partial(shape, q, k_cache, v_cache, block_table, context_lens, S, out,
+                                  lse, slot->ptr, kScratchBytes, stream, false, true, &S_run,
+                                  &reduce);
+  if (r != PA_OK) return r;
+  // this call's partials follow its own counters: those of more rows may be gone
+  if (rows < slot->zero_rows) slot->zero_rows = rows;
+  return reduce ? run_reduce(shape, context_lens, S_run, slot->ptr, out, lse, stream) : PA_OK;
 }
 
 pa_status pa_decode_mla(const pa_shape* shape, const void* q, const void* kv_cache,

@@ -86,7 +86,8 @@ typedef enum pa_status {
   PA_ERR_INVALID = 1,     /* NULL required pointer, non-positive size, inconsistent shape */
   PA_ERR_UNSUPPORTED = 2, /* well-formed but no kernel for this dtype/head_dim/block_size */
   PA_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than pa_decode_workspace_size() */
-  PA_ERR_HIP = 4          /* the HIP runtime reported an error (device query or launch) */
+  PA_ERR_HIP = 4,         /* the HIP runtime reported an error (device query or launch) */
+  PA_ERR_SCRATCH = 5      /* pa_decode_static: partials beyond its 64 MiB static scratch */
 } pa_status;
 
 /* PA_FP8_E4M3 is a cache dtype only (pa_shape.kv_dtype): OCP FP8 E4M3 codes
@@ -189,6 +190,26 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
                     const void* v_cache, const int32_t* block_table,
                     const int32_t* context_lens, int32_t num_splits, void* out,
                     float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same computation, kernels and arguments as pa_decode;
+ * the split partials and arrival counters live in a library-owned 64 MiB
+ * device array (one per device, held until the process ends) instead of a
+ * workspace.  The call allocates nothing.  A shape and split count whose
+ * workspace (pa_decode_workspace_size) exceeds 64 MiB gives PA_ERR_SCRATCH,
+ * with nothing launched.  Counters that an in-kernel merge needs and that an
+ * earlier call may have overwritten are zeroed with a fill kernel on `stream`
+ * first (at most one extra launch, when the row count grows).  Every call on
+ * a device shares that device's array: calls that overlap on one device (other
+ * streams, other host threads without ordering) race and give wrong results;
+ * a faulted call leaves it in an unknown state.
+ */
+pa_status pa_decode_static(const pa_shape* shape, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* block_table,
+                           const int32_t* context_lens, int32_t num_splits, void* out,
+                           float* lse, void* stream);
 
 /*
  * MLA latent decode: every query head attends to one shared latent row per

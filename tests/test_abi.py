@@ -58,7 +58,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         assert _lib.status_string(code)
     assert _lib.status_string(99) == "unknown status"
     assert lib.pa_version() >= 100
@@ -346,3 +346,21 @@ def test_stream_read_checks(lib):
     assert lib.pa_stream_read(FAKE, 1000, sink, NULL) == _lib.PA_ERR_INVALID     # not 16-byte rows
     assert lib.pa_stream_read(ctypes.c_void_p(0x1008), 1024, sink, NULL) == _lib.PA_ERR_INVALID
 
+
+def test_static_entry_point_checks(lib):
+    """pa_decode_static validates like pa_decode and refuses partials beyond its
+    64 MiB array before touching the device."""
+    def static(s, splits, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, ctx=FAKE, out=FAKE)
+        a.update(kw)
+        return lib.pa_decode_static(ctypes.byref(s) if s is not None else None, a["q"], a["k"],
+                                    a["v"], a["bt"], a["ctx"], splits, a["out"], NULL, NULL)
+    assert static(None, 4) == _lib.PA_ERR_INVALID
+    assert static(shape(batch=0), 4) == _lib.PA_ERR_INVALID
+    for kw in ("q", "k", "v", "bt", "ctx", "out"):
+        assert static(shape(), 4, **{kw: NULL}) == _lib.PA_ERR_INVALID, kw
+    big = shape(batch=64, num_q_heads=64, num_kv_heads=8, max_context_len=4096,
+                max_blocks_per_seq=256, num_blocks=20000)
+    assert lib.pa_decode_workspace_size(ctypes.byref(big), 64, 0) > 64 << 20
+    assert static(big, 64) == _lib.PA_ERR_SCRATCH
+    assert "64 MiB" in _lib.status_string(_lib.PA_ERR_SCRATCH)
