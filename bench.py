@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode attn tokens/s + achieved KV-read HBM GB/s (% of MI355X peak), 1 GPU"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
-DEFAULT_CONFIG = "llama_mha_bf16"
+DEFAULT_CONFIG = "ragged_gqa_bf16"   # the largest single-GPU workload
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "decode_attention_paged_amd", "csrc")
 
@@ -65,22 +65,37 @@ def kernel_source_hash(family: str) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, family: str):
-    """HBM bytes per launch from the committed counter summary, if still current.
+def _profile_value(path: str, key: str, family: str):
+    """`key: <number>` from a committed profile summary, if still current.
 
-    The summary (profiles/pmc_<workload>.md) holds lines
-    `kernel_source_sha256: <hash>` and `hbm_bytes_per_launch: <bytes>`; the
-    figure is used only when the hash matches today's kernel sources.
+    The summary holds a line `kernel_source_sha256: <hash>`; its figures are
+    used only when the hash matches today's kernel sources.
     """
-    path = os.path.join(PROFILES, f"pmc_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     mh = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
-    mb = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    mb = re.search(key + r":\s*([0-9.eE+]+)", text)
     if not mh or not mb or mh.group(1) != kernel_source_hash(family):
         return None
     return float(mb.group(1))
+
+
+def load_traffic(workload: str, family: str):
+    """HBM bytes per launch (profiles/pmc_<workload>.md), if still current."""
+    return _profile_value(os.path.join(PROFILES, f"pmc_{workload}.md"), "hbm_bytes_per_launch",
+                          family)
+
+
+def load_mfma_busy(workload: str, family: str):
+    """Fraction of the kernel's CU cycles the matrix cores were busy
+    (profiles/mfma_<workload>.md, from SQ_VALU_MFMA_BUSY_CYCLES), if still current."""
+    return _profile_value(os.path.join(PROFILES, f"mfma_{workload}.md"), "mfma_busy_frac", family)
+
+
+def progress(msg: str) -> None:
+    """One line of progress on stderr (stdout carries only the JSON result)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def parse_args():
@@ -247,6 +262,35 @@ class Case:
         q = lambda f: t[min(len(t) - 1, int(f * len(t)))]
         return q(0.5), q(0.1), q(0.9)
 
+    def roofline(self, partial_ms: float):
+        """The partial kernel against the HBM roofline: algorithmic KV bytes per
+        launch over its average launch duration, and counter-measured traffic."""
+        achieved = self.kv_bytes / (partial_ms * 1e-3) / 1e9
+        traffic = load_traffic(self.name, self.family)
+        rf = {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "traffic_over_algorithmic": None if traffic is None else round(traffic / self.kv_bytes, 4),
+            "kernel": (f"{self.family} split-KV kernel with fused reduction" if self.fused
+                       else f"{self.family} partial kernel (the reduction is a second launch)"),
+            "algorithmic_bytes_per_launch": self.kv_bytes,
+            "avg_launch_ms": round(partial_ms, 5),
+        }
+        if self.mla:
+            tflops = self.flops() / (partial_ms * 1e-3) / 1e12
+            rf["mfma"] = {
+                "achieved_tflops": round(tflops, 1),
+                "peak_tflops": PEAK_BF16_TFLOPS,
+                "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                "flops_per_launch": self.flops(),
+                "busy_frac_counter": load_mfma_busy(self.name, self.family),
+            }
+        return rf
+
     def summary(self, r):
         frac = (self.kv_bytes / (r["partial_ms"] * 1e-3) / 1e9) / PEAK_HBM_GBS
         d = dict(
@@ -268,9 +312,8 @@ class Case:
             med, p10, p90 = r["cold_ms"]
             d["cold_call_ms"] = {"median": round(med, 5), "p10": round(p10, 5), "p90": round(p90, 5)}
             d["cold_kv_gbps"] = round(self.kv_bytes / (med * 1e-3) / 1e9, 1)
-        if self.mla:
-            d["mfma_tflops_partial"] = round(self.flops() / (r["partial_ms"] * 1e-3) / 1e12, 1)
-            d["mfma_frac_of_bf16_peak"] = round(d["mfma_tflops_partial"] / PEAK_BF16_TFLOPS, 4)
+        d["kv_tokens_per_s"] = round(self.tokens / (r["ms_per_step"] * 1e-3), 1)
+        d["roofline"] = self.roofline(r["partial_ms"])
         return d
 
     def free(self):
@@ -279,6 +322,42 @@ class Case:
         self.t.clear()
         del self.ws, self.out, self.lse
         torch.cuda.empty_cache()
+
+
+def stream_reference(nbytes: int = 4 << 30, reps: int = 5):
+    """Measured bandwidth of plain device streams beside the 8 TB/s peak: the
+    library's streaming-read probe over 4 GiB (the KV gather's load form; 16x
+    the 256 MB MALL, so it reads HBM), and a 4 GiB device-to-device copy
+    (reads and writes 4 GiB), timed with HIP events."""
+    import torch
+
+    import decode_attention_paged_amd as pa
+
+    src = torch.ones(nbytes // 4, device="cuda")
+    dst = torch.empty_like(src)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    t_read = timed(lambda: pa.stream_read(src, sink))
+    t_copy = timed(lambda: dst.copy_(src))
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return {"read_gbps": round(nbytes / t_read / 1e9, 1),
+            "copy_gbps": round(2 * nbytes / t_copy / 1e9, 1),
+            "bytes": nbytes,
+            "kind": "pa_stream_read (128-bit non-temporal loads, read only) and torch copy_ "
+                    "(read + write) over 4 GiB, HIP events"}
 
 
 def cpu_baseline(inp, min_s: float = 10.0, max_s: float = 30.0):
@@ -340,7 +419,9 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
 
+    progress(f"{args.config}: drawing inputs")
     main_case = Case(args.config)
+    progress(f"{args.config}: timing {args.steps} steps")
     r = main_case.time(args.steps, args.warmup)
     if not args.only:
         r["cold_ms"] = main_case.cold(min(args.steps, 50))
@@ -355,21 +436,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    traffic = load_traffic(args.config, main_case.family)
-    achieved = main_case.kv_bytes / (r["partial_ms"] * 1e-3) / 1e9
-    roofline = {
-        "bound": "hbm",
-        "achieved": round(achieved, 1),
-        "peak": PEAK_HBM_GBS,
-        "unit": "GB/s",
-        "frac": round(achieved / PEAK_HBM_GBS, 4),
-        "traffic": traffic,
-        "kernel": (f"{main_case.family} split-KV kernel with fused reduction" if main_case.fused
-                   else f"{main_case.family} partial kernel (the reduction is a second launch)"),
-        "algorithmic_bytes_per_launch": main_case.kv_bytes,
-        "avg_launch_ms": round(r["partial_ms"], 5),
-    }
+    roofline = main_case.roofline(r["partial_ms"])
     main_case.free()
+    if not args.only:
+        ref = stream_reference()
+        roofline["measured_stream"] = ref
+        roofline["frac_of_measured_read"] = round(roofline["achieved"] / ref["read_gbps"], 4)
 
     per_config = {}
     if not args.only:
@@ -377,6 +449,7 @@ def main():
             if name == args.config:
                 per_config[name] = main_sum
                 continue
+            progress(f"{name}: drawing inputs and timing")
             c = Case(name)
             rr = c.time(max(20, args.steps // 4), max(5, args.warmup // 2))
             rr["cold_ms"] = c.cold(20)
@@ -386,6 +459,7 @@ def main():
 
     cpu = None
     if not args.only and not args.no_cpu:
+        progress("CPU oracle baseline")
         cpu = cpu_baseline(inp)
 
     line = {
@@ -413,6 +487,7 @@ def main():
             "parallelism": "single GPU",
         },
         "kv_gbps_step": main_sum["kv_gbps_step"],
+        "kv_tokens_per_s": main_sum["kv_tokens_per_s"],
         "cold_call_ms": main_sum.get("cold_call_ms"),
         "kv_frac_of_peak_step": round(main_sum["kv_gbps_step"] / PEAK_HBM_GBS, 4),
         "roofline": roofline,
