@@ -114,6 +114,28 @@ __device__ __forceinline__ void dma16(const void* g, lds_char* wave_base) {
                : "memory");
 }
 
+// The same through a buffer resource: lane L reads record bytes voff .. +15
+// of the resource and writes them to wave_base + 16 L.  A lane whose bytes
+// lie past the resource's record count reads zeros (the buffer range check),
+// so the resource bounds what is read without per-lane selects.  The wave
+// offset operand stays 0 (on gfx950 the direct-to-LDS forms take the whole
+// global offset from voff).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void dma16_buf(const i32x4& rsrc, int voff, lds_char* wave_base) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+               :
+               : "v"(voff), "s"(rsrc), "{m0}"((uint32_t)(uintptr_t)wave_base)
+               : "memory");
+}
+// Raw buffer resource over `bytes` bytes from `base` (stride 0, 32-bit
+// data format: byte-addressed records), held in SGPRs.
+__device__ __forceinline__ i32x4 raw_rsrc(const void* base, int bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)),
+               __builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
+
 // LDS stores that the compiler's wait-count pass cannot see as LDS accesses.
 // It makes every LDS store wait for all direct-to-LDS loads in flight (it
 // cannot tell the ring buffers from the rest of LDS), which would drain the
@@ -800,6 +822,55 @@ __device__ __forceinline__ void mfma32_a(f32x16& d, const u32x4& a, const u32x4&
                                               __builtin_bit_cast(bf16x8, b), d, 0, 0, 0);
 }
 
+// Chunk loads of the wide workgroup.  A chunk is 36 loads of 1 KiB: load
+// j = 9q + r covers 16-byte slots 64r .. 64r + 63 of token rows 8q .. 8q + 7
+// (8 rows of 72 slots), and since the swizzle key repeats every 8 rows, its
+// lanes read the bytes of load r's lanes plus 8 rows (9216 bytes) times q.
+// Wave w issues loads r = 2w and 2w + 1 of every row group q and load r = 8
+// of group w, so it needs the lane offsets of three loads only, computed
+// once; a load is then one add and the buffer load (its chunk's resource
+// bounds it: rows past the split's end read zeros).
+struct WideLoads {
+  int pa, pb, p8;   // lane offsets of loads r = 2w, 2w + 1 and 8 in row group 0
+  int w;
+  __device__ __forceinline__ static int lane_off(int r, int lane) {
+    const int slot = 64 * r + lane;
+    const int t = slot / (kRowB / 16);
+    const int c = (slot % (kRowB / 16)) ^ row_key(t);
+    return t * kRowB + c * 16;
+  }
+  __device__ __forceinline__ void init(int w_, int lane) {
+    w = w_;
+    pa = lane_off(2 * w, lane);
+    pb = lane_off(2 * w + 1, lane);
+    p8 = lane_off(8, lane);
+  }
+  // A fresh definition of the offsets for each chunk, so the compiler does
+  // not hoist all nine sums out of the chunk loop (nine live registers).
+  __device__ __forceinline__ void refresh() { asm volatile("" : "+v"(pa), "+v"(pb), "+v"(p8)); }
+  // Load i (0 .. 8) of this wave's share of a chunk into chunk buffer dst.
+  __device__ __forceinline__ void issue(const i32x4& rsrc, lds_char* dst, int i) const {
+    const int q = i < 8 ? i >> 1 : w;
+    const int r = i < 8 ? 2 * w + (i & 1) : 8;
+    const int lo = i < 8 ? ((i & 1) ? pb : pa) : p8;
+    dma16_buf(rsrc, lo + 8 * kRowB * q, dst + (9 * q + r) * 1024);
+  }
+  __device__ __forceinline__ void issue_all(const i32x4& rsrc, lds_char* dst) const {
+#pragma unroll
+    for (int i = 0; i < 9; ++i) issue(rsrc, dst, i);
+  }
+};
+static_assert(kDmaInst == 36 && kWideNW == 4 && kRowB == 1152, "wide load plan");
+
+// Resource of chunk ci: its rows in the cache, the record count the bytes of
+// the chunk inside the split (0 for a chunk past its end).
+__device__ __forceinline__ i32x4 wide_rsrc(ChunkSource<kWideNW, 64>& src, int ci) {
+  const int tok0 = src.t0 + ci * kCT;
+  if (tok0 >= src.t1) return raw_rsrc(src.cbase, 0);
+  const char* base = src.cbase + (size_t)src.page_of(ci) * (64 * kRowB) + (tok0 % 64) * kRowB;
+  return raw_rsrc(base, min(src.t1 - tok0, kCT) * kRowB);
+}
+
 struct WideState {
   u32x4 qf[kWideKS];                  // Q^T B operands of heads 32w .. 32w+31
   f32x16 acc[kWideMB][kWideNB];       // O^T: dims 128w + 32mb .., heads 32nb ..
@@ -976,15 +1047,17 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
   src.nblocks = p.nblocks;
   src.w = w;
   src.lane = lane;
-  // Chunks 0 and 1 of every pass are issued even past the split's end (those
-  // loads read the zero block), so the count in flight is known.  The first
+  // Every chunk is loaded, also past the split's end (those loads write
+  // zeros), so the count in flight is the same at every step.  The first
   // pass issues them before the query loads and then waits for everything:
   // the compiler does not see the direct-to-LDS loads, and a partial wait here
   // would leave it believing query loads are still in flight inside the loop
   // (where it would then wait for every chunk load in flight).
+  WideLoads ld;
+  ld.init(w, lane);
   src.begin(s * p.c);
-  src.issue(slot(0), 0);
-  src.issue(slot(1), 1);
+  ld.issue_all(wide_rsrc(src, 0), slot(0));
+  ld.issue_all(wide_rsrc(src, 1), slot(1));
   WideState st;
   const WideVaBase vb = wide_va_base(w, lane);
   const size_t row0 = (size_t)b * p.ql * p.Hq + head0;
@@ -1009,18 +1082,16 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
     st.bad = false;
     if (!first) {
       src.begin(s * p.c);
-      src.issue(slot(0), 0);
-      src.issue(slot(1), 1);
+      ld.issue_all(wide_rsrc(src, 0), slot(0));
+      ld.issue_all(wide_rsrc(src, 1), slot(1));
       wait_vm<kNwi>();                                // chunk 0 (chunk 1 may be in flight)
     }
     lds_barrier();
     if (nchunks > 0) {
-      const bool more = 2 < nchunks;
-      const auto pre = src.prepare(2);
+      ld.refresh();
+      const i32x4 rs = wide_rsrc(src, 2);
       f32x16 s0, s1;
-      wide_score_mfma(st, slot(0), lane, s0, s1, [&](int k) {
-        if (more) src.issue_k(pre, slot(2), k);
-      });
+      wide_score_mfma(st, slot(0), lane, s0, s1, [&](int k) { ld.issue(rs, slot(2), k); });
       float v[16];
       wide_scores_max(st, s0, s1, v, lane, t0, t1, cs);
       wide_weights(st, v, pbuf(0), w, lane, cs);
@@ -1029,17 +1100,17 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
       // chunk ci has landed (this wave's loads, then, after the barrier,
       // every wave's); the probabilities of ci - 1 are complete; the value
       // product of ci - 2 is done, so its slot and probability buffer are free
-      if (ci + 1 < nchunks) wait_vm<kNwi>(); else wait_vm<0>();
+      wait_vm<kNwi>();
       lds_barrier();
       // scores of ci (with the loads of ci + 2 between them) and their max,
       // the value product of ci - 1 (independent of them), then the weights
       // of ci, which the compiler can interleave with that value product
-      const bool more = ci + 2 < nchunks;
-      const auto pre = src.prepare(ci + 2);
+      // (chunks past the split's end are loaded too, as zeros: every step
+      // issues the same loads, so the wait counts above hold)
+      ld.refresh();
+      const i32x4 rs = wide_rsrc(src, ci + 2);
       f32x16 s0, s1;
-      wide_score_mfma(st, slot(ci), lane, s0, s1, [&](int k) {
-        if (more) src.issue_k(pre, slot(ci + 2), k);
-      });
+      wide_score_mfma(st, slot(ci), lane, s0, s1, [&](int k) { ld.issue(rs, slot(ci + 2), k); });
       float v[16];
       wide_scores_max(st, s0, s1, v, lane, t0 + ci * kCT, t1, cs);
       wide_values(st, slot(ci - 1), pbuf(ci - 1), vb, lane);
@@ -1050,7 +1121,7 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
       wide_values(st, slot(nchunks - 1), pbuf(nchunks - 1), vb, lane);
     }
     // Did any head's chunk max overflow the headroom over its reference max?
-    wait_vm<0>();                                     // loads issued past the end of a short split
+    wait_vm<0>();                                     // the two chunks loaded past the split's end
     lds_barrier();
     int* votes = (int*)ring_lds;
     if (lane == 0) votes[w] = __builtin_amdgcn_ballot_w64(st.bad) != 0;
