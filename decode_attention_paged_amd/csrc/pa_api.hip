@@ -209,23 +209,33 @@ int resolve_splits(const pa_shape& s, int32_t num_splits, bool mla) {
 }
 
 // Workspace layout (S > 1), R = B * q_len * Hq rows, each region 256-byte
-// aligned: counters i32 [R] | o_part f32 [R][S][Dv] | lse_part f32 [R][S].
+// aligned: counters i32 [R] | o_part [R][S][Dv] | lse_part f32 [R][S].
 // The counters come first, at an offset that does not depend on S: calls with
 // the same R find them where the previous call left them (zero), whatever
 // their split counts, and the partials never overwrite them.
+//
+// o_part is float32, except on the MLA matrix-core path (bf16 latents),
+// whose split outputs are stored as bfloat16: there the partials of 128
+// heads x 512 dims per split are a sixth of the latent bytes a split reads
+// (float32: a quarter), written once and read once by the reduction, and the
+// output they merge into is bfloat16 as well.  The merge weights (lse_part)
+// stay float32 everywhere.
 size_t ws_rows(const pa_shape& s) { return (size_t)s.batch * rows_of(s) * s.num_q_heads; }
+bool part_bf16(const pa_shape& s, bool mla) { return pick_kernel(s, mla) == Kernel::MlaMfma; }
 size_t ws_counter_bytes(const pa_shape& s) { return align_up(ws_rows(s) * sizeof(int32_t)); }
 size_t ws_opart_offset(const pa_shape& s) { return ws_counter_bytes(s); }
-size_t ws_lse_offset(const pa_shape& s, int S) {
-  return ws_opart_offset(s) + align_up(ws_rows(s) * S * s.head_dim_v * sizeof(float));
+size_t ws_lse_offset(const pa_shape& s, int S, bool mla) {
+  const size_t esz = part_bf16(s, mla) ? sizeof(uint16_t) : sizeof(float);
+  return ws_opart_offset(s) + align_up(ws_rows(s) * S * s.head_dim_v * esz);
 }
-size_t workspace_bytes_for(const pa_shape& s, int S) {
+size_t workspace_bytes_for(const pa_shape& s, int S, bool mla) {
   if (S <= 1) return 0;
-  return ws_lse_offset(s, S) + align_up(ws_rows(s) * S * sizeof(float));
+  return ws_lse_offset(s, S, mla) + align_up(ws_rows(s) * S * sizeof(float));
 }
 
-pa::Params make_params(const pa_shape& s, int S, const void* q, const void* k, const void* v,
-                       const int32_t* bt, const int32_t* ctx, void* out, float* lse, void* ws) {
+pa::Params make_params(const pa_shape& s, int S, bool mla, const void* q, const void* k,
+                       const void* v, const int32_t* bt, const int32_t* ctx, void* out, float* lse,
+                       void* ws) {
   pa::Params p{};
   p.q = q;
   p.k = k;
@@ -253,8 +263,11 @@ pa::Params make_params(const pa_shape& s, int S, const void* q, const void* k, c
   if (S > 1) {
     char* base = static_cast<char*>(ws);
     p.counters = reinterpret_cast<int32_t*>(base);
-    p.o_part = reinterpret_cast<float*>(base + ws_opart_offset(s));
-    p.lse_part = reinterpret_cast<float*>(base + ws_lse_offset(s, S));
+    if (part_bf16(s, mla))
+      p.o_part16 = reinterpret_cast<uint16_t*>(base + ws_opart_offset(s));
+    else
+      p.o_part = reinterpret_cast<float*>(base + ws_opart_offset(s));
+    p.lse_part = reinterpret_cast<float*>(base + ws_lse_offset(s, S, mla));
   }
   return p;
 }
@@ -297,17 +310,17 @@ pa_status run_partial(const pa_shape* shape, const void* q, const void* k, const
   // workspace check for an explicit split count needs no device query
   if (num_splits > 0) {
     const int S = resolve_splits(*shape, num_splits, mla);
-    if (S > 1 && (!ws || ws_bytes < workspace_bytes_for(*shape, S))) return PA_ERR_WORKSPACE;
+    if (S > 1 && (!ws || ws_bytes < workspace_bytes_for(*shape, S, mla))) return PA_ERR_WORKSPACE;
   }
   const int S = resolve_splits(*shape, num_splits, mla);
   if (S < 1) return PA_ERR_HIP;
-  if (S > 1 && (!ws || ws_bytes < workspace_bytes_for(*shape, S))) return PA_ERR_WORKSPACE;
+  if (S > 1 && (!ws || ws_bytes < workspace_bytes_for(*shape, S, mla))) return PA_ERR_WORKSPACE;
   const Kernel kern = pick_kernel(*shape, mla);
   if (kern == Kernel::MlaMfma) {
     const int P = max_pages(*shape);
     if ((P + S - 1) / S > pa::mla_max_split_tokens(shape->block_size)) return PA_ERR_UNSUPPORTED;
   }
-  pa::Params p = make_params(*shape, S, q, k, mla ? k : v, bt, ctx, out, lse, ws);
+  pa::Params p = make_params(*shape, S, mla, q, k, mla ? k : v, bt, ctx, out, lse, ws);
   // The fused merge runs in the last workgroup of each unit, after every
   // other split of the unit: cheap when the unit's partials are small, a
   // serial tail when they are large.  Above kFusedMergeBytes per unit the
@@ -328,11 +341,11 @@ pa_status run_partial(const pa_shape* shape, const void* q, const void* k, const
   return PA_OK;
 }
 
-pa_status run_reduce(const pa_shape* shape, const int32_t* ctx, int S, const void* ws, void* out,
-                     float* lse, void* stream) {
+pa_status run_reduce(const pa_shape* shape, const int32_t* ctx, int S, bool mla, const void* ws,
+                     void* out, float* lse, void* stream) {
   if (S <= 1) return PA_OK;
-  const pa::Params p = make_params(*shape, S, nullptr, nullptr, nullptr, nullptr, ctx, out, lse,
-                                   const_cast<void*>(ws));
+  const pa::Params p = make_params(*shape, S, mla, nullptr, nullptr, nullptr, nullptr, ctx, out,
+                                   lse, const_cast<void*>(ws));
   const hipError_t e = pa::launch_reduce(p, shape->dtype == PA_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -405,7 +418,7 @@ size_t pa_decode_workspace_size(const pa_shape* shape, int32_t num_splits, int32
   if (check_shape(shape, mla != 0) != PA_OK) return 0;
   const int S = resolve_splits(*shape, num_splits, mla != 0);
   if (S < 1) return 0;
-  return workspace_bytes_for(*shape, S);
+  return workspace_bytes_for(*shape, S, mla != 0);
 }
 
 pa_status pa_workspace_init(const pa_shape* shape, int32_t num_splits, int32_t mla,
@@ -415,12 +428,14 @@ pa_status pa_workspace_init(const pa_shape* shape, int32_t num_splits, int32_t m
   if (num_splits > 0) {
     const int S = resolve_splits(*shape, num_splits, mla != 0);
     if (S <= 1) return PA_OK;
-    if (!workspace || workspace_bytes < workspace_bytes_for(*shape, S)) return PA_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < workspace_bytes_for(*shape, S, mla != 0))
+      return PA_ERR_WORKSPACE;
   }
   const int S = resolve_splits(*shape, num_splits, mla != 0);
   if (S < 1) return PA_ERR_HIP;
   if (S <= 1) return PA_OK;
-  if (!workspace || workspace_bytes < workspace_bytes_for(*shape, S)) return PA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < workspace_bytes_for(*shape, S, mla != 0))
+    return PA_ERR_WORKSPACE;
   int32_t* cnt = static_cast<int32_t*>(workspace);
   const size_t n = ws_rows(*shape);
   return pa::launch_zero_i32(cnt, n, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK
@@ -452,13 +467,15 @@ pa_status pa_reduce(const pa_shape* shape, const int32_t* context_lens, int32_t 
   if (num_splits > 0) {
     const int S = resolve_splits(*shape, num_splits, mla != 0);
     if (S <= 1) return PA_OK;
-    if (!workspace || workspace_bytes < workspace_bytes_for(*shape, S)) return PA_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < workspace_bytes_for(*shape, S, mla != 0))
+      return PA_ERR_WORKSPACE;
   }
   const int S = resolve_splits(*shape, num_splits, mla != 0);
   if (S < 1) return PA_ERR_HIP;
   if (S <= 1) return PA_OK;
-  if (!workspace || workspace_bytes < workspace_bytes_for(*shape, S)) return PA_ERR_WORKSPACE;
-  return run_reduce(shape, context_lens, S, workspace, out, lse, stream);
+  if (!workspace || workspace_bytes < workspace_bytes_for(*shape, S, mla != 0))
+    return PA_ERR_WORKSPACE;
+  return run_reduce(shape, context_lens, S, mla != 0, workspace, out, lse, stream);
 }
 
 pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache, const void* v_cache,
@@ -470,7 +487,7 @@ pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache, c
                                    out, lse, workspace, workspace_bytes, stream, false, true, &S,
                                    &reduce);
   if (st != PA_OK) return st;
-  return reduce ? run_reduce(shape, context_lens, S, workspace, out, lse, stream) : PA_OK;
+  return reduce ? run_reduce(shape, context_lens, S, false, workspace, out, lse, stream) : PA_OK;
 }
 
 pa_status pa_decode_static(const pa_shape* shape, const void* q, const void* k_cache,
@@ -482,7 +499,7 @@ pa_status pa_decode_static(const pa_shape* shape, const void* q, const void* k_c
   if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out) return PA_ERR_INVALID;
   const int S = resolve_splits(*shape, num_splits, false);
   if (S < 1) return PA_ERR_HIP;
-  const size_t need = workspace_bytes_for(*shape, S);
+  const size_t need = workspace_bytes_for(*shape, S, false);
   if (need > kScratchBytes) return PA_ERR_SCRATCH;
   std::lock_guard<std::mutex> lk(g_scratch_mu);
   ScratchSlot* slot = scratch_slot();
@@ -505,7 +522,7 @@ pa_status pa_decode_static(const pa_shape* shape, const void* q, const void* k_c
   if (r != PA_OK) return r;
   // this call's partials follow its own counters: those of more rows may be gone
   if (rows < slot->zero_rows) slot->zero_rows = rows;
-  return reduce ? run_reduce(shape, context_lens, S_run, slot->ptr, out, lse, stream) : PA_OK;
+  return reduce ? run_reduce(shape, context_lens, S_run, false, slot->ptr, out, lse, stream) : PA_OK;
 }
 
 pa_status pa_decode_mla(const pa_shape* shape, const void* q, const void* kv_cache,
@@ -518,7 +535,7 @@ pa_status pa_decode_mla(const pa_shape* shape, const void* q, const void* kv_cac
                                    num_splits, out, lse, workspace, workspace_bytes, stream, true,
                                    true, &S, &reduce);
   if (st != PA_OK) return st;
-  return reduce ? run_reduce(shape, context_lens, S, workspace, out, lse, stream) : PA_OK;
+  return reduce ? run_reduce(shape, context_lens, S, true, workspace, out, lse, stream) : PA_OK;
 }
 
 

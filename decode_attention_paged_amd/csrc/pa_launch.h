@@ -16,7 +16,8 @@ struct Params {
   const int32_t* context_lens; // [B]
   void* out;                 // [B][ql][Hq][Dv] dtype
   float* lse;                // [B][ql][Hq] or nullptr
-  float* o_part;             // [B][ql][Hq][S][Dv] (S > 1)
+  float* o_part;             // [B][ql][Hq][S][Dv] float32 (S > 1), or null when o_part16 is set
+  uint16_t* o_part16;        // the same layout in bfloat16 (S > 1, MLA matrix-core path), else null
   float* lse_part;           // [B][ql][Hq][S]     (S > 1)
   int32_t* counters;         // [B][Hq] arrival counters of the fused reduction (S > 1, ql == 1)
   int32_t B, Hq, Hkv, D, Dv, bs, maxb, nblocks, max_ctx;

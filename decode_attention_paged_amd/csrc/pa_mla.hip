@@ -15,7 +15,8 @@
 // value product through LDS.  This is Flash-Decoding's attention of the query
 // with one block of keys and values plus the block's log-sum-exp (the
 // "flash decoding ++" entry, its three-steps snippet, second step); the
-// split's (o_s, lse_s) go to the workspace for the reduction.
+// split's (o_s, lse_s) go to the workspace for the reduction, o_s in
+// bfloat16 (the output's type), lse_s in float32.
 //
 // Two workgroup shapes, both with two waves per SIMD (at most 256 registers
 // a wave):
@@ -721,17 +722,13 @@ __global__ __launch_bounds__((RoleCfg<HH, HBW>::NW * 64)) void mla_roles_partial
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
         const int d = C::DW * r.v + mb * 16 + quad * 4;
-        if (p.final_write) {
-          u32x2 pk;
-          pk[0] = pack_bf16(r.acc[mb][nb][0] * inv, r.acc[mb][nb][1] * inv);
-          pk[1] = pack_bf16(r.acc[mb][nb][2] * inv, r.acc[mb][nb][3] * inv);
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + row * kDv + d) = pk;
-        } else {
-          f32x4 o;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = r.acc[mb][nb][j] * inv;
-          *reinterpret_cast<f32x4*>(p.o_part + (row * p.S + s) * kDv + d) = o;
-        }
+        // the output, or this split's partial (bfloat16 either way)
+        uint16_t* dst = p.final_write ? static_cast<uint16_t*>(p.out) + row * kDv + d
+                                      : p.o_part16 + (row * p.S + s) * kDv + d;
+        u32x2 pk;
+        pk[0] = pack_bf16(r.acc[mb][nb][0] * inv, r.acc[mb][nb][1] * inv);
+        pk[1] = pack_bf16(r.acc[mb][nb][2] * inv, r.acc[mb][nb][3] * inv);
+        *reinterpret_cast<u32x2*>(dst) = pk;
       }
     }
     if (r.v == 0 && lane < C::NH) {
@@ -800,6 +797,10 @@ constexpr int kWideKS = kDqk / 16;           // 36 score k-steps
 constexpr int kWideLook = 4;                 // score operand reads ahead of their MFMAs
 constexpr int kWidePB = kWideNH * kCT * 2;   // bytes of one probability buffer
 static_assert(kDmaInst % kWideNW == 0, "uniform load share");
+constexpr int kWideOutRowB = 2 * kDv + 16;   // staged output row (bytes), padded against bank conflicts
+static_assert(kWideNH * kWideOutRowB <= kRing * kChunkB, "output tile fits the ring");
+static_assert(2 * kWideNH * 4 <= 2 * kWidePB, "statistics fit the probability buffers");
+static_assert(kDv == 64 * 8, "one 16-byte store per lane covers an output row");
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -1138,7 +1139,12 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
   // the accumulators are read by VALU below: cover the last MFMA's latency
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
-  float* stat_m = (float*)ring_lds;
+  // Per-head statistics go to the probability buffers (free now); the
+  // normalised outputs of all 128 heads are staged in the ring as bfloat16
+  // rows and then written with contiguous 16-byte stores, one 1 KiB row per
+  // store instruction.  Written from the accumulators directly, every store
+  // instruction would scatter 16-byte pieces over 32 rows.
+  float* stat_m = (float*)pl_lds;
   float* stat_l = stat_m + kWideNH;
   // The epilogue derives its lane values afresh (an opaque copy of the lane
   // id), so the compiler keeps nothing from the prologue alive across the
@@ -1154,31 +1160,42 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
     }
   }
   lds_barrier();
+  char* const tile = ring_lds;
 #pragma unroll
   for (int nb = 0; nb < kWideNB; ++nb) {
     const int h = 32 * nb + re;
     const float mm = stat_m[h];
     const float inv = (mm == kNegInf) ? 0.f : 1.f / stat_l[h];
-    const size_t row = row0 + h;
 #pragma unroll
     for (int mb = 0; mb < kWideMB; ++mb) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        // dims 128w + 32mb + 8g + 4*hsel .. +3
+        // dims 128w + 32mb + 8g + 4*hsel .. +3 of head h
         const int d = kWideDW * w + 32 * mb + 8 * g + 4 * he;
         const f32x16& a = st.acc[mb][nb];
-        if (p.final_write) {
-          u32x2 pk;
-          pk[0] = pack_bf16(a[4 * g] * inv, a[4 * g + 1] * inv);
-          pk[1] = pack_bf16(a[4 * g + 2] * inv, a[4 * g + 3] * inv);
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + row * kDv + d) = pk;
-        } else {
-          f32x4 o;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = a[4 * g + j] * inv;
-          *reinterpret_cast<f32x4*>(p.o_part + (row * p.S + s) * kDv + d) = o;
-        }
+        u32x2 pk;
+        pk[0] = pack_bf16(a[4 * g] * inv, a[4 * g + 1] * inv);
+        pk[1] = pack_bf16(a[4 * g + 2] * inv, a[4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(tile + h * kWideOutRowB + 2 * d) = pk;
       }
+    }
+  }
+  lds_barrier();
+  // wave w writes the rows of heads 32w .. 32w+31: the output, or this
+  // split's partial (bfloat16 either way)
+#pragma unroll
+  for (int i = 0; i < kWideHW; i += 8) {
+    u32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = *reinterpret_cast<const u32x4*>(tile + (kWideHW * w + i + j) * kWideOutRowB +
+                                             16 * lane_e);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const size_t row = row0 + kWideHW * w + i + j;
+      uint16_t* dst = p.final_write ? static_cast<uint16_t*>(p.out) + row * kDv
+                                    : p.o_part16 + (row * p.S + s) * kDv;
+      *reinterpret_cast<u32x4*>(dst + 8 * lane_e) = v[j];
     }
   }
   if (he == 0) {

@@ -143,9 +143,10 @@ int32_t pa_decode_launches(const pa_shape* shape, int32_t num_splits, int32_t ml
 
 /*
  * Bytes of workspace a call with this shape and split count needs: int32
- * arrival counters [R] at offset 0, then float32 partials o[R][S][head_dim_v]
- * and float32 lse[R][S], R = batch * q_len * num_q_heads rows, each region
- * 256-byte aligned.  0 when S resolves to 1 (the partial kernel then writes
+ * arrival counters [R] at offset 0, then partials o[R][S][head_dim_v]
+ * (float32; bfloat16 for MLA, whose output is bfloat16 too) and float32
+ * lse[R][S], R = batch * q_len * num_q_heads rows, each region 256-byte
+ * aligned.  0 when S resolves to 1 (the partial kernel then writes
  * out/lse directly).  num_splits <= 0 resolves through the heuristic (which
  * may query the device).  Returns 0 on an invalid shape.  Host only.
  *

@@ -176,6 +176,16 @@ def test_workspace_checks(lib):
     assert lib.pa_decode_workspace_size(ctypes.byref(s), 1, 0) == 0
 
 
+def test_mla_workspace_layout(lib):
+    """MLA partials are bfloat16: counters | o partials (2 bytes each) | float32 lse."""
+    s = shape(num_q_heads=128, num_kv_heads=1, head_dim=576, head_dim_v=512, block_size=64,
+              max_context_len=300)
+    rows = 2 * 128
+    up = lambda x: -(-x // 256) * 256
+    assert lib.pa_decode_workspace_size(ctypes.byref(s), 4, 1) == \
+        up(rows * 4) + up(rows * 4 * 512 * 2) + up(rows * 4 * 4)
+
+
 def test_workspace_init_checks(lib):
     s = shape()
     init = lambda sh, ws, n, splits=4: lib.pa_workspace_init(ctypes.byref(sh), splits, 0, ws, n, NULL)
