@@ -862,6 +862,7 @@ struct WideLoads {
   }
 };
 static_assert(kDmaInst == 36 && kWideNW == 4 && kRowB == 1152, "wide load plan");
+static_assert(kWideNH == kRing * kCT, "the queries of a head group fill the ring");
 
 // Resource of chunk ci: its rows in the cache, the record count the bytes of
 // the chunk inside the split (0 for a chunk past its end).
@@ -883,17 +884,28 @@ struct WideState {
 // heads, in two accumulator chains: even and odd k-steps).  issue(k) runs
 // before k-step 4k (k < 9): this wave's loads of a later chunk go out between
 // the MFMAs, so the matrix core stays busy while the load path accepts them.
+// Lane pointers of the 16-byte operand reads of a buffer in the chunk layout:
+// k-step kb of lane (r, hsel) is chunk 2kb + hsel of row r, which sits at
+// chunk (2kb + hsel) ^ (r & 7), byte 16*(hsel ^ (r & 1)) +
+// 32*((kb & 3) ^ ((r >> 1) & 3)) + 128*(kb >> 2) of the row.  As a score A
+// operand the row is a token; as a query B operand it is a head.
+struct WideRowReads {
+  const lds_char* pr[4];
+  __device__ __forceinline__ WideRowReads(const lds_char* buf, int lane) {
+    const int r = lane & 31, hsel = lane >> 5;
+#pragma unroll
+    for (int m4 = 0; m4 < 4; ++m4)
+      pr[m4] = buf + r * kRowB + 16 * (hsel ^ (r & 1)) + 32 * (m4 ^ ((r >> 1) & 3));
+  }
+  __device__ __forceinline__ u32x4 operator()(int kb) const {
+    return *(const lds_u32x4*)(pr[kb & 3] + 128 * (kb >> 2));
+  }
+};
+
 template <typename Issue>
 __device__ __forceinline__ void wide_score_mfma(const WideState& st, const lds_char* buf, int lane,
                                                 f32x16& s0, f32x16& s1, const Issue& issue) {
-  const int r = lane & 31, hsel = lane >> 5;
-  // Chunk c of row r sits at c ^ (r & 7); with c = 2kb + hsel that is byte
-  // 16*(hsel ^ (r & 1)) + 32*((kb & 3) ^ ((r >> 1) & 3)) + 128*(kb >> 2).
-  const lds_char* pr[4];
-#pragma unroll
-  for (int m4 = 0; m4 < 4; ++m4)
-    pr[m4] = buf + r * kRowB + 16 * (hsel ^ (r & 1)) + 32 * (m4 ^ ((r >> 1) & 3));
-  auto load_a = [&](int kb) { return *(const lds_u32x4*)(pr[kb & 3] + 128 * (kb >> 2)); };
+  const WideRowReads load_a(buf, lane);
   constexpr int L = kWideLook;
   u32x4 ab[L + 1];
 #pragma unroll
@@ -1022,7 +1034,6 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
   const int s = u / p.B;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane & 31, hsel = lane >> 5;
   const int head0 = hg * kWideNH;
   const int ctx = clampi(p.context_lens[b], 0, p.max_ctx);
   const int pages = (ctx + 63) / 64;
@@ -1048,27 +1059,34 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
   src.nblocks = p.nblocks;
   src.w = w;
   src.lane = lane;
-  // Every chunk is loaded, also past the split's end (those loads write
-  // zeros), so the count in flight is the same at every step.  The first
-  // pass issues them before the query loads and then waits for everything:
-  // the compiler does not see the direct-to-LDS loads, and a partial wait here
-  // would leave it believing query loads are still in flight inside the loop
-  // (where it would then wait for every chunk load in flight).
   WideLoads ld;
   ld.init(w, lane);
-  src.begin(s * p.c);
-  ld.issue_all(wide_rsrc(src, 0), slot(0));
-  ld.issue_all(wide_rsrc(src, 1), slot(1));
   WideState st;
   const WideVaBase vb = wide_va_base(w, lane);
   const size_t row0 = (size_t)b * p.ql * p.Hq + head0;
   {
-    // B operand of k-step kb: head 32w + r, dims 16kb + 8*hsel .. +7
-    const char* qr = static_cast<const char*>(p.q) + (row0 + kWideHW * w + r) * kRowB + hsel * 16;
+    // The queries of the 128 heads (rows of 1152 bytes, like latent rows)
+    // come through the ring, 32 heads to a slot in the chunk layout, with the
+    // chunk loads (contiguous 1 KiB per load); wave w then reads the B
+    // operands of heads 32w .. 32w+31 from slot w: k-step kb of lane
+    // (r, hsel) is dims 16kb + 8*hsel .. +7 of head 32w + r.  Loaded from
+    // global memory straight into these registers, every load would touch
+    // 32 rows with 32 bytes each.
+    const char* qb = static_cast<const char*>(p.q) + row0 * kRowB;
 #pragma unroll
-    for (int kb = 0; kb < kWideKS; ++kb) st.qf[kb] = ld128(qr + kb * 32);
+    for (int i = 0; i < kRing; ++i) ld.issue_all(raw_rsrc(qb + i * kChunkB, kChunkB), slot(i));
+    wait_vm<0>();
+    lds_barrier();
+    const WideRowReads load_q(slot(w), lane);
+#pragma unroll
+    for (int kb = 0; kb < kWideKS; ++kb) st.qf[kb] = load_q(kb);
+    lds_barrier();                                    // every wave holds its queries
   }
-  wait_vm<0>();
+  // Every chunk is loaded, also past the split's end (those loads write
+  // zeros), so the count in flight is the same at every step.
+  src.begin(s * p.c);
+  ld.issue_all(wide_rsrc(src, 0), slot(0));
+  ld.issue_all(wide_rsrc(src, 1), slot(1));
   st.m = kNegInf;
   st.mtop = kNegInf;
   for (bool first = true;; first = false) {
@@ -1085,8 +1103,8 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
       src.begin(s * p.c);
       ld.issue_all(wide_rsrc(src, 0), slot(0));
       ld.issue_all(wide_rsrc(src, 1), slot(1));
-      wait_vm<kNwi>();                                // chunk 0 (chunk 1 may be in flight)
     }
+    wait_vm<kNwi>();                                  // chunk 0 (chunk 1 may be in flight)
     lds_barrier();
     if (nchunks > 0) {
       ld.refresh();
