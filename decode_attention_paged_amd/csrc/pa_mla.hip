@@ -5,30 +5,31 @@
 // handles the heads of one head group for one (sequence, split) and walks
 // the split in chunks of 32 tokens (half a 64-token page):
 //
-//   scores  S^T[32 tok x 16 heads] = C[32 x 576] Q^T        per 16-head block
+//   scores  S^T[32 tok x heads] = C[32 x 576] Q^T
 //   values  O^T[512 dims x heads] += V^T[512 x 32] P^T      split by dims over waves
 //
-// on v_mfma_f32_16x16x32_bf16.  Queries stay in registers as score B
-// operands; the value product is split by output dims, so the transposed
-// value reads (ds_read_b64_tr_b16, the slowest LDS read) touch each latent
-// element once per workgroup.  The probabilities P move from the score to the
-// value product through LDS.  This is Flash-Decoding's attention of the query
-// with one block of keys and values plus the block's log-sum-exp (the
-// "flash decoding ++" entry, its three-steps snippet, second step); the
-// split's (o_s, lse_s) go to the workspace for the reduction, o_s in
-// bfloat16 (the output's type), lse_s in float32.
+// on the matrix cores.  Queries stay in registers as score B operands; the
+// value product is split by output dims, so the transposed value reads
+// (ds_read_b64_tr_b16, the slowest LDS read) touch each latent element once
+// per workgroup.  The probabilities P move from the score to the value
+// product through LDS.  This is Flash-Decoding's attention of the query with
+// one block of keys and values plus the block's log-sum-exp (the "flash
+// decoding ++" entry, its three-steps snippet, second step); the split's
+// (o_s, lse_s) go to the workspace for the reduction, o_s in bfloat16 (the
+// output's type), lse_s in float32.
 //
-// Two workgroup shapes, both with two waves per SIMD (at most 256 registers
-// a wave):
-//   * wide (128 heads, 64-token pages): 8 alike waves.  Wave w scores head
-//     block w and accumulates dims 64w .. 64w+63 of all 128 heads; each CU
-//     streams every latent row of its split once.
+// Two workgroup shapes:
+//   * wide (128 heads, 64-token pages): 4 waves, one per SIMD, on
+//     v_mfma_f32_32x32x16_bf16; wave w scores heads 32w .. 32w+31 and
+//     accumulates dims 128w .. 128w+127 of all 128 heads; each CU streams
+//     every latent row of its split once (details at mla_wide_partial).
 //   * role-split (16, 32 or 64 heads; also one-token pages, whose token ids
-//     take 8 KiB of LDS): score waves hold the queries, value waves hold the
-//     accumulators and issue the chunk loads.  With 128 heads the grid has
-//     two such workgroups per (sequence, split), 8 apart in dispatch order:
-//     the same XCD (workgroups go round-robin to the 8 XCDs), so the second
-//     reads the rows from that XCD's L2.
+//     take 8 KiB of LDS): two waves per SIMD on v_mfma_f32_16x16x32_bf16;
+//     score waves hold the queries, value waves hold the accumulators and
+//     issue the chunk loads.  With 128 heads the grid has two such
+//     workgroups per (sequence, split), 8 apart in dispatch order: the same
+//     XCD (workgroups go round-robin to the 8 XCDs), so the second reads the
+//     rows from that XCD's L2.
 //
 // The reference max of each head is fixed for a pass over the split: the
 // first chunk's max.  Every later chunk's weights 2^(s - m) stay below
@@ -41,17 +42,16 @@
 // over at most twice; only scores that climb by 2^kHeadroom within a split
 // pay for the second pass.
 //
-// Chunks stream HBM -> LDS with direct-to-LDS loads (global_load_lds_dwordx4,
-// no registers), two chunks in flight while one is scored and the one before
-// goes through the value product.  Barriers are raw s_barrier with explicit
-// waits: __syncthreads() would also wait for every chunk in flight.
+// Chunks stream HBM -> LDS with direct-to-LDS loads (no registers), two
+// chunks in flight while one is scored and the one before goes through the
+// value product.  Barriers are raw s_barrier with explicit waits:
+// __syncthreads() would also wait for every chunk in flight.
 //
 // LDS chunk rows are 1152 bytes (72 chunks of 16 bytes).  Chunk c of token
-// row t sits at position c ^ (t & 7); with it the score reads (16 rows, one
+// row t sits at position c ^ (t & 7); with it the score reads (rows of one
 // chunk each) and the transposed value reads run at the conflict-free rate
 // (measured against a linear read of the same size).  The probabilities are
-// stored so that the value product's B-operand read is linear: for head block
-// nb, the 16-byte slot q*16 + n holds tokens 8q .. 8q+7 of head 16 nb + n.
+// stored so that the value product's B-operand read is linear.
 
 #include "pa_device.h"
 #include "pa_launch.h"
@@ -312,7 +312,9 @@ struct ChunkSource<NW, 1> {
 
 // Operands of the value product for dims DW*w .. DW*w + DW - 1 of every
 // head.  A operand (V^T): tokens quad*8 .. +7 of one dim per lane, two
-// transposed reads; B operand (P^T): one 16-byte slot.
+// transposed reads; B operand (P^T): one 16-byte slot.  The probabilities of
+// head block nb are stored so that this read is linear: 16-byte slot
+// q*16 + n holds tokens 8q .. 8q+7 of head 16 nb + n.
 template <int DW>
 struct ValueOps {
   const lds_char* buf;
