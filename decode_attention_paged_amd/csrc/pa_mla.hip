@@ -825,38 +825,56 @@ __device__ __forceinline__ void mfma32_a(f32x16& d, const u32x4& a, const u32x4&
                                               __builtin_bit_cast(bf16x8, b), d, 0, 0, 0);
 }
 
+// Swizzle key of the wide workgroup's chunk rows: 16-byte chunk c of row t
+// sits at c ^ wide_key(t), with key bits (t1 ^ t2, t3, t1) of the row's bits
+// t1..t3.  A 16-byte read instruction is served 16 lanes at a time across
+// 64 banks; for the score and query reads (16 consecutive rows at one chunk)
+// the key spreads the 8 even and the 8 odd rows over distinct bank groups,
+// and for the transposed value reads (rows r, r + 1, r + 2, r + 3 at four
+// chunks, r a multiple of 4) it separates rows r and r + 2, which a key of
+// t & 7 maps to the same banks (measured: 62 % fewer bank-conflict cycles).
+// Rows r and r + 4 (r & 4 == 0) differ in key bit 2 only.
+__device__ __forceinline__ int wide_key(int t) {
+  return ((((t >> 2) ^ (t >> 1)) & 1) << 2) | (((t >> 3) & 1) << 1) | ((t >> 1) & 1);
+}
+
 // Chunk loads of the wide workgroup.  A chunk is 36 loads of 1 KiB: load
 // j = 9q + r covers 16-byte slots 64r .. 64r + 63 of token rows 8q .. 8q + 7
-// (8 rows of 72 slots), and since the swizzle key repeats every 8 rows, its
-// lanes read the bytes of load r's lanes plus 8 rows (9216 bytes) times q.
-// Wave w issues loads r = 2w and 2w + 1 of every row group q and load r = 8
-// of group w, so it needs the lane offsets of three loads only, computed
-// once; a load is then one add and the buffer load (its chunk's resource
-// bounds it: rows past the split's end read zeros).
+// (8 rows of 72 slots); the swizzle key repeats every 16 rows, so its lanes
+// read the bytes of load r's lanes in a row group of q's parity plus 16 rows
+// (18432 bytes) times q / 2.  Wave w issues loads r = 2w and 2w + 1 of every
+// row group q and load r = 8 of group w, so it needs the lane offsets of
+// five loads only, computed once; a load is then one add and the buffer load
+// (its chunk's resource bounds it: rows past the split's end read zeros).
 struct WideLoads {
-  int pa, pb, p8;   // lane offsets of loads r = 2w, 2w + 1 and 8 in row group 0
+  int pa0, pb0, pa1, pb1;   // lane offsets of loads r = 2w, 2w + 1 in row groups 0 and 1
+  int p8;                   // of load r = 8 in row group w % 2
   int w;
-  __device__ __forceinline__ static int lane_off(int r, int lane) {
+  __device__ __forceinline__ static int lane_off(int r, int parity, int lane) {
     const int slot = 64 * r + lane;
-    const int t = slot / (kRowB / 16);
-    const int c = (slot % (kRowB / 16)) ^ row_key(t);
+    const int t = 8 * parity + slot / (kRowB / 16);
+    const int c = (slot % (kRowB / 16)) ^ wide_key(t);
     return t * kRowB + c * 16;
   }
   __device__ __forceinline__ void init(int w_, int lane) {
     w = w_;
-    pa = lane_off(2 * w, lane);
-    pb = lane_off(2 * w + 1, lane);
-    p8 = lane_off(8, lane);
+    pa0 = lane_off(2 * w, 0, lane);
+    pb0 = lane_off(2 * w + 1, 0, lane);
+    pa1 = lane_off(2 * w, 1, lane);
+    pb1 = lane_off(2 * w + 1, 1, lane);
+    p8 = lane_off(8, w & 1, lane);
   }
   // A fresh definition of the offsets for each chunk, so the compiler does
   // not hoist all nine sums out of the chunk loop (nine live registers).
-  __device__ __forceinline__ void refresh() { asm volatile("" : "+v"(pa), "+v"(pb), "+v"(p8)); }
+  __device__ __forceinline__ void refresh() {
+    asm volatile("" : "+v"(pa0), "+v"(pb0), "+v"(pa1), "+v"(pb1), "+v"(p8));
+  }
   // Load i (0 .. 8) of this wave's share of a chunk into chunk buffer dst.
   __device__ __forceinline__ void issue(const i32x4& rsrc, lds_char* dst, int i) const {
     const int q = i < 8 ? i >> 1 : w;
     const int r = i < 8 ? 2 * w + (i & 1) : 8;
-    const int lo = i < 8 ? ((i & 1) ? pb : pa) : p8;
-    dma16_buf(rsrc, lo + 8 * kRowB * q, dst + (9 * q + r) * 1024);
+    const int lo = i < 8 ? ((i & 1) ? ((q & 1) ? pb1 : pb0) : ((q & 1) ? pa1 : pa0)) : p8;
+    dma16_buf(rsrc, lo + 16 * kRowB * (q >> 1), dst + (9 * q + r) * 1024);
   }
   __device__ __forceinline__ void issue_all(const i32x4& rsrc, lds_char* dst) const {
 #pragma unroll
@@ -888,16 +906,16 @@ struct WideState {
 // the MFMAs, so the matrix core stays busy while the load path accepts them.
 // Lane pointers of the 16-byte operand reads of a buffer in the chunk layout:
 // k-step kb of lane (r, hsel) is chunk 2kb + hsel of row r, which sits at
-// chunk (2kb + hsel) ^ (r & 7), byte 16*(hsel ^ (r & 1)) +
-// 32*((kb & 3) ^ ((r >> 1) & 3)) + 128*(kb >> 2) of the row.  As a score A
+// chunk (2kb + hsel) ^ k (k = wide_key(r)), byte 16*(hsel ^ (k & 1)) +
+// 32*((kb & 3) ^ (k >> 1)) + 128*(kb >> 2) of the row.  As a score A
 // operand the row is a token; as a query B operand it is a head.
 struct WideRowReads {
   const lds_char* pr[4];
   __device__ __forceinline__ WideRowReads(const lds_char* buf, int lane) {
-    const int r = lane & 31, hsel = lane >> 5;
+    const int r = lane & 31, hsel = lane >> 5, k = wide_key(r);
 #pragma unroll
     for (int m4 = 0; m4 < 4; ++m4)
-      pr[m4] = buf + r * kRowB + 16 * (hsel ^ (r & 1)) + 32 * (m4 ^ ((r >> 1) & 3));
+      pr[m4] = buf + r * kRowB + 16 * (hsel ^ (k & 1)) + 32 * (m4 ^ (k >> 1));
   }
   __device__ __forceinline__ u32x4 operator()(int kb) const {
     return *(const lds_u32x4*)(pr[kb & 3] + 128 * (kb >> 2));
@@ -980,7 +998,7 @@ __device__ __forceinline__ void wide_weights(WideState& st, float (&v)[16], lds_
 // and r0 + 4 (r0 = 16kb + 8*(lane >> 5) + (lane & 15) / 4), each of a
 // 4-token x 16-dim block per 16 lanes.  Its 16-byte chunk index within the
 // row is 16w + 4mb + b2 (b2 in 0..3: dim half and lane), stored at that index
-// XOR (row & 7).  Bit 2 of the index is mb & 1 and rows r0 and r0 + 4 differ
+// XOR wide_key(row).  Bit 2 of the index is mb & 1 and rows r0 and r0 + 4 differ
 // in bit 2 of the key, so every read address is one of two bases plus an
 // immediate: 128*(mb >> 1) + 18432*kb (+ 4608 for the second row).
 struct WideVaBase {
@@ -992,7 +1010,7 @@ __device__ __forceinline__ WideVaBase wide_va_base(int w, int lane) {
   const int bc = 2 * (16 * (gq & 1)) + (n & 3) * 8;  // byte column within the 64-byte M-block
   const int b2 = bc >> 4, lo = bc & 15;
   const int row = r0 * kRowB + 16 * 16 * w + lo;
-  return WideVaBase{row + 16 * (b2 ^ row_key(r0)), row + 16 * ((b2 ^ row_key(r0)) ^ 4)};
+  return WideVaBase{row + 16 * (b2 ^ wide_key(r0)), row + 16 * ((b2 ^ wide_key(r0)) ^ 4)};
 }
 __device__ __forceinline__ u32x4 wide_va(const lds_char* buf, const WideVaBase& vb, int mb, int kb) {
   const int imm = 128 * (mb >> 1) + 16 * kRowB * kb;
