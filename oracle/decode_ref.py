@@ -43,7 +43,9 @@ last page are never read.  bf16 inputs are widened bit-exactly (bits << 16).
 An FP8 KV cache (the "llms-attention" post names FP8 only as hardware low
 precision FlashAttention-3 uses) is read as OCP E4M3 codes with one scale per
 tensor: a key is k_scale times its code's value, a value v_scale times its
-code's value; queries and outputs keep their own dtype.
+code's value; queries and outputs keep their own dtype.  An FP8 latent cache
+holds one code row per token: the key is k_scale times the whole row, the
+value v_scale times its leading dv entries.
 
 Pool layouts (the library's documented layouts):
     k_pool [num_blocks][Hkv][bs][D]
@@ -296,12 +298,16 @@ def paged_decode_split(q, k_pool, v_pool, block_table, context_lens, scale, dtyp
 
 
 def paged_decode_mla(q, c_pool, block_table, context_lens, scale, dv=512, dtype="bf16",
-                     heads=None):
+                     heads=None, kv_dtype=None, k_scale=1.0, v_scale=1.0):
     """Reference MLA decode: all query heads attend to one latent per token.
 
     Keys are the full latent rows c_i [Dqk]; values are c_i[:dv] (the same
-    stored vector).  Returns (out [B][Hq][dv], lse [B][Hq]) in float64.
+    stored vector).  ``kv_dtype`` is the latent cache's element type when it
+    differs from ``dtype`` ("fp8": E4M3 codes; keys are k_scale times the
+    row, values v_scale times its head).  Returns (out [B][Hq][dv],
+    lse [B][Hq]) in float64.
     """
+    kvd = dtype if kv_dtype is None else kv_dtype
     qf = as_f64(q, dtype)
     B, Hq, Dqk = qf.shape
     nb, bs, Dc = c_pool.shape
@@ -318,8 +324,9 @@ def paged_decode_mla(q, c_pool, block_table, context_lens, scale, dv=512, dtype=
         if want is not None and b not in want:
             continue
         pages, slots = token_locations(block_table[b], int(ctx[b]), bs)
-        c = as_f64(gather_latent(c_pool, pages, slots), dtype)
+        c = as_f64(gather_latent(c_pool, pages, slots), kvd)
         keys, values = latent_kv(c, dv)
+        keys, values = keys * k_scale, values * v_scale
         for h in (range(Hq) if want is None else want[b]):
             out[b, h], lse[b, h] = attend(qf[b, h], keys, values, scale)
     return out, lse
@@ -375,7 +382,7 @@ def paged_decode_rows(q, k_pool, v_pool, block_table, context_lens, scale, dtype
 
 
 def paged_decode_mla_rows(q, c_pool, block_table, context_lens, scale, dv=512, dtype="bf16",
-                          rows=None):
+                          rows=None, kv_dtype=None, k_scale=1.0, v_scale=1.0):
     """The latent variant with q_len query rows per sequence (q [B][q_len][Hq][Dqk])."""
     if q.ndim != 4:
         raise ValueError("q must be [B][q_len][Hq][Dqk]")
@@ -386,7 +393,9 @@ def paged_decode_mla_rows(q, c_pool, block_table, context_lens, scale, dv=512, d
     for j, heads in _rows_by_j(rows, L).items():
         ctx_j = np.array([row_context(c, L, j) for c in ctx], dtype=np.int64)
         out[:, j], lse[:, j] = paged_decode_mla(np.ascontiguousarray(q[:, j]), c_pool, block_table,
-                                                ctx_j, scale, dv=dv, dtype=dtype, heads=heads)
+                                                ctx_j, scale, dv=dv, dtype=dtype, heads=heads,
+                                                kv_dtype=kv_dtype, k_scale=k_scale,
+                                                v_scale=v_scale)
     return out, lse
 
 
@@ -399,12 +408,13 @@ def decode_inputs(inp, heads=None):
     if inp.q.ndim == 4:
         if inp.kind == "mla":
             return paged_decode_mla_rows(inp.q, inp.c_pages, bt, inp.context_lens, inp.scale,
-                                         dv=inp.head_dim_v, dtype=inp.dtype, rows=heads)
+                                         dv=inp.head_dim_v, dtype=inp.dtype, rows=heads,
+                                         **_kv_args(inp))
         return paged_decode_rows(inp.q, inp.k_pages, inp.v_pages, bt, inp.context_lens,
                                  inp.scale, dtype=inp.dtype, rows=heads, **_kv_args(inp))
     if inp.kind == "mla":
         return paged_decode_mla(inp.q, inp.c_pages, bt, inp.context_lens, inp.scale,
-                                dv=inp.head_dim_v, dtype=inp.dtype, heads=heads)
+                                dv=inp.head_dim_v, dtype=inp.dtype, heads=heads, **_kv_args(inp))
     return paged_decode(inp.q, inp.k_pages, inp.v_pages, bt, inp.context_lens, inp.scale,
                         dtype=inp.dtype, heads=heads, **_kv_args(inp))
 

@@ -642,6 +642,56 @@ def pin_fp8_decode(o):
             _close(l1, ref_l[:, 0], what="fp8 lse")
 
 
+def pin_mla_fp8_decode(o):
+    """The latent variant over FP8 codes equals pure-Python loops over the
+    rows dequantized by torch: keys k_scale times the row, values v_scale
+    times its head (one and three query rows)."""
+    import torch
+    widen = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for seed, L in ((62, 1), (63, 3)):
+        rng = np.random.default_rng(seed)
+        B, Hq, Dc, dv, bs, ctxs = 2, 3, 6, 4, 4, [6, 9]
+        n_pages = [-(-c // bs) for c in ctxs]
+        total = sum(n_pages) + 2
+        perm = rng.permutation(total)
+        bt = np.full((B, max(n_pages)), -1, dtype=np.int64)
+        off = 0
+        for b, n in enumerate(n_pages):
+            bt[b, :n] = perm[off:off + n]
+            off += n
+        codes = _fp8_codes(rng, (total, bs, Dc))
+        ks, vs = 0.037, 1.9
+        kd, vd = (widen(codes) * ks).tolist(), (widen(codes) * vs).tolist()
+        q = rng.standard_normal((B, L, Hq, Dc))
+        scale = 0.43
+        qll, btl = q.tolist(), bt.tolist()
+        ref_o = np.zeros((B, L, Hq, dv))
+        ref_l = np.zeros((B, L, Hq))
+        for b in range(B):
+            for j in range(L):
+                vis = [i for i in range(ctxs[b]) if i <= ctxs[b] - L + j]
+                for h in range(Hq):
+                    kr = [kd[btl[b][i // bs]][i % bs] for i in vis]
+                    vr = [vd[btl[b][i // bs]][i % bs] for i in vis]
+                    s_ = [scale * math.fsum(qll[b][j][h][d] * x[d] for d in range(Dc)) for x in kr]
+                    m = max(s_)
+                    e = [math.exp(x - m) for x in s_]
+                    tot = math.fsum(e)
+                    ref_o[b, j, h] = [math.fsum(e[i] * vr[i][d] for i in range(len(vr))) / tot
+                                      for d in range(dv)]
+                    ref_l[b, j, h] = m + math.log(tot)
+        out, lse = o.paged_decode_mla_rows(q, codes, bt, np.array(ctxs), scale, dv=dv, dtype="f64",
+                                           kv_dtype="fp8", k_scale=ks, v_scale=vs)
+        _close(out, ref_o, what=f"mla fp8 rows out L{L}")
+        _close(lse, ref_l, what=f"mla fp8 rows lse L{L}")
+        if L == 1:
+            o1, l1 = o.paged_decode_mla(np.ascontiguousarray(q[:, 0]), codes, bt, np.array(ctxs),
+                                        scale, dv=dv, dtype="f64", kv_dtype="fp8", k_scale=ks,
+                                        v_scale=vs)
+            _close(o1, ref_o[:, 0], what="mla fp8 out")
+            _close(l1, ref_l[:, 0], what="mla fp8 lse")
+
+
 ALL_PINS = [
     pin_bruteforce, pin_mla_bruteforce, pin_mla_token_index_list, pin_bf16_widening, pin_sdpa,
     pin_ctx_one,
@@ -650,5 +700,5 @@ ALL_PINS = [
     pin_gqa_equals_mha, pin_mla_equals_mqa, pin_batch_independence, pin_sampled_heads,
     pin_append_then_decode, pin_append_out_of_range, pin_append_latent,
     pin_rows_bruteforce, pin_rows_sdpa, pin_rows_single_is_decode, pin_rows_causality,
-    pin_mla_rows_bruteforce, pin_fp8_widening, pin_fp8_decode,
+    pin_mla_rows_bruteforce, pin_fp8_widening, pin_fp8_decode, pin_mla_fp8_decode,
 ]

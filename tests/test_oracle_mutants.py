@@ -253,6 +253,14 @@ def _decode_v_unscaled(*a, k_scale=1.0, v_scale=1.0, **kw):
     return ref._orig_paged_decode(*a, k_scale=k_scale, v_scale=1.0, **kw)
 
 
+def _mla_scales_swapped(*a, k_scale=1.0, v_scale=1.0, **kw):
+    return ref._orig_paged_decode_mla(*a, k_scale=v_scale, v_scale=k_scale, **kw)
+
+
+def _mla_k_scale_dropped(*a, k_scale=1.0, v_scale=1.0, **kw):
+    return ref._orig_paged_decode_mla(*a, k_scale=1.0, v_scale=v_scale, **kw)
+
+
 MUTANTS = {
     "scores_noscale": ("scores", _scores_noscale),
     "scores_negated": ("scores", _scores_negated),
@@ -290,6 +298,8 @@ MUTANTS = {
     "fp8_sign_dropped": ("fp8_e4m3_bits_to_f64", _fp8_unsigned),
     "fp8_scales_swapped": ("paged_decode", _decode_scales_swapped),
     "fp8_v_scale_dropped": ("paged_decode", _decode_v_unscaled),
+    "mla_fp8_scales_swapped": ("paged_decode_mla", _mla_scales_swapped),
+    "mla_fp8_k_scale_dropped": ("paged_decode_mla", _mla_k_scale_dropped),
 }
 
 
@@ -300,6 +310,7 @@ def test_mutant_is_caught(name, monkeypatch):
     monkeypatch.setitem(ref.__dict__, "_orig_gather_kv", ref.gather_kv)
     monkeypatch.setitem(ref.__dict__, "_orig_append_kv", ref.append_kv)
     monkeypatch.setitem(ref.__dict__, "_orig_paged_decode", ref.paged_decode)
+    monkeypatch.setitem(ref.__dict__, "_orig_paged_decode_mla", ref.paged_decode_mla)
     monkeypatch.setattr(ref, attr, fn)
     caught = []
     for pin in ALL_PINS:
