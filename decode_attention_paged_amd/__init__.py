@@ -130,12 +130,14 @@ def _mha_shape(q, k_cache, v_cache, block_table, context_lens, max_context_len, 
                       kv_dtype=kvd, k_scale=ks, v_scale=vs)
 
 
-def _mla_shape(q, kv_cache, block_table, context_lens, max_context_len, scale, head_dim_v):
+def _mla_shape(q, kv_cache, block_table, context_lens, max_context_len, scale, head_dim_v,
+               k_scale=None, v_scale=None):
     _need(q, "q")
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
     dev = q.device
-    _need(kv_cache, "kv_cache", q.dtype, 3, dev)
+    _need(kv_cache, "kv_cache", None, 3, dev)
+    kvd, ks, vs = _kv_dtype(kv_cache, q.dtype, k_scale, v_scale)
     _need(block_table, "block_table", torch.int32, 2, dev)
     _need(context_lens, "context_lens", torch.int32, 1, dev)
     B, L, Hq, D = _q_dims(q)
@@ -146,7 +148,8 @@ def _mla_shape(q, kv_cache, block_table, context_lens, max_context_len, scale, h
         max_context_len = int(context_lens.max().item()) if B else 0
     return make_shape(batch=B, num_q_heads=Hq, num_kv_heads=1, head_dim=D, head_dim_v=head_dim_v,
                       block_size=bs, max_blocks_per_seq=block_table.shape[1], num_blocks=nb,
-                      max_context_len=max_context_len, scale=scale, dtype=q.dtype, q_len=L)
+                      max_context_len=max_context_len, scale=scale, dtype=q.dtype, q_len=L,
+                      kv_dtype=kvd, k_scale=ks, v_scale=vs)
 
 
 def choose_num_splits(shape: PaShape, num_cus: int = 0, mla: bool = False) -> int:
@@ -242,11 +245,18 @@ def decode(q, k_cache, v_cache, block_table, context_lens, *, max_context_len=No
 
 
 def decode_mla(q, kv_cache, block_table, context_lens, *, max_context_len=None, scale=None,
-               head_dim_v=512, num_splits=0, out=None, lse=None, workspace=None, stream=None):
-    """MLA latent decode: keys = latent rows, values = their first head_dim_v entries."""
+               head_dim_v=512, num_splits=0, out=None, lse=None, workspace=None, stream=None,
+               k_scale=None, v_scale=None):
+    """MLA latent decode: keys = latent rows, values = their first head_dim_v entries.
+
+    An FP8 latent cache (torch.float8_e4m3fn, bf16 q) needs k_scale and
+    v_scale: a key is k_scale times the row's values, a value v_scale times
+    its first head_dim_v.
+    """
     if scale is None:
         raise ValueError("MLA needs an explicit scale")
-    shape = _mla_shape(q, kv_cache, block_table, context_lens, max_context_len, scale, head_dim_v)
+    shape = _mla_shape(q, kv_cache, block_table, context_lens, max_context_len, scale, head_dim_v,
+                       k_scale, v_scale)
     out, lse, ws = _outputs(shape, q, out, lse, workspace, num_splits, True)
     _note_workspace(ws, _rows(shape))
     st = _lib.load().pa_decode_mla(ctypes.byref(shape), _ptr(q), _ptr(kv_cache), _ptr(block_table),
@@ -336,9 +346,11 @@ def append_kv(k_new, v_new, k_cache, v_cache, block_table, context_lens, stream=
 
 
 def append_latent(c_new, kv_cache, block_table, context_lens, stream=None):
-    """MLA: write one new latent row per sequence (c_new [B][D]) into the paged cache."""
+    """MLA: write one new latent row per sequence (c_new [B][D]) into the paged cache
+    (FP8 codes for an FP8 cache, quantised by the caller)."""
     _need(c_new, "c_new", ndim=2)
-    if c_new.dtype not in _DTYPES:
+    fp8 = _FP8 is not None and c_new.dtype == _FP8
+    if c_new.dtype not in _DTYPES and not fp8:
         raise ValueError(f"unsupported dtype {c_new.dtype}")
     dev = c_new.device
     _need(kv_cache, "kv_cache", c_new.dtype, 3, dev)
@@ -352,7 +364,9 @@ def append_latent(c_new, kv_cache, block_table, context_lens, stream=None):
         raise ValueError("block_table / context_lens batch differs from c_new")
     shape = make_shape(batch=B, num_q_heads=1, num_kv_heads=1, head_dim=D, head_dim_v=D,
                        block_size=bs, max_blocks_per_seq=block_table.shape[1], num_blocks=nb,
-                       max_context_len=0, scale=1.0, dtype=c_new.dtype)
+                       max_context_len=0, scale=1.0,
+                       dtype=torch.bfloat16 if fp8 else c_new.dtype,
+                       kv_dtype=_lib.PA_FP8_E4M3 if fp8 else 0)
     st = _lib.load().pa_append_latent(ctypes.byref(shape), _ptr(c_new), _ptr(kv_cache),
                                       _ptr(block_table), _ptr(context_lens), _stream(stream))
     _lib.check(st, "pa_append_latent")

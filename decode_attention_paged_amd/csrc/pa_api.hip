@@ -37,7 +37,10 @@ enum class Kernel { None, MhaValu, GqaMfma, MlaMfma };
 Kernel pick_kernel(const pa_shape& s, bool mla) {
   const bool bf16 = s.dtype == PA_BF16;
   if (mla) {
-    if (fp8_kv(s)) return Kernel::None;
+    if (fp8_kv(s))
+      return bf16 && pa::mla_mfma_fp8_supported(s.head_dim, s.head_dim_v, s.block_size, s.num_q_heads)
+                 ? Kernel::MlaMfma
+                 : Kernel::None;
     return pa::mla_mfma_supported(bf16, s.head_dim, s.head_dim_v, s.block_size, s.num_q_heads)
                ? Kernel::MlaMfma
                : Kernel::None;
@@ -332,7 +335,7 @@ pa_status run_partial(const pa_shape* shape, const void* q, const void* k, const
   switch (kern) {
     case Kernel::MhaValu: e = pa::launch_mha_valu(p, shape->dtype == PA_BF16, fp8_kv(*shape), hs); break;
     case Kernel::GqaMfma: e = pa::launch_gqa_mfma(p, fp8_kv(*shape), hs); break;
-    case Kernel::MlaMfma: e = pa::launch_mla_mfma(p, hs); break;
+    case Kernel::MlaMfma: e = pa::launch_mla_mfma(p, fp8_kv(*shape), hs); break;
     default: return PA_ERR_UNSUPPORTED;
   }
   if (e != hipSuccess) return PA_ERR_HIP;
@@ -583,8 +586,10 @@ pa_status pa_append_latent(const pa_shape* shape, const void* c_new, void* kv_ca
   if (st != PA_OK) return st;
   if (!c_new || !kv_cache || !block_table || !context_lens) return PA_ERR_INVALID;
   const pa_shape& s = *shape;
-  // no latent decode reads FP8 codes: refuse to write caches nothing can read
-  if (s.kv_dtype == PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
+  // FP8 latent rows only in the layout the FP8 latent decode reads (576-wide
+  // rows on 64-token pages): refuse to write caches nothing can read
+  if (s.kv_dtype == PA_FP8_E4M3 && !(s.head_dim == 576 && s.block_size == 64))
+    return PA_ERR_UNSUPPORTED;
   pa::AppendParams a{c_new, nullptr, kv_cache, nullptr, block_table, context_lens,
                      s.batch, 1, s.head_dim, 0, s.block_size, s.max_blocks_per_seq,
                      s.num_blocks};

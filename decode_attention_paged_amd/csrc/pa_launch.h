@@ -34,7 +34,7 @@ struct Params {
 // Each returns hipSuccess or the launch error.  Shapes are validated by the caller.
 hipError_t launch_mha_valu(const Params& p, bool bf16, bool fp8kv, hipStream_t st);
 hipError_t launch_gqa_mfma(const Params& p, bool fp8kv, hipStream_t st);
-hipError_t launch_mla_mfma(const Params& p, hipStream_t st);
+hipError_t launch_mla_mfma(const Params& p, bool fp8kv, hipStream_t st);
 hipError_t launch_reduce(const Params& p, bool bf16, hipStream_t st);
 hipError_t launch_zero_i32(int32_t* dst, size_t n, hipStream_t st);
 
@@ -65,6 +65,8 @@ bool gqa_mfma_supported(bool bf16, int D, int Dv, int bs, int G, int ql);
 bool gqa_mfma_fp8_supported(int D, int bs, int G, int ql);
 bool mha_valu_fp8_supported(int D, int bs);
 bool mla_mfma_supported(bool bf16, int Dqk, int Dv, int bs, int Hq);
+// FP8 E4M3 latent cache (bf16 queries): the 128-head kernel on 64-token pages.
+bool mla_mfma_fp8_supported(int Dqk, int Dv, int bs, int Hq);
 // Query heads one MLA workgroup holds (the grid has Hq / this head groups).
 int mla_heads_per_workgroup(int Hq, int bs);
 // Longest split (tokens) the MLA kernel takes for this page size (one-token

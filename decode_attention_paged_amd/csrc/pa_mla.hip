@@ -148,6 +148,9 @@ __device__ __forceinline__ uint32_t lds_addr(const lds_char* p) {
 __device__ __forceinline__ void ds_store_b64(lds_char* p, u32x2 v) {
   asm volatile("ds_write_b64 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
 }
+__device__ __forceinline__ void ds_store_b128(lds_char* p, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(lds_addr(p)), "v"(v) : "memory");
+}
 
 __device__ __forceinline__ u32x2 lds_tr16(const lds_char* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)p));
@@ -893,6 +896,49 @@ __device__ __forceinline__ i32x4 wide_rsrc(ChunkSource<kWideNW, 64>& src, int ci
   return raw_rsrc(base, min(src.t1 - tok0, kCT) * kRowB);
 }
 
+// FP8 latent caches (one E4M3 code per element: a 64-token page is 36864
+// bytes, the size of a bf16 chunk).  Whole pages stream linearly into two
+// staging slots (load j of a page: bytes 1024 j .. +1023, wave w issues
+// j = w + 4i), two pages ahead; each step widens the 32 rows of its chunk
+// (half a page) into the bf16 chunk layout above, so the score and value
+// products run unchanged.  The page's record count bounds it: rows past the
+// split's end read zeros.
+constexpr int kPageB8 = 64 * kDqk;                   // 36864 bytes per FP8 page
+static_assert(kPageB8 == kChunkB, "an FP8 page fills a chunk slot");
+__device__ __forceinline__ i32x4 page8_rsrc(ChunkSource<kWideNW, 64>& src, int g) {
+  const int tok0 = src.t0 + 64 * g;
+  if (tok0 >= src.t1) return raw_rsrc(src.cbase, 0);
+  const char* base = src.cbase + (size_t)src.page_of(2 * g) * kPageB8;
+  return raw_rsrc(base, min(src.t1 - tok0, 64) * kDqk);
+}
+// Load k (0 .. 8) of this wave's share of a page into staging slot dst.
+__device__ __forceinline__ void page8_issue(const i32x4& rsrc, lds_char* dst, int w, int lane,
+                                            int k) {
+  const int j = w + kWideNW * k;
+  dma16_buf(rsrc, 1024 * j + 16 * lane, dst + 1024 * j);
+}
+__device__ __forceinline__ void page8_issue_all(const i32x4& rsrc, lds_char* dst, int w, int lane) {
+#pragma unroll
+  for (int k = 0; k < kDmaInst / kWideNW; ++k) page8_issue(rsrc, dst, w, lane, k);
+}
+// Widen rows 32h .. 32h+31 of a staged page into a bf16 chunk buffer: wave w
+// takes the 8-byte pieces m = 64 j + lane (j = w + 4i) of the half, piece m
+// being elements 8 (m % 72) .. +7 of row m / 72, i.e. 16-byte chunk m % 72
+// of that bf16 row (stored at chunk ^ wide_key(row)).
+__device__ __forceinline__ void widen_half(const lds_char* stg, int h, lds_char* dst, int w,
+                                           int lane) {
+  // addresses derived afresh each call (an opaque copy of the lane id), not
+  // kept in registers across the chunk loop
+  asm volatile("" : "+v"(lane));
+#pragma unroll
+  for (int i = 0; i < kDmaInst / kWideNW; ++i) {
+    const int m = 64 * (w + kWideNW * i) + lane;
+    const u32x2 c8 = *(const __attribute__((address_space(3))) u32x2*)(stg + 18432 * h + 8 * m);
+    const int t = m / (kRowB / 16), c = m - t * (kRowB / 16);
+    ds_store_b128(dst + t * kRowB + 16 * (c ^ wide_key(t)), fp8x8_to_bf16x8(c8[0], c8[1]));
+  }
+}
+
 struct WideState {
   u32x4 qf[kWideKS];                  // Q^T B operands of heads 32w .. 32w+31
   f32x16 acc[kWideMB][kWideNB];       // O^T: dims 128w + 32mb .., heads 32nb ..
@@ -1040,6 +1086,9 @@ __device__ __forceinline__ void wide_values(WideState& st, const lds_char* buf, 
   }
 }
 
+// F8: FP8 E4M3 latent cache (two bf16 chunk slots plus two FP8 page slots in
+// the same LDS; see page8_issue and widen_half).
+template <bool F8>
 __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
   __shared__ __attribute__((aligned(16))) char ring_lds[kRing * kChunkB];
   __shared__ __attribute__((aligned(16))) char pl_lds[2 * kWidePB];
@@ -1068,7 +1117,9 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
 
   lds_char* const ring = (lds_char*)ring_lds;
   lds_char* const pl = (lds_char*)pl_lds;
-  auto slot = [&](int ci) { return ring + (ci % kRing) * kChunkB; };
+  constexpr int kSlots = F8 ? 2 : kRing;              // bf16 chunk slots
+  auto slot = [&](int ci) { return ring + (ci % kSlots) * kChunkB; };
+  auto stg = [&](int g) { return ring + (2 + (g & 1)) * kChunkB; };   // FP8 page slots
   auto pbuf = [&](int ci) { return pl + (ci & 1) * kWidePB; };
   ChunkSource<kWideNW, 64> src;
   src.bt = p.block_table + (size_t)b * p.maxb;
@@ -1094,19 +1145,28 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
     // 32 rows with 32 bytes each.
     const char* qb = static_cast<const char*>(p.q) + row0 * kRowB;
 #pragma unroll
-    for (int i = 0; i < kRing; ++i) ld.issue_all(raw_rsrc(qb + i * kChunkB, kChunkB), slot(i));
+    for (int i = 0; i < kRing; ++i)
+      ld.issue_all(raw_rsrc(qb + i * kChunkB, kChunkB), ring + i * kChunkB);
     wait_vm<0>();
     lds_barrier();
-    const WideRowReads load_q(slot(w), lane);
+    const WideRowReads load_q(ring + w * kChunkB, lane);
 #pragma unroll
     for (int kb = 0; kb < kWideKS; ++kb) st.qf[kb] = load_q(kb);
     lds_barrier();                                    // every wave holds its queries
   }
   // Every chunk is loaded, also past the split's end (those loads write
   // zeros), so the count in flight is the same at every step.
-  src.begin(s * p.c);
-  ld.issue_all(wide_rsrc(src, 0), slot(0));
-  ld.issue_all(wide_rsrc(src, 1), slot(1));
+  auto issue_first_two = [&]() {
+    src.begin(s * p.c);
+    if constexpr (F8) {
+      page8_issue_all(page8_rsrc(src, 0), stg(0), w, lane);
+      page8_issue_all(page8_rsrc(src, 1), stg(1), w, lane);
+    } else {
+      ld.issue_all(wide_rsrc(src, 0), slot(0));
+      ld.issue_all(wide_rsrc(src, 1), slot(1));
+    }
+  };
+  issue_first_two();
   st.m = kNegInf;
   st.mtop = kNegInf;
   for (bool first = true;; first = false) {
@@ -1119,11 +1179,37 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
         for (int i = 0; i < 16; ++i) st.acc[mb][nb][i] = 0.f;
       }
     st.bad = false;
-    if (!first) {
-      src.begin(s * p.c);
-      ld.issue_all(wide_rsrc(src, 0), slot(0));
-      ld.issue_all(wide_rsrc(src, 1), slot(1));
-    }
+    if (!first) issue_first_two();
+    if constexpr (F8) {
+      // Page g (chunks 2g, 2g+1) is issued at step 2g - 3 into FP8 slot
+      // g % 2, freed when step 2g - 1 has widened its second half; step ci
+      // widens its chunk into bf16 slot ci % 2, whose last reader was the
+      // value product of ci - 2 (step ci - 1), between two barriers.
+      auto widen = [&](int ci) {
+        if ((ci & 1) == 0) wait_vm<kNwi>();           // page ci / 2 (the next one may be in flight)
+        lds_barrier();
+        widen_half(stg(ci >> 1), ci & 1, slot(ci), w, lane);
+        lds_barrier();
+        if (ci & 1) page8_issue_all(page8_rsrc(src, (ci + 3) >> 1), stg((ci + 3) >> 1), w, lane);
+      };
+      if (nchunks > 0) {
+        widen(0);
+        f32x16 s0, s1;
+        wide_score_mfma(st, slot(0), lane, s0, s1, [&](int) {});
+        float v[16];
+        wide_scores_max(st, s0, s1, v, lane, t0, t1, cs);
+        wide_weights(st, v, pbuf(0), w, lane, cs);
+      }
+      for (int ci = 1; ci < nchunks; ++ci) {
+        widen(ci);
+        f32x16 s0, s1;
+        wide_score_mfma(st, slot(ci), lane, s0, s1, [&](int) {});
+        float v[16];
+        wide_scores_max(st, s0, s1, v, lane, t0 + ci * kCT, t1, cs);
+        wide_values(st, slot(ci - 1), pbuf(ci - 1), vb, lane);
+        wide_weights(st, v, pbuf(ci), w, lane, cs);
+      }
+    } else {
     wait_vm<kNwi>();                                  // chunk 0 (chunk 1 may be in flight)
     lds_barrier();
     if (nchunks > 0) {
@@ -1155,12 +1241,13 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
       wide_values(st, slot(ci - 1), pbuf(ci - 1), vb, lane);
       wide_weights(st, v, pbuf(ci), w, lane, cs);
     }
+    }
     if (nchunks > 0) {
       lds_barrier();                                  // the last chunk's probabilities
       wide_values(st, slot(nchunks - 1), pbuf(nchunks - 1), vb, lane);
     }
     // Did any head's chunk max overflow the headroom over its reference max?
-    wait_vm<0>();                                     // the two chunks loaded past the split's end
+    wait_vm<0>();                                     // the loads past the split's end
     lds_barrier();
     int* votes = (int*)ring_lds;
     if (lane == 0) votes[w] = __builtin_amdgcn_ballot_w64(st.bad) != 0;
@@ -1203,7 +1290,8 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
   for (int nb = 0; nb < kWideNB; ++nb) {
     const int h = 32 * nb + re;
     const float mm = stat_m[h];
-    const float inv = (mm == kNegInf) ? 0.f : 1.f / stat_l[h];
+    // (v_scale: the factor of every FP8 value, 1 for bf16 caches)
+    const float inv = (mm == kNegInf) ? 0.f : p.v_scale / stat_l[h];
 #pragma unroll
     for (int mb = 0; mb < kWideMB; ++mb) {
 #pragma unroll
@@ -1250,10 +1338,11 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
   }
 }
 
+template <bool F8>
 hipError_t launch_wide(const Params& p, hipStream_t st) {
   const long blocks = (long)(p.ql * p.Hq / kWideNH) * p.S * p.B;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mla_wide_partial, dim3((unsigned)blocks), dim3(kWideNW * 64), 0, st, p);
+  hipLaunchKernelGGL(mla_wide_partial<F8>, dim3((unsigned)blocks), dim3(kWideNW * 64), 0, st, p);
   return hipGetLastError();
 }
 
@@ -1264,6 +1353,10 @@ bool mla_mfma_supported(bool bf16, int Dqk, int Dv, int bs, int Hq) {
          (Hq % 64 == 0 || Hq == 32 || Hq == 16);
 }
 
+bool mla_mfma_fp8_supported(int Dqk, int Dv, int bs, int Hq) {
+  return Dqk == kDqk && Dv == kDv && bs == 64 && Hq % kWideNH == 0;
+}
+
 int mla_heads_per_workgroup(int Hq, int bs) {
   if (bs == 64 && Hq % kWideNH == 0) return kWideNH;
   return Hq % 64 == 0 ? 64 : Hq;
@@ -1271,8 +1364,12 @@ int mla_heads_per_workgroup(int Hq, int bs) {
 
 int mla_max_split_tokens(int bs) { return bs == 1 ? kMaxIdsBS1 : 0x7fffffff; }
 
-hipError_t launch_mla_mfma(const Params& p, hipStream_t st) {
-  if (p.bs == 64 && p.Hq % kWideNH == 0) return launch_wide(p, st);
+hipError_t launch_mla_mfma(const Params& p, bool fp8kv, hipStream_t st) {
+  if (fp8kv) {
+    if (!mla_mfma_fp8_supported(p.D, p.Dv, p.bs, p.Hq)) return hipErrorInvalidValue;
+    return launch_wide<true>(p, st);
+  }
+  if (p.bs == 64 && p.Hq % kWideNH == 0) return launch_wide<false>(p, st);
   if (p.Hq % 64 == 0) return launch_roles<2, 2>(p, st);
   if (p.Hq == 32) return launch_roles<2, 1>(p, st);
   if (p.Hq == 16) return launch_roles<1, 1>(p, st);

@@ -135,15 +135,23 @@ def test_fp8_scales_checked(lib, ks, vs):
 def test_fp8_shapes_pass_validation(lib):
     """FP8 caches with bf16 queries validate (the workspace check fails first,
     so nothing launches); an explicit cache dtype equal to the query's is the
-    default; the latent (MLA) path has no FP8 kernel."""
+    default; FP8 latent caches take 128-head groups on 64-token pages."""
     for kw in (dict(), dict(num_kv_heads=2), dict(q_len=2), dict(block_size=32, max_context_len=200)):
         s = shape(kv_dtype=_lib.PA_FP8_E4M3, k_scale=0.02, v_scale=3.0, **kw)
         assert decode(lib, s, splits=4) == _lib.PA_ERR_WORKSPACE, kw
     assert decode(lib, shape(kv_dtype=_lib.PA_BF16), splits=4) == _lib.PA_ERR_WORKSPACE
-    m = shape(num_q_heads=128, num_kv_heads=1, head_dim=576, head_dim_v=512, block_size=64,
-              max_context_len=300, kv_dtype=_lib.PA_FP8_E4M3, k_scale=0.1, v_scale=0.1)
-    assert lib.pa_decode_mla(ctypes.byref(m), FAKE, FAKE, FAKE, FAKE, 1, FAKE, NULL, NULL, 0,
-                             NULL) == _lib.PA_ERR_UNSUPPORTED
+    def mla(**kw):
+        base = dict(num_q_heads=128, num_kv_heads=1, head_dim=576, head_dim_v=512, block_size=64,
+                    max_context_len=300, kv_dtype=_lib.PA_FP8_E4M3, k_scale=0.1, v_scale=0.1)
+        base.update(kw)
+        m = shape(**base)
+        return lib.pa_decode_mla(ctypes.byref(m), FAKE, FAKE, FAKE, FAKE, 4, FAKE, NULL, NULL, 0,
+                                 NULL)
+    for kw in (dict(), dict(num_q_heads=256), dict(q_len=2)):
+        assert mla(**kw) == _lib.PA_ERR_WORKSPACE, kw
+    for kw in (dict(num_q_heads=64), dict(num_q_heads=16), dict(block_size=1, max_blocks_per_seq=300),
+               dict(dtype=_lib.PA_F32)):
+        assert mla(**kw) == _lib.PA_ERR_UNSUPPORTED, kw
 
 
 def test_several_rows_supported(lib):
@@ -303,10 +311,12 @@ def test_append_null_pointers(lib):
         assert append_latent(lib, ms, **{kw: NULL}) == _lib.PA_ERR_INVALID, kw
     # the latent pool has one KV head
     assert append_latent(lib, shape(num_kv_heads=2, num_q_heads=2)) == _lib.PA_ERR_INVALID
-    # no latent decode reads FP8 codes, so the latent append refuses them
-    assert append_latent(lib, shape(num_q_heads=1, num_kv_heads=1, head_dim=576, head_dim_v=576,
-                                    block_size=64, kv_dtype=_lib.PA_FP8_E4M3)) == \
-        _lib.PA_ERR_UNSUPPORTED
+    # FP8 latent rows only in the layout the FP8 latent decode reads
+    for kw in (dict(head_dim=512, head_dim_v=512), dict(block_size=1)):
+        base = dict(num_q_heads=1, num_kv_heads=1, head_dim=576, head_dim_v=576, block_size=64,
+                    kv_dtype=_lib.PA_FP8_E4M3)
+        base.update(kw)
+        assert append_latent(lib, shape(**base)) == _lib.PA_ERR_UNSUPPORTED, kw
 
 
 def test_append_grid_limits(lib):

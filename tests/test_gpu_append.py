@@ -31,6 +31,10 @@ CASES = {
     "mla_bf16": dict(kind="mla", dtype="bf16", batch=3, num_q_heads=16, num_kv_heads=1,
                      head_dim=576, head_dim_v=512, block_size=64, context_lens=[65, 64, 1],
                      num_blocks=12, scale=192 ** -0.5),
+    "mla_fp8": dict(kind="mla", dtype="bf16", batch=3, num_q_heads=128, num_kv_heads=1,
+                    head_dim=576, head_dim_v=512, block_size=64, context_lens=[65, 64, 1],
+                    num_blocks=12, scale=192 ** -0.5, kv_dtype="fp8", k_scale=0.05,
+                    v_scale=0.06),
 }
 
 
@@ -83,12 +87,12 @@ def test_append_then_decode(name):
         page = int(full.block_table[b, n // full.block_size])
         slot = n % full.block_size
         if full.kind == "mla":
-            t_before["kv_cache"][page, slot, :] = float("nan")
+            _poison(t_before["kv_cache"], (page, slot, slice(None)))
         else:
             _poison(t_before["k_cache"], (page, slice(None), slot, slice(None)))
             _poison(t_before["v_cache"], (page, slice(None), slice(None), slot))
     if full.kind == "mla":
-        c_new = _dev(np.stack([r[0] for r in rows]), full.dtype)
+        c_new = _dev(np.stack([r[0] for r in rows]), full.kv_dtype or full.dtype)
         pa.append_latent(c_new, t_before["kv_cache"], t_before["block_table"],
                          t_before["context_lens"])
         torch.cuda.synchronize()
@@ -105,11 +109,11 @@ def test_append_then_decode(name):
     # the caller advances the lengths, then decodes the new token
     t_before["context_lens"] += 1
     ref_out, ref_lse = oracle.decode_inputs(full)
+    fp8 = dict(k_scale=full.k_scale, v_scale=full.v_scale) if full.kv_dtype == "fp8" else {}
     if full.kind == "mla":
         out, lse = pa.decode_mla(t_before["q"], t_before["kv_cache"], t_before["block_table"],
-                                 t_before["context_lens"], scale=full.scale, num_splits=2)
+                                 t_before["context_lens"], scale=full.scale, num_splits=2, **fp8)
     else:
-        fp8 = dict(k_scale=full.k_scale, v_scale=full.v_scale) if full.kv_dtype == "fp8" else {}
         out, lse = pa.decode(t_before["q"], t_before["k_cache"], t_before["v_cache"],
                              t_before["block_table"], t_before["context_lens"],
                              scale=full.scale, num_splits=2, **fp8)

@@ -39,12 +39,12 @@ def say(msg):
 def run(inp, t=None, num_splits=0, poison=True):
     if t is None:
         t = to_device(inp, "cuda", poison)
+    fp8 = dict(k_scale=inp.k_scale, v_scale=inp.v_scale) if inp.kv_dtype == "fp8" else {}
     if inp.kind == "mla":
         out, lse = pa.decode_mla(t["q"], t["kv_cache"], t["block_table"], t["context_lens"],
                                  max_context_len=inp.max_context_len, scale=inp.scale,
-                                 head_dim_v=inp.head_dim_v, num_splits=num_splits)
+                                 head_dim_v=inp.head_dim_v, num_splits=num_splits, **fp8)
     else:
-        fp8 = dict(k_scale=inp.k_scale, v_scale=inp.v_scale) if inp.kv_dtype == "fp8" else {}
         out, lse = pa.decode(t["q"], t["k_cache"], t["v_cache"], t["block_table"],
                              t["context_lens"], max_context_len=inp.max_context_len,
                              scale=inp.scale, num_splits=num_splits, **fp8)
@@ -228,11 +228,16 @@ def test_several_rows(name):
 
 
 # ----------------------------------------------------------------------------------------------
-# FP8 E4M3 caches with bf16 queries (both kernels, one and several rows): every output compared.
-# Unused pages and tail slots hold the FP8 NaN code.
+# FP8 E4M3 caches with bf16 queries (both kernels, one and several rows; the latent kernel on
+# 128-head groups): every output compared.  Unused pages and tail slots hold the FP8 NaN code.
 # ----------------------------------------------------------------------------------------------
 
 FP8_KV = dict(kv_dtype="fp8", k_scale=0.037, v_scale=1.9)
+# One latent row holds keys and values: codes are N(0,1) / k_scale, so v_scale near k_scale
+# keeps the values (and outputs) near unit size, where the absolute bound applies.
+FP8_LATENT = dict(kv_dtype="fp8", k_scale=0.037, v_scale=0.045)
+MLA_DIMS = dict(kind="mla", dtype="bf16", num_kv_heads=1, head_dim=576, head_dim_v=512,
+                block_size=64, scale=192 ** -0.5)
 FP8 = {
     "fp8_mha_bs16": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=4, num_kv_heads=4,
                          head_dim=128, block_size=16, context_lens=[1, 37, 300], num_blocks=64,
@@ -254,6 +259,14 @@ FP8 = {
     "fp8_rows_gqa_g4_q4": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=8, num_kv_heads=2,
                                head_dim=128, block_size=16, context_lens=[2, 17, 333],
                                num_blocks=60, q_len=4, **FP8_KV),
+    # pages of one, two and eleven (the last ragged) with a one-token sequence
+    "fp8_mla_h128": dict(MLA_DIMS, batch=3, num_q_heads=128, context_lens=[1, 100, 700],
+                         num_blocks=24, **FP8_LATENT),
+    # two head groups; a context of exactly one page
+    "fp8_mla_h256": dict(MLA_DIMS, batch=2, num_q_heads=256, context_lens=[64, 129],
+                         num_blocks=8, **FP8_LATENT),
+    "fp8_rows_mla_h128_q3": dict(MLA_DIMS, batch=2, num_q_heads=128, context_lens=[3, 300],
+                                 num_blocks=10, q_len=3, **FP8_LATENT),
 }
 
 
@@ -262,7 +275,7 @@ def test_fp8_kv(name):
     inp = make_paged_inputs(name=name, seed=400 + sorted(FP8).index(name), **FP8[name])
     ref_out, ref_lse = oracle.decode_inputs(inp)
     t = to_device(inp, "cuda", poison=True)
-    assert t["k_cache"].dtype == torch.float8_e4m3fn
+    assert t["kv_cache" if inp.kind == "mla" else "k_cache"].dtype == torch.float8_e4m3fn
     P = -(-inp.max_context_len // inp.block_size)
     for S in [0, 1, 2, 3, 7, P + 5]:
         say(f"{name} S={S}")
@@ -277,7 +290,7 @@ def test_fp8_kv(name):
 
 FULL = ["tiny_mha_f32", "llama_mha_bf16", "long_gqa_bf16", "ragged_gqa_bf16", "mla_bf16",
         "mla_topk_bf16", "mla_allentries_bf16", "llama_mha_q4_bf16", "long_gqa_q4_bf16",
-        "mla_q2_bf16", "llama_mha_fp8", "long_gqa_fp8", "ragged_gqa_fp8"]
+        "mla_q2_bf16", "llama_mha_fp8", "long_gqa_fp8", "ragged_gqa_fp8", "mla_fp8"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -320,6 +333,8 @@ PROP_MLA = dict(kind="mla", dtype="bf16", batch=2, num_q_heads=32, num_kv_heads=
                 scale=192 ** -0.5)
 # 128 heads on 64-token pages: the wide latent workgroup
 PROP_MLA128 = dict(PROP_MLA, num_q_heads=128)
+# the same on an FP8 latent cache
+PROP_MLA128_FP8 = dict(PROP_MLA128, kv_dtype="fp8", k_scale=0.037, v_scale=0.045)
 
 
 def _permuted(t, inp, seed):
@@ -328,16 +343,19 @@ def _permuted(t, inp, seed):
     u = dict(t)
     for key in ("k_cache", "v_cache", "kv_cache"):
         if key in t:
-            pool = torch.empty_like(t[key])
-            pool[perm] = t[key]
-            u[key] = pool
+            src = t[key]
+            if src.dtype == torch.float8_e4m3fn:       # move FP8 pages as bytes
+                src = src.view(torch.uint8)
+            pool = torch.empty_like(src)
+            pool[perm] = src
+            u[key] = pool.view(t[key].dtype)
     bt = t["block_table"].long()
     u["block_table"] = torch.where(bt >= 0, perm[bt.clamp(min=0)], bt).to(torch.int32)
     return u
 
 
-@pytest.mark.parametrize("spec", [PROP, PROP_MHA, PROP_MLA, PROP_MLA128],
-                         ids=["gqa", "mha", "mla", "mla128"])
+@pytest.mark.parametrize("spec", [PROP, PROP_MHA, PROP_MLA, PROP_MLA128, PROP_MLA128_FP8],
+                         ids=["gqa", "mha", "mla", "mla128", "mla128_fp8"])
 @pytest.mark.parametrize("S", [0, 1, 5])
 def test_page_permutation_bitwise(spec, S):
     inp = make_paged_inputs(seed=11, **spec)
@@ -428,7 +446,8 @@ def test_identical_keys_give_mean_of_values(spec):
     assert np.abs(from_device(out)[b] - want).max() <= 2e-2
 
 
-@pytest.mark.parametrize("spec", [PROP, PROP_MHA, PROP_MLA], ids=["gqa", "mha", "mla"])
+@pytest.mark.parametrize("spec", [PROP, PROP_MHA, PROP_MLA, PROP_MLA128_FP8],
+                         ids=["gqa", "mha", "mla", "mla128_fp8"])
 def test_empty_context(spec):
     s = dict(spec, context_lens=[0] + list(spec["context_lens"][1:]))
     inp = make_paged_inputs(seed=15, **s)
@@ -561,3 +580,30 @@ def test_rising_scores(spec):
         say(f"rising scores {inp.kind} S={S}")
         out, lse = run(inp, t, num_splits=S)
         compare(inp, out, lse, ref_out, ref_lse, f"rising scores S={S}")
+
+
+def test_rising_scores_fp8_latent():
+    """The rising-scores case on an FP8 latent cache: the codes of a key-only
+    dim climb with the token index (a quarter of it, rounded to E4M3), and the
+    query's weight on that dim makes each 32-token chunk's max exceed the
+    previous one by far more than the headroom, so the wide kernel starts its
+    splits over with a raised reference max."""
+    lens = [1000, 77]
+    s = dict(PROP_MLA128_FP8, context_lens=lens, k_scale=0.25, v_scale=0.3,
+             num_blocks=sum(-(-n // 64) for n in lens) + 10)
+    inp = make_paged_inputs(seed=19, **s)
+    bt = inp.compact_block_table()
+    d = inp.head_dim - 1
+    codes = torch.from_numpy(np.arange(max(lens), dtype=np.float32) / 4).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for b in range(inp.batch):
+        for tok in range(int(inp.context_lens[b])):
+            inp.c_pages[bt[b, tok // 64], tok % 64, d] = codes[tok]
+    from workloads import f32_to_bf16_bits
+    inp.q[:, :, d] = f32_to_bf16_bits(np.array([256.0], np.float32))[0]
+    ref_out, ref_lse = oracle.decode_inputs(inp)
+    t = to_device(inp, "cuda")
+    for S in (1, 3, 0):
+        say(f"rising scores fp8 latent S={S}")
+        out, lse = run(inp, t, num_splits=S)
+        compare(inp, out, lse, ref_out, ref_lse, f"rising scores fp8 latent S={S}")

@@ -184,7 +184,7 @@ def make_paged_inputs(*, name: str = "custom", kind: str = "mha", dtype: str = "
     if dtype not in ("f32", "bf16"):
         raise ValueError(dtype)
     fp8 = kv_dtype == "fp8"
-    if kv_dtype not in (None, dtype, "fp8") or (fp8 and (dtype != "bf16" or kind == "mla")):
+    if kv_dtype not in (None, dtype, "fp8") or (fp8 and dtype != "bf16"):
         raise ValueError(f"cache dtype {kv_dtype} with {dtype} queries / {kind}")
     if kind == "mla":
         num_kv_heads = 1
@@ -235,7 +235,12 @@ def make_paged_inputs(*, name: str = "custom", kind: str = "mha", dtype: str = "
         off += n
 
     if kind == "mla":
-        c = _Draw(rng).normal(total * block_size * dq, dtype).reshape(total, block_size, dq)
+        if fp8:        # one code row per token, codes of value / k_scale
+            nan = np.uint8(FP8_NAN_CODE)
+            c = _Draw(rng).normal_fp8(total * block_size * dq, k_scale)
+        else:
+            c = _Draw(rng).normal(total * block_size * dq, dtype)
+        c = c.reshape(total, block_size, dq)
         if poison:
             c[tail] = nan
         inp.c_pages = c
@@ -353,6 +358,12 @@ CONFIGS = {
         kv_dtype="fp8", k_scale=0.017, v_scale=0.019,
         meta=dict(desc="long-context GQA, FP8 E4M3 KV (bf16 q): B1, 32 q / 8 kv heads, D128, "
                        "ctx 131072, bs16")),
+    "mla_fp8": dict(
+        kind="mla", dtype="bf16", batch=32, num_q_heads=128, num_kv_heads=1, head_dim=576,
+        head_dim_v=512, block_size=64, context_lens=[8192] * 32, num_blocks=4096,
+        scale=1.0 / math.sqrt(192), seed=5, kv_dtype="fp8", k_scale=0.02, v_scale=0.02,
+        meta=dict(desc="MLA latent, FP8 E4M3 cache (bf16 q): B32, 128 heads, latent 576 "
+                       "(V = first 512), ctx 8192, bs64")),
     "ragged_gqa_fp8": dict(
         kind="mha", dtype="bf16", batch=64, num_q_heads=64, num_kv_heads=8, head_dim=128,
         block_size=16, context_lens=_loguniform_ctx(128, 32768, 64), num_blocks=65536,
@@ -364,7 +375,7 @@ CONFIGS = {
 
 CONFIG_ORDER = ["tiny_mha_f32", "llama_mha_bf16", "long_gqa_bf16", "ragged_gqa_bf16", "mla_bf16",
                 "mla_topk_bf16", "mla_allentries_bf16", "llama_mha_q4_bf16", "long_gqa_q4_bf16",
-                "mla_q2_bf16", "llama_mha_fp8", "long_gqa_fp8", "ragged_gqa_fp8"]
+                "mla_q2_bf16", "llama_mha_fp8", "long_gqa_fp8", "ragged_gqa_fp8", "mla_fp8"]
 
 
 def make_config(name: str, *, poison: bool = True, values: bool = True, seed: int | None = None,

@@ -55,7 +55,8 @@ def to_device(inp, device="cuda", poison: bool = True) -> dict:
         "context_lens": torch.from_numpy(inp.context_lens.astype(np.int32)).to(device),
     }
     if inp.kind == "mla":
-        t["kv_cache"] = _pool(inp.c_pages, inp.page_ids, inp.num_blocks, inp.dtype, device, poison)
+        t["kv_cache"] = _pool(inp.c_pages, inp.page_ids, inp.num_blocks, inp.kv_dtype or inp.dtype,
+                              device, poison)
     else:
         kvd = inp.kv_dtype or inp.dtype
         t["k_cache"] = _pool(inp.k_pages, inp.page_ids, inp.num_blocks, kvd, device, poison)
