@@ -42,7 +42,7 @@ CSRC = os.path.join(ROOT, "decode_attention_paged_amd", "csrc")
 # the sources each partial kernel is compiled from (its file and the headers it includes)
 KERNEL_SOURCES = {
     "mha": ("pa_mha.hip", "pa_device.h", "pa_launch.h", "pa_merge.h"),
-    "gqa": ("pa_gqa.hip", "pa_device.h", "pa_launch.h", "pa_merge.h"),
+    "gqa": ("pa_gqa.hip", "pa_sched.hip", "pa_device.h", "pa_launch.h", "pa_merge.h"),
     "mla": ("pa_mla.hip", "pa_device.h", "pa_launch.h"),
 }
 
@@ -156,7 +156,8 @@ class Case:
         # kernel and the reduction (pa_decode_launches says which).  Two-launch
         # calls are made here as the two calls they consist of, so that each
         # kernel can be timed alone.
-        self.fused = pa.decode_launches(self.shape, self.S, self.mla) == 1
+        self.launches = pa.decode_launches(self.shape, self.S, self.mla)
+        self.fused = self.launches == 1
         if self.mla:
             kv = P(t["kv_cache"].data_ptr())
             self._partial = (lib.pa_decode_mla_partial,
@@ -276,6 +277,8 @@ class Case:
             "traffic": traffic,
             "traffic_over_algorithmic": None if traffic is None else round(traffic / self.kv_bytes, 4),
             "kernel": (f"{self.family} split-KV kernel with fused reduction" if self.fused
+                       else f"{self.family} partial step: unit-order launch + partial kernel "
+                            "(the reduction is a third launch)" if self.launches == 3
                        else f"{self.family} partial kernel (the reduction is a second launch)"),
             "algorithmic_bytes_per_launch": self.kv_bytes,
             "avg_launch_ms": round(partial_ms, 5),

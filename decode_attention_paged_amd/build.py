@@ -34,8 +34,8 @@ COMMON_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
-SOURCES = ["pa_api.hip", "pa_mha.hip", "pa_gqa.hip", "pa_mla.hip", "pa_reduce.hip", "pa_append.hip",
-           "pa_probe.hip"]
+SOURCES = ["pa_api.hip", "pa_mha.hip", "pa_gqa.hip", "pa_sched.hip", "pa_mla.hip", "pa_reduce.hip",
+           "pa_append.hip", "pa_probe.hip"]
 
 
 def hipcc() -> str:

@@ -16,6 +16,8 @@ constexpr long kFusedMergeBytes = 4 * 1024;   // largest per-unit partial set me
 constexpr double kSplitBytesValu = 128.0 * 1024.0;   // KV bytes per workgroup, VALU kernel
 constexpr double kSplitBytesMfma = 1024.0 * 1024.0;  // KV bytes per workgroup, MFMA kernel
 constexpr int kMinSplitsLong = 8;                    // splits of the longest sequence (MFMA kernel, full grid)
+constexpr int kSchedSplitsLong = 10;                 // the same when the units run longest first
+constexpr double kScheduleUnitBytes = 384.0 * 1024.0;  // smallest unit (KV bytes) run longest first
 constexpr double kMinSplitBytesValu = 32.0 * 1024.0;  // fewest KV bytes per workgroup, VALU kernel
 constexpr double kMinSplitBytesMfma = 64.0 * 1024.0;  // fewest KV bytes per workgroup, MFMA kernel
 constexpr int kMaxQLen = 16;                         // query rows per sequence
@@ -172,10 +174,20 @@ int heuristic_splits(const pa_shape& s, int cus, bool mla) {
     // units differ in length, and workgroups as long as a whole short-batch
     // sequence leave a tail: the longest sequence gets at least kMinSplitsLong
     // splits (Llama-style MHA with 4 query rows on the MFMA kernel: 8 splits,
-    // 110 us against 116 at 2; the ragged batch keeps its 16).
+    // 110 us against 116 at 2).
     if (k == Kernel::GqaMfma && units >= cus) {
       const int c_long = (P + kMinSplitsLong - 1) / kMinSplitsLong;
       if (c > c_long) c = c_long;
+      // Several sequences with large units run longest first (uses_schedule),
+      // so a late unit no longer sets the tail and splits can be larger:
+      // kSchedSplitsLong for the longest sequence.  The ragged batch: 350.6 us
+      // at 10 splits against 357.5 at 15 (FP8 183.3 against 190.0); four
+      // other draws of it: -2.9 % to +1.2 % (mean -1.4 %) against 15 splits,
+      // while the best count varied from 7 to 10.
+      const int c_sched = (P + kSchedSplitsLong - 1) / kSchedSplitsLong;
+      if (s.batch > 1 && c_sched > c &&
+          (double)c_sched * s.block_size * (s.head_dim + s.head_dim_v) * esz >= kScheduleUnitBytes)
+        c = c_sched;
     }
     if (c < c_min) c = c_min;
     S = (P + c - 1) / c;
@@ -231,9 +243,32 @@ size_t ws_lse_offset(const pa_shape& s, int S, bool mla) {
   const size_t esz = part_bf16(s, mla) ? sizeof(uint16_t) : sizeof(float);
   return ws_opart_offset(s) + align_up(ws_rows(s) * S * s.head_dim_v * esz);
 }
+// A batch of several sequences on the grouped-query kernel runs its units in
+// the order a schedule launch writes after lse_part: u32 [B * S] (pa_sched.hip),
+// longest first, so that no long unit starts late and leaves a tail.  The
+// launch costs ~6 us on MI355X, so it is used only where a unit can leave a
+// tail much longer than that: units of at least kScheduleUnitBytes of KV
+// (~30 us each at the per-workgroup share of HBM bandwidth; the ragged
+// batch's bf16 units are 1 MiB: 370.7 -> 359.2 us, FP8 0.5 MiB: 201.4 ->
+// 190.7 us; Llama-style MHA with 4 rows, 256 KiB units of near-equal
+// sequences: 115.1 -> 116.8 us, so it keeps the plain grid order).
+bool fuses(const pa_shape& s, int S, Kernel kern);
+bool uses_schedule(const pa_shape& s, int S, bool mla) {
+  if (S <= 1 || s.batch <= 1 || pick_kernel(s, mla) != Kernel::GqaMfma) return false;
+  // a call that merges in-kernel stays one launch (its units are tiny anyway)
+  if (fuses(s, S, Kernel::GqaMfma)) return false;
+  if ((long long)s.batch * S >= (1LL << 31)) return false;
+  const long long c = (max_pages(s) + S - 1) / S;
+  const int esz = fp8_kv(s) ? 1 : (s.dtype == PA_BF16 ? 2 : 4);
+  return (double)c * s.block_size * (s.head_dim + s.head_dim_v) * esz >= kScheduleUnitBytes;
+}
+size_t ws_sched_offset(const pa_shape& s, int S, bool mla) {
+  return ws_lse_offset(s, S, mla) + align_up(ws_rows(s) * S * sizeof(float));
+}
 size_t workspace_bytes_for(const pa_shape& s, int S, bool mla) {
   if (S <= 1) return 0;
-  return ws_lse_offset(s, S, mla) + align_up(ws_rows(s) * S * sizeof(float));
+  return ws_sched_offset(s, S, mla) +
+         (uses_schedule(s, S, mla) ? align_up((size_t)s.batch * S * sizeof(uint32_t)) : 0);
 }
 
 pa::Params make_params(const pa_shape& s, int S, bool mla, const void* q, const void* k,
@@ -271,6 +306,8 @@ pa::Params make_params(const pa_shape& s, int S, bool mla, const void* q, const 
     else
       p.o_part = reinterpret_cast<float*>(base + ws_opart_offset(s));
     p.lse_part = reinterpret_cast<float*>(base + ws_lse_offset(s, S, mla));
+    if (uses_schedule(s, S, mla))
+      p.sched = reinterpret_cast<uint32_t*>(base + ws_sched_offset(s, S, mla));
   }
   return p;
 }
@@ -334,7 +371,10 @@ pa_status run_partial(const pa_shape* shape, const void* q, const void* k, const
   hipError_t e;
   switch (kern) {
     case Kernel::MhaValu: e = pa::launch_mha_valu(p, shape->dtype == PA_BF16, fp8_kv(*shape), hs); break;
-    case Kernel::GqaMfma: e = pa::launch_gqa_mfma(p, fp8_kv(*shape), hs); break;
+    case Kernel::GqaMfma:
+      e = p.sched ? pa::launch_unit_schedule(p, hs) : hipSuccess;
+      if (e == hipSuccess) e = pa::launch_gqa_mfma(p, fp8_kv(*shape), hs);
+      break;
     case Kernel::MlaMfma: e = pa::launch_mla_mfma(p, fp8_kv(*shape), hs); break;
     default: return PA_ERR_UNSUPPORTED;
   }
@@ -406,7 +446,8 @@ int32_t pa_decode_launches(const pa_shape* shape, int32_t num_splits, int32_t ml
   const int S = resolve_splits(*shape, num_splits, mla != 0);
   if (S < 1) return 0;
   if (S == 1) return 1;
-  return fuses(*shape, S, pick_kernel(*shape, mla != 0)) ? 1 : 2;
+  if (fuses(*shape, S, pick_kernel(*shape, mla != 0))) return 1;
+  return uses_schedule(*shape, S, mla != 0) ? 3 : 2;
 }
 
 int32_t pa_choose_num_splits(const pa_shape* shape, int32_t num_cus, int32_t mla) {

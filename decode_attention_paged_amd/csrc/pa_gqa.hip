@@ -210,8 +210,18 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
   using Tile = typename std::conditional<F8, PairTile8, PairTile>::type;
   constexpr int kT = F8 ? kTile8 : kTile;               // bytes per (page, head) tile
   constexpr int kR = F8 ? kRowB8 : kRowB;               // bytes per K row
-  const int kvh = blockIdx.x, b = blockIdx.z;
-  const int s = split_of_block(blockIdx.y, b, p.S);
+  const int kvh = blockIdx.x;
+  int b, s;
+  if (p.sched) {
+    // the unit order of a ragged batch (longest first; see pa_sched.hip)
+    const uint32_t e = p.sched[blockIdx.z * p.S + blockIdx.y];
+    if (e == kNoUnit) return;
+    b = (int)(e & 0xffffu);
+    s = (int)(e >> 16);
+  } else {
+    b = blockIdx.z;
+    s = split_of_block(blockIdx.y, b, p.S);
+  }
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int quad = lane >> 4, n = lane & 15;

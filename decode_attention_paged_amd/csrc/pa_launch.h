@@ -20,6 +20,8 @@ struct Params {
   uint16_t* o_part16;        // the same layout in bfloat16 (S > 1, MLA matrix-core path), else null
   float* lse_part;           // [B][ql][Hq][S]     (S > 1)
   int32_t* counters;         // [B][Hq] arrival counters of the fused reduction (S > 1, ql == 1)
+  uint32_t* sched;           // grouped-query kernel on a batch: [B * S] unit order, or null
+                             // (entry: sequence | split << 16, kNoUnit for a slot without one)
   int32_t B, Hq, Hkv, D, Dv, bs, maxb, nblocks, max_ctx;
   int32_t ql;                // query rows per sequence (>= 1): rows are (b, j, h), j < ql
   int32_t S;                 // splits in the grid
@@ -31,11 +33,15 @@ struct Params {
   int32_t wg_waves;          // grouped-query kernel: waves per workgroup, 4 or 8
 };
 
+constexpr uint32_t kNoUnit = 0xFFFFFFFFu;
+
 // Each returns hipSuccess or the launch error.  Shapes are validated by the caller.
 hipError_t launch_mha_valu(const Params& p, bool bf16, bool fp8kv, hipStream_t st);
 hipError_t launch_gqa_mfma(const Params& p, bool fp8kv, hipStream_t st);
 hipError_t launch_mla_mfma(const Params& p, bool fp8kv, hipStream_t st);
 hipError_t launch_reduce(const Params& p, bool bf16, hipStream_t st);
+// Writes p.sched (longest units first) from the context lengths; one workgroup.
+hipError_t launch_unit_schedule(const Params& p, hipStream_t st);
 hipError_t launch_zero_i32(int32_t* dst, size_t n, hipStream_t st);
 
 // Arguments of the paged KV append (MLA: k_new / k_cache are the latent

@@ -136,8 +136,12 @@ int32_t pa_choose_num_splits(const pa_shape* shape, int32_t num_cus, int32_t mla
  * Kernel launches a pa_decode / pa_decode_mla call with this shape and split
  * count makes: 1 when S resolves to 1 or the splits are merged inside the
  * partial kernel (MHA/GQA, when a unit's partials are at most 4 KiB), 2 when
- * a separate reduction launch follows (MLA, larger partials).  0 on an
- * invalid shape.  num_splits <= 0 resolves through the heuristic.  Host only.
+ * a separate reduction launch follows (MLA, larger partials), 3 when the
+ * partial kernel is also preceded by the unit-order launch (the grouped-query
+ * kernel on several sequences with units of at least 384 KiB of KV: the
+ * (sequence, split) units then run longest first; see the workspace layout).
+ * 0 on an invalid shape.  num_splits <= 0 resolves through the heuristic.
+ * Host only.
  */
 int32_t pa_decode_launches(const pa_shape* shape, int32_t num_splits, int32_t mla);
 
@@ -145,8 +149,9 @@ int32_t pa_decode_launches(const pa_shape* shape, int32_t num_splits, int32_t ml
  * Bytes of workspace a call with this shape and split count needs: int32
  * arrival counters [R] at offset 0, then partials o[R][S][head_dim_v]
  * (float32; bfloat16 for MLA, whose output is bfloat16 too) and float32
- * lse[R][S], R = batch * q_len * num_q_heads rows, each region 256-byte
- * aligned.  0 when S resolves to 1 (the partial kernel then writes
+ * lse[R][S], R = batch * q_len * num_q_heads rows, and, when the call runs
+ * its units longest first (pa_decode_launches == 3), the unit order u32
+ * [batch][S] (written by the call itself), each region 256-byte aligned.  0 when S resolves to 1 (the partial kernel then writes
  * out/lse directly).  num_splits <= 0 resolves through the heuristic (which
  * may query the device).  Returns 0 on an invalid shape.  Host only.
  *

@@ -162,6 +162,7 @@ def test_several_rows_supported(lib):
         assert decode(lib, s, splits=4) == _lib.PA_ERR_WORKSPACE, kw
         up = lambda x: -(-x // 256) * 256
         rows = 2 * kw["q_len"] * 8
+        # counters, float32 partials, their lse (units of 2 pages: no unit order)
         assert lib.pa_decode_workspace_size(ctypes.byref(s), 4, 0) == \
             up(rows * 4 * 128 * 4) + up(rows * 4 * 4) + up(rows * 4), kw
         # q_len = 0 and 1 both mean one row
@@ -169,6 +170,37 @@ def test_several_rows_supported(lib):
         lib.pa_decode_workspace_size(ctypes.byref(shape(q_len=1)), 4, 0)
     # several rows never fuse the merge into the partial kernel
     assert lib.pa_decode_launches(ctypes.byref(shape(q_len=2)), 2, 0) == 2
+
+
+def test_unit_order_region(lib):
+    """Several sequences on the grouped-query kernel with units of >= 384 KiB
+    of KV get a unit-order table (one u32 per (sequence, split)) after the
+    partials; one sequence, smaller units, or the VALU kernel do not."""
+    up = lambda x: -(-x // 256) * 256
+    def size(**kw):
+        base = dict(batch=4, num_q_heads=16, num_kv_heads=2, max_context_len=6400,
+                    max_blocks_per_seq=400)
+        base.update(kw)
+        s = shape(**base)
+        return lib.pa_decode_workspace_size(ctypes.byref(s), 4, 0), s
+    def plain(B, Hq, S, Dv=128):
+        rows = B * Hq
+        return up(rows * 4) + up(rows * S * Dv * 4) + up(rows * S * 4)
+    # 400 pages, S = 4: c = 100 pages x 16 tokens x 512 B = 800 KiB per unit
+    n, _ = size()
+    assert n == plain(4, 16, 4) + up(4 * 4 * 4)
+    # FP8 halves the unit: 400 KiB, still scheduled
+    n, _ = size(kv_dtype=_lib.PA_FP8_E4M3, k_scale=0.1, v_scale=0.1)
+    assert n == plain(4, 16, 4) + up(4 * 4 * 4)
+    # units of 25 pages (200 KiB): plain order
+    n, s = size(max_context_len=1600, max_blocks_per_seq=100)
+    assert n == plain(4, 16, 4)
+    # one sequence: plain order
+    n, s = size(batch=1)
+    assert n == plain(1, 16, 4)
+    # MHA on the VALU kernel: plain order
+    n, s = size(num_kv_heads=16)
+    assert n == plain(4, 16, 4)
 
 
 def test_workspace_checks(lib):
@@ -326,7 +358,8 @@ def test_append_grid_limits(lib):
 
 def test_decode_launches(lib):
     """One launch when the splits merge in-kernel (small per-unit partials) or
-    S == 1; two when a reduction launch follows; 0 for a bad shape."""
+    S == 1; two when a reduction launch follows; three with the unit-order
+    launch; 0 for a bad shape."""
     def n(s, S, mla=0):
         return lib.pa_decode_launches(ctypes.byref(s), S, mla)
     mha = shape(batch=16, num_q_heads=32, num_kv_heads=32, max_context_len=4096,
@@ -341,6 +374,13 @@ def test_decode_launches(lib):
     mla = shape(batch=32, num_q_heads=128, num_kv_heads=1, head_dim=576, head_dim_v=512,
                 block_size=64, max_context_len=8192, max_blocks_per_seq=128, num_blocks=4096)
     assert n(mla, 4, 1) == 2 and n(mla, 1, 1) == 1
+    # several sequences with units of >= 384 KiB: the unit-order launch first
+    ragged = shape(batch=64, num_q_heads=64, num_kv_heads=8, max_context_len=32768,
+                   max_blocks_per_seq=2048, num_blocks=65536)
+    assert n(ragged, 10) == 3                    # 205 pages x 8 KiB per unit
+    assert n(ragged, 64) == 2                    # 32 pages: plain order
+    assert n(shape(batch=1, num_q_heads=64, num_kv_heads=8, max_context_len=32768,
+                   max_blocks_per_seq=2048, num_blocks=65536), 10) == 2
     assert n(shape(batch=0), 4) == 0
 
 
