@@ -627,9 +627,9 @@ pa_status pa_append_latent(const pa_shape* shape, const void* c_new, void* kv_ca
   if (st != PA_OK) return st;
   if (!c_new || !kv_cache || !block_table || !context_lens) return PA_ERR_INVALID;
   const pa_shape& s = *shape;
-  // FP8 latent rows only in the layout the FP8 latent decode reads (576-wide
-  // rows on 64-token pages): refuse to write caches nothing can read
-  if (s.kv_dtype == PA_FP8_E4M3 && !(s.head_dim == 576 && s.block_size == 64))
+  // FP8 latent rows only in the layouts the FP8 latent decode reads (576-wide
+  // rows on 64-token or one-token pages): refuse to write caches nothing can read
+  if (s.kv_dtype == PA_FP8_E4M3 && !(s.head_dim == 576 && (s.block_size == 64 || s.block_size == 1)))
     return PA_ERR_UNSUPPORTED;
   pa::AppendParams a{c_new, nullptr, kv_cache, nullptr, block_table, context_lens,
                      s.batch, 1, s.head_dim, 0, s.block_size, s.max_blocks_per_seq,

@@ -199,6 +199,16 @@ constexpr float kHeadroom = 16.0f;   // log2 units a chunk's max may exceed the 
 constexpr int kRing = 4;             // chunk slots: value product, scores, two loads in flight
 constexpr int kMaxIdsBS1 = 2048;     // token ids of one split held in LDS (one-token pages)
 
+// FP8 latent rows (one E4M3 code per element, 576 bytes) for the role-split
+// workgroup: a 32-token chunk is 18 KiB of codes, staged linearly (row t at
+// 576 t) by 20 loads of 1 KiB, 5 per loading wave (the last two read the
+// zero block into the slot's padding), and widened into the bf16 chunk
+// layout in LDS before its scores (widen_rows8).
+constexpr int kRow8 = kDqk;                     // 576 bytes per FP8 row
+constexpr int kChunk8 = kCT * kRow8;            // 18432 bytes of codes per chunk
+constexpr int kLoads8 = 20;                     // loads per FP8 chunk (18 + 2 of padding)
+constexpr int kStage8 = kLoads8 * 1024;         // bytes per FP8 staging slot
+
 // Where the rows of chunk ci come from, for 64-token pages (one page id per
 // chunk) and for one-token pages (a per-sequence token-index list: every row
 // has its own id).  Rows at or past the split's end t1 are read from the
@@ -264,6 +274,22 @@ struct ChunkSource<NW, 64> {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) issue_k(pr, dst, k);
   }
+  // FP8 rows: this wave's share of chunk ci's codes (half a page, contiguous)
+  // into a staging slot, linearly; bytes past the split's end read zeros.
+  __device__ __forceinline__ void issue8(lds_char* dst, int ci) {
+    static_assert(kLoads8 % NW == 0, "uniform FP8 load share");
+    const int tok0 = t0 + ci * kCT;
+    const char* src = cbase + (size_t)page_of(ci) * (64 * kRow8) + (tok0 % 64) * kRow8;
+    const int lim = min((t1 - tok0) * kRow8, kChunk8);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int k = 0; k < kLoads8 / NW; ++k) {
+      const int j = w + NW * k;
+      const int off = 1024 * j + 16 * ln;
+      dma16(off < lim ? (const void*)(src + off) : (const void*)g_zero16, dst + 1024 * j);
+    }
+  }
 };
 
 template <int NW>
@@ -309,6 +335,32 @@ struct ChunkSource<NW, 1> {
       const void* g = t < nrows ? (const void*)(cbase + (size_t)id * kRowB + c * 16)
                                 : (const void*)g_zero16;
       dma16(g, dst + j * 1024);
+    }
+  }
+  // FP8 rows: this wave's share of chunk ci's codes into a staging slot,
+  // linearly (row t at 576 t); a 1 KiB load spans up to three rows, each
+  // lane reads the id of its own row.  Rows past the split's end, and the
+  // padding, read zeros.
+  __device__ __forceinline__ void issue8(lds_char* dst, int ci) {
+    static_assert(kLoads8 % NW == 0, "uniform FP8 load share");
+    const int tok0 = t0 + ci * kCT;
+    const int nrows = min(t1 - tok0, kCT);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    int id[kLoads8 / NW];
+#pragma unroll
+    for (int k = 0; k < kLoads8 / NW; ++k) {
+      const int t = (1024 * (w + NW * k) + 16 * ln) / kRow8;
+      id[k] = ids[min(max(tok0 - t0 + t, 0), kMaxIdsBS1 - 1)];
+    }
+#pragma unroll
+    for (int k = 0; k < kLoads8 / NW; ++k) {
+      const int j = w + NW * k;
+      const int off = 1024 * j + 16 * ln;
+      const int t = off / kRow8;
+      const void* g = t < nrows ? (const void*)(cbase + (size_t)id[k] * kRow8 + (off - t * kRow8))
+                                : (const void*)g_zero16;
+      dma16(g, dst + 1024 * j);
     }
   }
 };
@@ -402,13 +454,40 @@ constexpr int kMtopOff = 64;       // float mtop[2][NH]: largest chunk max per t
 constexpr int kStatOff = 2048;     // float stat_m[NH], stat_l[2][NH]
 static_assert(kMtopOff + 2 * 64 * 4 <= kStatOff && kStatOff + 3 * 64 * 4 <= kChunkB,
               "end-of-pass regions fit the ring's first slot for up to 64 heads");
+static_assert(2 * kChunkB + 3 * kStage8 <= kRing * kChunkB, "FP8 staging fits the ring");
+
+// Widen the 32 staged FP8 rows of a chunk into a bf16 chunk buffer (the
+// role-split layout: 16-byte piece c of row t at c ^ row_key(t)); thread i of
+// NT takes pieces i, i + NT, ...  Piece m is codes 8 m .. 8 m + 7 of the
+// stage, i.e. elements 8 (m % 72) .. +7 of row m / 72.
+template <int NT>
+__device__ __forceinline__ void widen_rows8(const lds_char* stg, lds_char* dst) {
+  int i0 = threadIdx.x;
+  asm volatile("" : "+v"(i0));
+#pragma unroll
+  for (int k = 0; k < (kCT * (kRowB / 16) + NT - 1) / NT; ++k) {
+    const int m = i0 + NT * k;
+    if (m < kCT * (kRowB / 16)) {
+      const u32x2 c8 = *(const __attribute__((address_space(3))) u32x2*)(stg + 8 * m);
+      const int t = m / (kRowB / 16), c = m - t * (kRowB / 16);
+      ds_store_b128(dst + t * kRowB + 16 * (c ^ row_key(t)), fp8x8_to_bf16x8(c8[0], c8[1]));
+    }
+  }
+}
 
 template <int HH, int HBW>
 struct RoleShared {
   lds_char* ring;
   lds_char* pl;                    // probabilities, two buffers of NH*kCT bf16
   int nchunks;
-  __device__ __forceinline__ lds_char* slot(int ci) const { return ring + (ci % kRing) * kChunkB; }
+  int nslots;                      // bf16 chunk slots: 4, or 2 with FP8 staging after them
+  __device__ __forceinline__ lds_char* slot(int ci) const {
+    return ring + (ci & (nslots - 1)) * kChunkB;
+  }
+  // FP8 codes of chunk ci (three staging slots after the two bf16 ones)
+  __device__ __forceinline__ lds_char* stg8(int ci) const {
+    return ring + 2 * kChunkB + (ci % 3) * kStage8;
+  }
   __device__ __forceinline__ lds_char* pbuf(int ci) const {
     return pl + (ci & 1) * (RoleCfg<HH, HBW>::NH * kCT * 2);
   }
@@ -572,9 +651,10 @@ struct ScoreRole {
   __device__ __forceinline__ void finish_b() {}
 };
 
-template <int HH, int HBW, int BS>
+template <int HH, int HBW, int BS, bool F8>
 struct ValueRole {
   using C = RoleCfg<HH, HBW>;
+  static constexpr int kNwi = F8 ? kLoads8 / C::NP : C::NWI;   // loads per chunk and wave
   const RoleShared<HH, HBW>& sh;
   ChunkSource<C::NP, BS>& src;
   int v, lane;
@@ -605,23 +685,29 @@ struct ValueRole {
   // Chunks 0 and 1 are issued even past the split's end (those loads read
   // the zero block), so the count in flight is known: chunk 0 has landed once
   // at most one chunk's loads are outstanding.
+  // chunk ci into its bf16 slot, or its codes into its FP8 staging slot
+  __device__ __forceinline__ void load(int ci) {
+    if constexpr (F8) src.issue8(sh.stg8(ci), ci);
+    else src.issue(sh.slot(ci), ci);
+  }
   __device__ __forceinline__ void prologue() {
-    src.issue(sh.slot(0), 0);
-    src.issue(sh.slot(1), 1);
-    wait_vm<C::NWI>();
+    load(0);
+    load(1);
+    wait_vm<kNwi>();
   }
   __device__ __forceinline__ void step0a() {
-    if (2 < sh.nchunks) src.issue(sh.slot(2), 2);
+    if (2 < sh.nchunks) load(2);
   }
   __device__ __forceinline__ void step0b() {}
   // Before the barrier that opens step ci: chunk ci has landed.
   __device__ __forceinline__ void before_barrier(int ci) {
-    if (ci + 1 < sh.nchunks) wait_vm<C::NWI>(); else wait_vm<0>();
+    if (ci + 1 < sh.nchunks) wait_vm<kNwi>(); else wait_vm<0>();
   }
-  // Step ci: refill the slot of chunk ci - 2 with chunk ci + 2, then the value
+  // Step ci: refill the slot of chunk ci - 2 with chunk ci + 2 (FP8: the
+  // staging slot of chunk ci - 1, widened in the step before), then the value
   // product of chunk ci - 1.
   __device__ __forceinline__ void step(int ci) {
-    if (ci + 2 < sh.nchunks) src.issue(sh.slot(ci + 2), ci + 2);
+    if (ci + 2 < sh.nchunks) load(ci + 2);
     pv(ci - 1);
   }
   __device__ __forceinline__ void pass_end() { wait_vm<0>(); }
@@ -632,14 +718,22 @@ struct ValueRole {
 
 // The pass loop both roles run; every barrier of the workgroup is here, so
 // both roles meet the same barriers in the same order.
-template <typename Role, typename Begin>
+// With FP8 rows, each chunk is widened by every wave between two barriers
+// (the first: its codes have landed; the second: its bf16 rows are in place).
+template <bool F8, typename Role, typename Begin, typename Widen>
 __device__ __forceinline__ void role_loop(Role& r, int nchunks, const lds_char* ring, int ns, int w,
-                                          const Begin& begin_pass) {
+                                          const Begin& begin_pass, const Widen& widen) {
   for (;;) {
     r.pass_begin();
     begin_pass();                   // may hold a full barrier (token-id staging)
     r.prologue();
     lds_barrier();                  // chunk 0 in LDS
+    if constexpr (F8) {
+      if (nchunks > 0) {
+        widen(0);
+        lds_barrier();
+      }
+    }
     r.step0a();
     lds_barrier();                  // first-chunk maxima exchanged
     r.step0b();
@@ -647,6 +741,12 @@ __device__ __forceinline__ void role_loop(Role& r, int nchunks, const lds_char* 
       r.before_barrier(ci);
       lds_barrier();                // chunk ci in LDS, probabilities of ci - 1 written,
                                     // value product of ci - 2 done
+      if constexpr (F8) {
+        if (ci < nchunks) {
+          widen(ci);
+          lds_barrier();
+        }
+      }
       r.step(ci);
     }
     r.pass_end();
@@ -663,7 +763,7 @@ __device__ __forceinline__ void role_loop(Role& r, int nchunks, const lds_char* 
   }
 }
 
-template <int HH, int HBW, int BS>
+template <int HH, int HBW, int BS, bool F8>
 __global__ __launch_bounds__((RoleCfg<HH, HBW>::NW * 64)) void mla_roles_partial(Params p) {
   using C = RoleCfg<HH, HBW>;
   __shared__ __attribute__((aligned(16))) char ring_lds[kRing * kChunkB];
@@ -688,7 +788,8 @@ __global__ __launch_bounds__((RoleCfg<HH, HBW>::NW * 64)) void mla_roles_partial
   const int p1 = min(pages, s * p.c + p.c);
   const int nchunks = t1 > t0 ? (t1 - t0 + kCT - 1) / kCT : 0;
 
-  RoleShared<HH, HBW> sh{(lds_char*)ring_lds, (lds_char*)pl_lds, nchunks};
+  RoleShared<HH, HBW> sh{(lds_char*)ring_lds, (lds_char*)pl_lds, nchunks, F8 ? 2 : kRing};
+  auto widen = [&](int ci) { widen_rows8<C::NW * 64>(sh.stg8(ci), sh.slot(ci)); };
   ChunkSource<C::NP, BS> src;
   src.bt = p.block_table + (size_t)b * p.maxb;
   src.cbase = static_cast<const char*>(p.k);
@@ -705,12 +806,12 @@ __global__ __launch_bounds__((RoleCfg<HH, HBW>::NW * 64)) void mla_roles_partial
   if (w < C::NS) {
     ScoreRole<HH, HBW, BS> r{sh, w & 1, w >> 1, lane, t0, t1, p.scale_log2};
     r.load_q(static_cast<const char*>(p.q) + row0 * kRowB);
-    role_loop(r, nchunks, (const lds_char*)ring_lds, C::NS, w, begin_pass);
+    role_loop<F8>(r, nchunks, (const lds_char*)ring_lds, C::NS, w, begin_pass, widen);
     r.finish_a();
     lds_barrier();                                    // statistics visible
   } else {
-    ValueRole<HH, HBW, BS> r{sh, src, w - C::NS, lane};
-    role_loop(r, nchunks, (const lds_char*)ring_lds, C::NS, w, begin_pass);
+    ValueRole<HH, HBW, BS, F8> r{sh, src, w - C::NS, lane};
+    role_loop<F8>(r, nchunks, (const lds_char*)ring_lds, C::NS, w, begin_pass, widen);
     lds_barrier();                                    // statistics visible
     // the accumulators are read by VALU below: cover the last MFMA's latency
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -722,7 +823,8 @@ __global__ __launch_bounds__((RoleCfg<HH, HBW>::NW * 64)) void mla_roles_partial
       const int h = nb * 16 + n;
       const float mm = stat_m[h];
       const float lt = stat_l[h] + stat_l[C::NH + h];
-      const float inv = (mm == kNegInf) ? 0.f : 1.f / lt;
+      // (v_scale: the factor of every FP8 value, 1 for bf16 caches)
+      const float inv = (mm == kNegInf) ? 0.f : p.v_scale / lt;
       const size_t row = row0 + h;
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
@@ -750,17 +852,24 @@ __global__ __launch_bounds__((RoleCfg<HH, HBW>::NW * 64)) void mla_roles_partial
   }
 }
 
+template <int HH, int HBW, int BS, bool F8>
+void launch_roles_as(const Params& p, long blocks, hipStream_t st) {
+  hipLaunchKernelGGL((mla_roles_partial<HH, HBW, BS, F8>), dim3((unsigned)blocks),
+                     dim3(RoleCfg<HH, HBW>::NW * 64), 0, st, p);
+}
+
 template <int HH, int HBW>
-hipError_t launch_roles(const Params& p, hipStream_t st) {
+hipError_t launch_roles(const Params& p, bool fp8kv, hipStream_t st) {
   using C = RoleCfg<HH, HBW>;
   const long blocks = (long)(p.ql * p.Hq / C::NH) * p.S * p.B;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  if (p.bs == 1)
-    hipLaunchKernelGGL((mla_roles_partial<HH, HBW, 1>), dim3((unsigned)blocks), dim3(C::NW * 64), 0,
-                       st, p);
-  else
-    hipLaunchKernelGGL((mla_roles_partial<HH, HBW, 64>), dim3((unsigned)blocks), dim3(C::NW * 64),
-                       0, st, p);
+  if (p.bs == 1) {
+    if (fp8kv) launch_roles_as<HH, HBW, 1, true>(p, blocks, st);
+    else launch_roles_as<HH, HBW, 1, false>(p, blocks, st);
+  } else {
+    if (fp8kv) launch_roles_as<HH, HBW, 64, true>(p, blocks, st);
+    else launch_roles_as<HH, HBW, 64, false>(p, blocks, st);
+  }
   return hipGetLastError();
 }
 
@@ -1354,7 +1463,7 @@ bool mla_mfma_supported(bool bf16, int Dqk, int Dv, int bs, int Hq) {
 }
 
 bool mla_mfma_fp8_supported(int Dqk, int Dv, int bs, int Hq) {
-  return Dqk == kDqk && Dv == kDv && bs == 64 && Hq % kWideNH == 0;
+  return mla_mfma_supported(true, Dqk, Dv, bs, Hq);
 }
 
 int mla_heads_per_workgroup(int Hq, int bs) {
@@ -1365,14 +1474,11 @@ int mla_heads_per_workgroup(int Hq, int bs) {
 int mla_max_split_tokens(int bs) { return bs == 1 ? kMaxIdsBS1 : 0x7fffffff; }
 
 hipError_t launch_mla_mfma(const Params& p, bool fp8kv, hipStream_t st) {
-  if (fp8kv) {
-    if (!mla_mfma_fp8_supported(p.D, p.Dv, p.bs, p.Hq)) return hipErrorInvalidValue;
-    return launch_wide<true>(p, st);
-  }
-  if (p.bs == 64 && p.Hq % kWideNH == 0) return launch_wide<false>(p, st);
-  if (p.Hq % 64 == 0) return launch_roles<2, 2>(p, st);
-  if (p.Hq == 32) return launch_roles<2, 1>(p, st);
-  if (p.Hq == 16) return launch_roles<1, 1>(p, st);
+  if (p.bs == 64 && p.Hq % kWideNH == 0)
+    return fp8kv ? launch_wide<true>(p, st) : launch_wide<false>(p, st);
+  if (p.Hq % 64 == 0) return launch_roles<2, 2>(p, fp8kv, st);
+  if (p.Hq == 32) return launch_roles<2, 1>(p, fp8kv, st);
+  if (p.Hq == 16) return launch_roles<1, 1>(p, fp8kv, st);
   return hipErrorInvalidValue;
 }
 

@@ -233,10 +233,10 @@ pa_status pa_decode_static(const pa_shape* shape, const void* q, const void* k_c
  * more; the heuristic never does).  Any q_len up to 16; its rows run as
  * further head groups, each with its own causal end.  FP8 latent caches
  * (kv_dtype PA_FP8_E4M3, one code per element, rows of 576 bytes): PA_BF16
- * q, num_q_heads a multiple of 128, block_size 64; a key is k_scale times the
- * row's values, a value v_scale times its first 512 (codes widened to
- * bfloat16 exactly, k_scale folded into the score scale, v_scale into the
- * outputs); PA_ERR_UNSUPPORTED for other FP8 shapes.
+ * q, the same head counts and block sizes; a key is k_scale times the row's
+ * values, a value v_scale times its first 512 (codes widened to bfloat16
+ * exactly in LDS, k_scale folded into the score scale, v_scale into the
+ * outputs).
  */
 pa_status pa_decode_mla(const pa_shape* shape, const void* q, const void* kv_cache,
                         const int32_t* block_table, const int32_t* context_lens,
@@ -297,8 +297,8 @@ pa_status pa_append_kv(const pa_shape* shape, const void* k_new, const void* v_n
  * MLA variant: kv_cache[page][slot][:] = c_new[b][:], c_new [batch][head_dim]
  * (the whole latent row: keys and values come from the same memory).
  * num_kv_heads must be 1.  With kv_dtype PA_FP8_E4M3, c_new holds the codes
- * (one byte per element) and the layout must be the one the FP8 latent
- * decode reads (head_dim 576, block_size 64), else PA_ERR_UNSUPPORTED.
+ * (one byte per element) and the layout must be one the FP8 latent decode
+ * reads (head_dim 576, block_size 64 or 1), else PA_ERR_UNSUPPORTED.
  * Otherwise as pa_append_kv.
  */
 pa_status pa_append_latent(const pa_shape* shape, const void* c_new, void* kv_cache,

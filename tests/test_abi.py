@@ -135,7 +135,7 @@ def test_fp8_scales_checked(lib, ks, vs):
 def test_fp8_shapes_pass_validation(lib):
     """FP8 caches with bf16 queries validate (the workspace check fails first,
     so nothing launches); an explicit cache dtype equal to the query's is the
-    default; FP8 latent caches take 128-head groups on 64-token pages."""
+    default; FP8 latent caches take the bf16 latent shapes."""
     for kw in (dict(), dict(num_kv_heads=2), dict(q_len=2), dict(block_size=32, max_context_len=200)):
         s = shape(kv_dtype=_lib.PA_FP8_E4M3, k_scale=0.02, v_scale=3.0, **kw)
         assert decode(lib, s, splits=4) == _lib.PA_ERR_WORKSPACE, kw
@@ -147,9 +147,10 @@ def test_fp8_shapes_pass_validation(lib):
         m = shape(**base)
         return lib.pa_decode_mla(ctypes.byref(m), FAKE, FAKE, FAKE, FAKE, 4, FAKE, NULL, NULL, 0,
                                  NULL)
-    for kw in (dict(), dict(num_q_heads=256), dict(q_len=2)):
+    for kw in (dict(), dict(num_q_heads=256), dict(q_len=2), dict(num_q_heads=64),
+               dict(num_q_heads=16), dict(num_q_heads=32), dict(block_size=1, max_blocks_per_seq=300)):
         assert mla(**kw) == _lib.PA_ERR_WORKSPACE, kw
-    for kw in (dict(num_q_heads=64), dict(num_q_heads=16), dict(block_size=1, max_blocks_per_seq=300),
+    for kw in (dict(num_q_heads=48), dict(block_size=16, max_blocks_per_seq=20),
                dict(dtype=_lib.PA_F32)):
         assert mla(**kw) == _lib.PA_ERR_UNSUPPORTED, kw
 
@@ -344,7 +345,7 @@ def test_append_null_pointers(lib):
     # the latent pool has one KV head
     assert append_latent(lib, shape(num_kv_heads=2, num_q_heads=2)) == _lib.PA_ERR_INVALID
     # FP8 latent rows only in the layout the FP8 latent decode reads
-    for kw in (dict(head_dim=512, head_dim_v=512), dict(block_size=1)):
+    for kw in (dict(head_dim=512, head_dim_v=512), dict(block_size=16)):
         base = dict(num_q_heads=1, num_kv_heads=1, head_dim=576, head_dim_v=576, block_size=64,
                     kv_dtype=_lib.PA_FP8_E4M3)
         base.update(kw)

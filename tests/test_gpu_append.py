@@ -35,6 +35,11 @@ CASES = {
                     head_dim=576, head_dim_v=512, block_size=64, context_lens=[65, 64, 1],
                     num_blocks=12, scale=192 ** -0.5, kv_dtype="fp8", k_scale=0.05,
                     v_scale=0.06),
+    # token-index lists (one-token pages), 32 heads: the role-split kernel
+    "mla_fp8_bs1": dict(kind="mla", dtype="bf16", batch=3, num_q_heads=32, num_kv_heads=1,
+                        head_dim=576, head_dim_v=512, block_size=1, context_lens=[65, 64, 1],
+                        num_blocks=200, scale=192 ** -0.5, kv_dtype="fp8", k_scale=0.05,
+                        v_scale=0.06),
 }
 
 

@@ -267,6 +267,21 @@ FP8 = {
                          num_blocks=8, **FP8_LATENT),
     "fp8_rows_mla_h128_q3": dict(MLA_DIMS, batch=2, num_q_heads=128, context_lens=[3, 300],
                                  num_blocks=10, q_len=3, **FP8_LATENT),
+    # the role-split latent kernel: 16, 32 and 64 heads on 64-token pages, and one-token pages
+    # (token-index lists) with 128 and 32 heads
+    "fp8_mla_h16": dict(MLA_DIMS, batch=2, num_q_heads=16, context_lens=[1, 700], num_blocks=20,
+                        **FP8_LATENT),
+    "fp8_mla_h32": dict(MLA_DIMS, batch=2, num_q_heads=32, context_lens=[64, 129], num_blocks=8,
+                        **FP8_LATENT),
+    "fp8_mla_h64": dict(MLA_DIMS, batch=1, num_q_heads=64, context_lens=[300], num_blocks=6,
+                        **FP8_LATENT),
+    "fp8_mla_bs1_h128": dict(MLA_DIMS, batch=3, num_q_heads=128, block_size=1,
+                             context_lens=[1, 100, 333], num_blocks=600, **FP8_LATENT),
+    "fp8_mla_bs1_h32": dict(MLA_DIMS, batch=2, num_q_heads=32, block_size=1, context_lens=[47, 65],
+                            num_blocks=200, **FP8_LATENT),
+    "fp8_rows_mla_bs1_h128_q2": dict(MLA_DIMS, batch=2, num_q_heads=128, block_size=1,
+                                     context_lens=[2, 150], num_blocks=300, q_len=2,
+                                     **FP8_LATENT),
 }
 
 
@@ -290,7 +305,8 @@ def test_fp8_kv(name):
 
 FULL = ["tiny_mha_f32", "llama_mha_bf16", "long_gqa_bf16", "ragged_gqa_bf16", "mla_bf16",
         "mla_topk_bf16", "mla_allentries_bf16", "llama_mha_q4_bf16", "long_gqa_q4_bf16",
-        "mla_q2_bf16", "llama_mha_fp8", "long_gqa_fp8", "ragged_gqa_fp8", "mla_fp8"]
+        "mla_q2_bf16", "llama_mha_fp8", "long_gqa_fp8", "ragged_gqa_fp8", "mla_fp8",
+        "mla_topk_fp8"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -582,15 +598,17 @@ def test_rising_scores(spec):
         compare(inp, out, lse, ref_out, ref_lse, f"rising scores S={S}")
 
 
-def test_rising_scores_fp8_latent():
+@pytest.mark.parametrize("heads,bs", [(128, 64), (64, 64), (128, 1)],
+                         ids=["wide", "roles", "roles_bs1"])
+def test_rising_scores_fp8_latent(heads, bs):
     """The rising-scores case on an FP8 latent cache: the codes of a key-only
     dim climb with the token index (a quarter of it, rounded to E4M3), and the
     query's weight on that dim makes each 32-token chunk's max exceed the
-    previous one by far more than the headroom, so the wide kernel starts its
-    splits over with a raised reference max."""
+    previous one by far more than the headroom, so the latent kernels start
+    their splits over with a raised reference max."""
     lens = [1000, 77]
-    s = dict(PROP_MLA128_FP8, context_lens=lens, k_scale=0.25, v_scale=0.3,
-             num_blocks=sum(-(-n // 64) for n in lens) + 10)
+    s = dict(PROP_MLA128_FP8, num_q_heads=heads, block_size=bs, context_lens=lens, k_scale=0.25,
+             v_scale=0.3, num_blocks=sum(-(-n // bs) for n in lens) + 10)
     inp = make_paged_inputs(seed=19, **s)
     bt = inp.compact_block_table()
     d = inp.head_dim - 1
@@ -598,7 +616,7 @@ def test_rising_scores_fp8_latent():
         torch.float8_e4m3fn).view(torch.uint8).numpy()
     for b in range(inp.batch):
         for tok in range(int(inp.context_lens[b])):
-            inp.c_pages[bt[b, tok // 64], tok % 64, d] = codes[tok]
+            inp.c_pages[bt[b, tok // bs], tok % bs, d] = codes[tok]
     from workloads import f32_to_bf16_bits
     inp.q[:, :, d] = f32_to_bf16_bits(np.array([256.0], np.float32))[0]
     ref_out, ref_lse = oracle.decode_inputs(inp)
