@@ -45,9 +45,12 @@ def _units(ctx, bs, c):
     return out
 
 
-@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
-def test_unit_order_and_result(fp8):
-    spec = dict(SPEC, **(dict(kv_dtype="fp8", k_scale=0.037, v_scale=0.045) if fp8 else {}))
+@pytest.mark.parametrize("fp8,q_len,heads", [(False, 1, 16), (True, 1, 16), (False, 2, 16),
+                                              (True, 3, 8)],
+                         ids=["bf16", "fp8", "bf16_q2", "fp8_q3_g4"])
+def test_unit_order_and_result(fp8, q_len, heads):
+    spec = dict(SPEC, num_q_heads=heads, q_len=q_len,
+                **(dict(kv_dtype="fp8", k_scale=0.037, v_scale=0.045) if fp8 else {}))
     inp = make_paged_inputs(seed=21, **spec)
     t = to_device(inp, "cuda", poison=True)
     ref_out, ref_lse = oracle.decode_inputs(inp)
@@ -56,20 +59,22 @@ def test_unit_order_and_result(fp8):
         head_dim=inp.head_dim, head_dim_v=inp.head_dim_v, block_size=inp.block_size,
         max_blocks_per_seq=inp.max_blocks_per_seq, num_blocks=inp.num_blocks,
         max_context_len=inp.max_context_len, scale=inp.scale, dtype=torch.bfloat16,
-        kv_dtype=pa._lib.PA_FP8_E4M3 if fp8 else 0, k_scale=inp.k_scale, v_scale=inp.v_scale)
+        q_len=q_len, kv_dtype=pa._lib.PA_FP8_E4M3 if fp8 else 0, k_scale=inp.k_scale,
+        v_scale=inp.v_scale)
     B, bs = inp.batch, inp.block_size
     P = -(-inp.max_context_len // bs)
-    rows = B * inp.num_q_heads
+    rows = B * q_len * inp.num_q_heads
+    qdims = (B, q_len) if q_len > 1 else (B,)
     for S in ((2,) if fp8 else (2, 3, 4)):
-        print(f"unit order fp8={fp8} S={S}", flush=True)
+        print(f"unit order fp8={fp8} q_len={q_len} heads={heads} S={S}", flush=True)
         c = -(-P // S)
         nbytes = pa.workspace_size(shape, S)
         sched_off = _up(rows * 4) + _up(rows * S * inp.head_dim_v * 4) + _up(rows * S * 4)
         assert nbytes == sched_off + _up(B * S * 4)
         ws = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda")
-        out = torch.empty((B, inp.num_q_heads, inp.head_dim_v), dtype=torch.bfloat16,
+        out = torch.empty(qdims + (inp.num_q_heads, inp.head_dim_v), dtype=torch.bfloat16,
                           device="cuda")
-        lse = torch.empty((B, inp.num_q_heads), dtype=torch.float32, device="cuda")
+        lse = torch.empty(qdims + (inp.num_q_heads,), dtype=torch.float32, device="cuda")
         pa.decode_partial(shape, t["q"], t["k_cache"], t["v_cache"], t["block_table"],
                           t["context_lens"], S, out, lse, ws)
         torch.cuda.synchronize()
