@@ -105,3 +105,57 @@ def test_unit_order_and_result(fp8, q_len, heads):
         fin = np.isfinite(ref_lse)
         assert np.array_equal(gl[~fin], ref_lse[~fin])      # empty sequences: -inf
         assert np.abs(gl[fin] - ref_lse[fin]).max() <= 1e-3
+
+
+def test_unit_order_more_sequences_than_threads():
+    """A batch of 1300 sequences (more than the schedule's 1024 threads, so
+    its placement pass reads some lengths again), mostly short, with a few
+    long ones whose units reach 384 KiB: the order is still a permutation of
+    the real units, longest first, and the result matches the oracle."""
+    rng = np.random.default_rng(5)
+    lens = [int(x) for x in rng.integers(0, 120, 1300)]
+    for i in (3, 700, 1100, 1299):
+        lens[i] = 3200
+    spec = dict(kind="mha", dtype="bf16", batch=len(lens), num_q_heads=8, num_kv_heads=2,
+                head_dim=128, block_size=16, context_lens=lens,
+                num_blocks=sum(-(-n // 16) for n in lens) + 16)
+    inp = make_paged_inputs(seed=22, **spec)
+    t = to_device(inp, "cuda", poison=True)
+    ref_out, ref_lse = oracle.decode_inputs(inp)
+    shape = pa.make_shape(
+        batch=inp.batch, num_q_heads=inp.num_q_heads, num_kv_heads=inp.num_kv_heads,
+        head_dim=inp.head_dim, head_dim_v=inp.head_dim_v, block_size=inp.block_size,
+        max_blocks_per_seq=inp.max_blocks_per_seq, num_blocks=inp.num_blocks,
+        max_context_len=inp.max_context_len, scale=inp.scale, dtype=torch.bfloat16)
+    B, S = inp.batch, 2
+    assert pa.decode_launches(shape, S) == 3
+    P = -(-inp.max_context_len // 16)
+    c = -(-P // S)
+    rows = B * inp.num_q_heads
+    sched_off = _up(rows * 4) + _up(rows * S * inp.head_dim_v * 4) + _up(rows * S * 4)
+    ws = torch.full((pa.workspace_size(shape, S),), 0xAB, dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, inp.num_q_heads, inp.head_dim_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, inp.num_q_heads), dtype=torch.float32, device="cuda")
+    print("unit order: 1300 sequences", flush=True)
+    pa.decode_partial(shape, t["q"], t["k_cache"], t["v_cache"], t["block_table"],
+                      t["context_lens"], S, out, lse, ws)
+    torch.cuda.synchronize()
+    tab = ws[sched_off:sched_off + 4 * B * S].cpu().numpy().view(np.uint32)
+    units = _units(inp.context_lens, 16, c)
+    n_full = sum(f for f, _ in units)
+    want = sorted((b, s) for b, (f, last) in enumerate(units) for s in range(f + (last is not None)))
+    n_real = len(want)
+    assert (tab[n_real:] == NO_UNIT).all()
+    got = tab[:n_real]
+    assert sorted(zip((got & 0xFFFF).astype(int).tolist(), (got >> 16).astype(int).tolist())) == want
+    seq = (got & 0xFFFF).astype(int)
+    sizes = [units[b][1] for b in seq[n_full:]]
+    assert [(c - x) * (BUCKETS - 1) // c for x in sizes] == \
+        sorted((c - x) * (BUCKETS - 1) // c for x in sizes)
+    pa.reduce(shape, t["context_lens"], S, ws, out, lse)
+    torch.cuda.synchronize()
+    assert np.abs(from_device(out) - ref_out).max() <= 2e-2
+    gl = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(gl[~fin], ref_lse[~fin])
+    assert np.abs(gl[fin] - ref_lse[fin]).max() <= 1e-3
