@@ -125,7 +125,9 @@ int32_t pa_version(void);
  * batch x heads alone cannot fill the GPU; the "flash decoding ++" entry,
  * its TRT-LLM multi_block_mode / vLLM PagedAttention V2 snippet).  Picks S so that the
  * partial kernel launches enough workgroups for `num_cus` compute units
- * while each split keeps enough pages to amortise its partial write.
+ * while each split keeps enough pages to amortise its partial write; when the
+ * batch runs its units longest first (pa_decode_launches == 3), splits are
+ * larger, the fewer the more (sequence, KV head) units the batch has.
  * num_cus <= 0 queries the current HIP device.  Returns S >= 1, or 0 if the
  * shape is invalid (or the device query failed).  `mla` != 0 selects the
  * latent kernel's work unit.  Host only.
