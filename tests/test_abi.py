@@ -425,3 +425,22 @@ def test_static_entry_point_checks(lib):
     assert lib.pa_decode_workspace_size(ctypes.byref(big), 64, 0) > 64 << 20
     assert static(big, 64) == _lib.PA_ERR_SCRATCH
     assert "64 MiB" in _lib.status_string(_lib.PA_ERR_SCRATCH)
+
+
+def test_split_plan_for_batches_run_longest_first(lib):
+    """With the units run longest first, the longest sequence gets 10 splits,
+    or 3 when the batch's (sequence, KV head) units fill every workgroup slot
+    (two per CU) twice over; smaller units keep the plain plan."""
+    def S(**kw):
+        base = dict(num_q_heads=64, num_kv_heads=8, max_context_len=32768,
+                    max_blocks_per_seq=2048, num_blocks=65536)
+        base.update(kw)
+        s = shape(**base)
+        n = lib.pa_choose_num_splits(ctypes.byref(s), 256, 0)
+        return n, lib.pa_decode_launches(ctypes.byref(s), n, 0)
+    assert S(batch=64) == (10, 3)                       # 512 units: 10 for the longest
+    assert S(batch=128) == (3, 3)                       # 1024 units: 3
+    assert S(batch=256, max_context_len=8192, max_blocks_per_seq=512) == (3, 3)
+    # 128 sequences of at most 1024 tokens: units of 22 pages stay below 384 KiB
+    n, launches = S(batch=128, max_context_len=1024, max_blocks_per_seq=64)
+    assert launches == 2
