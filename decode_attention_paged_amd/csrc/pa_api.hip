@@ -1,4 +1,5 @@
 // C ABI of libpa_decode: argument checks, the split plan, dispatch.
+#include <algorithm>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -18,6 +19,7 @@ constexpr double kSplitBytesMfma = 1024.0 * 1024.0;  // KV bytes per workgroup, 
 constexpr int kMinSplitsLong = 8;                    // splits of the longest sequence (MFMA kernel, full grid)
 constexpr int kSchedSplitsLong = 10;                 // the same when the units run longest first
 constexpr int kSchedSplitsMany = 3;                  // ... and the batch alone fills every slot twice
+constexpr double kManyUnitBytes = 512.0 * 1024.0;    // smallest split of such a batch (KV bytes)
 constexpr double kScheduleUnitBytes = 384.0 * 1024.0;  // smallest unit (KV bytes) run longest first
 constexpr double kMinSplitBytesValu = 32.0 * 1024.0;  // fewest KV bytes per workgroup, VALU kernel
 constexpr double kMinSplitBytesMfma = 64.0 * 1024.0;  // fewest KV bytes per workgroup, MFMA kernel
@@ -185,16 +187,24 @@ int heuristic_splits(const pa_shape& s, int cus, bool mla) {
       // at 10 splits against 357.5 at 15 (FP8 183.3 against 190.0); four
       // other draws of it: -2.9 % to +1.2 % (mean -1.4 %) against 15 splits,
       // while the best count varied from 7 to 10.
-      // A batch whose (sequence, KV head) units alone fill every workgroup
-      // slot (two per CU) twice over needs no splitting for parallelism, only
-      // against a tail: kSchedSplitsMany for the longest sequence (128
-      // sequences of 512-4096 tokens: 216.9 us at 3 splits against 254.8 at
-      // 8; 256 of log-uniform 64-8192 tokens: 295.4 against 328.8).
-      const int n_long = units >= 4L * cus ? kSchedSplitsMany : kSchedSplitsLong;
-      const int c_sched = (P + n_long - 1) / n_long;
+      const int c_sched = (P + kSchedSplitsLong - 1) / kSchedSplitsLong;
       if (s.batch > 1 && c_sched > c &&
           (double)c_sched * s.block_size * (s.head_dim + s.head_dim_v) * esz >= kScheduleUnitBytes)
         c = c_sched;
+      // A batch whose (sequence, KV head) units alone fill every workgroup
+      // slot (two per CU) twice over needs splitting only against a tail:
+      // kSchedSplitsMany for the longest sequence, and no split below
+      // kManyUnitBytes (a shorter longest sequence is not split at all).
+      // Measured (64 q / 8 kv heads, D128): 128 sequences of 512-4096
+      // tokens, 3 splits: 216.9 us against 254.8 at 8; 256 of log-uniform
+      // 64-8192: 295.4 against 328.8; 256 of 64-1024 tokens, unsplit: 113.6
+      // against 149.2 at 2; 512 of log-uniform 32-2048, 2 splits: 210.7
+      // against 253.0 at 4 and 233 unsplit.
+      if (s.batch > 1 && units >= 4L * cus) {
+        const int c_many = std::max((P + kSchedSplitsMany - 1) / kSchedSplitsMany,
+                                    (int)std::ceil(kManyUnitBytes / page_bytes));
+        if (c_many > c) c = c_many;
+      }
     }
     if (c < c_min) c = c_min;
     S = (P + c - 1) / c;

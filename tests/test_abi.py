@@ -430,7 +430,8 @@ def test_static_entry_point_checks(lib):
 def test_split_plan_for_batches_run_longest_first(lib):
     """With the units run longest first, the longest sequence gets 10 splits,
     or 3 when the batch's (sequence, KV head) units fill every workgroup slot
-    (two per CU) twice over; smaller units keep the plain plan."""
+    (two per CU) twice over, and then no split reads less than 512 KiB (a
+    short longest sequence is not split at all)."""
     def S(**kw):
         base = dict(num_q_heads=64, num_kv_heads=8, max_context_len=32768,
                     max_blocks_per_seq=2048, num_blocks=65536)
@@ -441,6 +442,10 @@ def test_split_plan_for_batches_run_longest_first(lib):
     assert S(batch=64) == (10, 3)                       # 512 units: 10 for the longest
     assert S(batch=128) == (3, 3)                       # 1024 units: 3
     assert S(batch=256, max_context_len=8192, max_blocks_per_seq=512) == (3, 3)
-    # 128 sequences of at most 1024 tokens: units of 22 pages stay below 384 KiB
-    n, launches = S(batch=128, max_context_len=1024, max_blocks_per_seq=64)
-    assert launches == 2
+    # 128 sequences of at most 1024 tokens (64 pages, 512 KiB): unsplit, one launch
+    assert S(batch=128, max_context_len=1024, max_blocks_per_seq=64) == (1, 1)
+    # 512 sequences of at most 2048 tokens: two splits of 512 KiB, run longest first
+    assert S(batch=512, max_context_len=2048, max_blocks_per_seq=128) == (2, 3)
+    # fewer units than twice the slots: the 10-split rule (Llama-style 4-row MHA keeps 8)
+    assert S(batch=16, num_q_heads=32, num_kv_heads=32, q_len=4, max_context_len=4096,
+             max_blocks_per_seq=256)[0] == 8
