@@ -20,6 +20,7 @@ constexpr int kMinSplitsLong = 8;                    // splits of the longest se
 constexpr int kSchedSplitsLong = 10;                 // the same when the units run longest first
 constexpr int kSchedSplitsMany = 3;                  // ... and the batch alone fills every slot twice
 constexpr double kManyUnitBytes = 512.0 * 1024.0;    // smallest split of such a batch (KV bytes)
+constexpr int kValuSplitsMany = 4;                   // longest sequence, VALU kernel, slots filled twice
 constexpr double kScheduleUnitBytes = 384.0 * 1024.0;  // smallest unit (KV bytes) run longest first
 constexpr double kMinSplitBytesValu = 32.0 * 1024.0;  // fewest KV bytes per workgroup, VALU kernel
 constexpr double kMinSplitBytesMfma = 64.0 * 1024.0;  // fewest KV bytes per workgroup, MFMA kernel
@@ -205,6 +206,15 @@ int heuristic_splits(const pa_shape& s, int cus, bool mla) {
                                     (int)std::ceil(kManyUnitBytes / page_bytes));
         if (c_many > c) c = c_many;
       }
+    }
+    // The VALU kernel holds 4 workgroups per CU; a batch whose (sequence,
+    // head) units alone fill those slots twice over gives the longest
+    // sequence kValuSplitsMany splits (64 sequences x 32 heads of 1-4K
+    // tokens: 437.8 us per step at 4 splits against 456.0 at 16; 128 x 32 of
+    // log-uniform 128-8K tokens: 723.6 against 778.9 at 32).
+    if (k == Kernel::MhaValu && s.batch > 1 && units >= 8L * cus) {
+      const int c_many = (P + kValuSplitsMany - 1) / kValuSplitsMany;
+      if (c_many > c) c = c_many;
     }
     if (c < c_min) c = c_min;
     S = (P + c - 1) / c;

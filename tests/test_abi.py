@@ -446,6 +446,11 @@ def test_split_plan_for_batches_run_longest_first(lib):
     assert S(batch=128, max_context_len=1024, max_blocks_per_seq=64) == (1, 1)
     # 512 sequences of at most 2048 tokens: two splits of 512 KiB, run longest first
     assert S(batch=512, max_context_len=2048, max_blocks_per_seq=128) == (2, 3)
+    # MHA on the VALU kernel (4 workgroups per CU): 64 x 32 units fill the slots twice
+    # over, so the longest sequence gets 4 splits; 16 x 32 keep the byte target (16)
+    mha = dict(num_q_heads=32, num_kv_heads=32, max_context_len=4096, max_blocks_per_seq=256)
+    assert S(batch=64, **mha)[0] == 4
+    assert S(batch=16, **mha)[0] == 16
     # fewer units than twice the slots: the 10-split rule (Llama-style 4-row MHA keeps 8)
     assert S(batch=16, num_q_heads=32, num_kv_heads=32, q_len=4, max_context_len=4096,
              max_blocks_per_seq=256)[0] == 8
