@@ -364,6 +364,12 @@ CONFIGS = {
         scale=1.0 / math.sqrt(192), seed=5, kv_dtype="fp8", k_scale=0.02, v_scale=0.02,
         meta=dict(desc="MLA latent, FP8 E4M3 cache (bf16 q): B32, 128 heads, latent 576 "
                        "(V = first 512), ctx 8192, bs64")),
+    "serving_gqa_bf16": dict(
+        kind="mha", dtype="bf16", batch=192, num_q_heads=64, num_kv_heads=8, head_dim=128,
+        block_size=16, context_lens=_loguniform_ctx(128, 16384, 192), num_blocks=65536,
+        scale=1.0 / math.sqrt(128), seed=7,
+        meta=dict(desc="serving-mix GQA bf16: 192 seqs, ctx log-U[128,16384], 64 q / 8 kv heads, "
+                       "D128, bs16")),
     "mla_topk_fp8": dict(
         kind="mla", dtype="bf16", batch=32, num_q_heads=128, num_kv_heads=1, head_dim=576,
         head_dim_v=512, block_size=1, context_lens=[1152] * 32, num_blocks=262144,
@@ -382,7 +388,7 @@ CONFIGS = {
 CONFIG_ORDER = ["tiny_mha_f32", "llama_mha_bf16", "long_gqa_bf16", "ragged_gqa_bf16", "mla_bf16",
                 "mla_topk_bf16", "mla_allentries_bf16", "llama_mha_q4_bf16", "long_gqa_q4_bf16",
                 "mla_q2_bf16", "llama_mha_fp8", "long_gqa_fp8", "ragged_gqa_fp8", "mla_fp8",
-                "mla_topk_fp8"]
+                "mla_topk_fp8", "serving_gqa_bf16"]
 
 
 def make_config(name: str, *, poison: bool = True, values: bool = True, seed: int | None = None,
