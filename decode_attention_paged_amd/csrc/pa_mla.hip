@@ -908,7 +908,11 @@ constexpr int kWideDW = kDv / kWideNW;       // 128 value dims per wave
 constexpr int kWideMB = kWideDW / 32;        // 4 M-blocks of 32 dims
 constexpr int kWideNB = kWideNH / 32;        // 4 head blocks of 32
 constexpr int kWideKS = kDqk / 16;           // 36 score k-steps
-constexpr int kWideLook = 4;                 // score operand reads ahead of their MFMAs
+// Score operand reads in flight ahead of their MFMAs.  With one wave per
+// SIMD an LDS read's latency is covered only by the reads issued before it:
+// eight 1 KiB reads in flight (one accumulation chain leaves the registers
+// for them) measured 2-4 % faster than four with two chains.
+constexpr int kWideLook = 8;
 constexpr int kWidePB = kWideNH * kCT * 2;   // bytes of one probability buffer
 static_assert(kDmaInst % kWideNW == 0, "uniform load share");
 constexpr int kWideOutRowB = 2 * kDv + 16;   // staged output row (bytes), padded against bank conflicts
@@ -927,8 +931,8 @@ __device__ __forceinline__ void mfma32_v_first(f32x16& d, const u32x4& a, const 
 __device__ __forceinline__ void mfma32_v(f32x16& d, const u32x4& a, const u32x4& b) {
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void drain_scores32(f32x16& s0, f32x16& s1) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1));
+__device__ __forceinline__ void drain_scores32(f32x16& s) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
 }
 // Value MFMA (accumulators in AGPRs: the compiler places them there, as
 // the VGPRs hold the queries).
@@ -1056,7 +1060,8 @@ struct WideState {
 };
 
 // Score MFMAs of chunk `buf` for heads 32w .. 32w+31 (S^T, 32 tokens x 32
-// heads, in two accumulator chains: even and odd k-steps).  issue(k) runs
+// heads, one accumulation chain: a dependent MFMA with the same accumulator
+// issues back to back).  issue(k) runs
 // before k-step 4k (k < 9): this wave's loads of a later chunk go out between
 // the MFMAs, so the matrix core stays busy while the load path accepts them.
 // Lane pointers of the 16-byte operand reads of a buffer in the chunk layout:
@@ -1079,7 +1084,7 @@ struct WideRowReads {
 
 template <typename Issue>
 __device__ __forceinline__ void wide_score_mfma(const WideState& st, const lds_char* buf, int lane,
-                                                f32x16& s0, f32x16& s1, const Issue& issue) {
+                                                f32x16& sc, const Issue& issue) {
   const WideRowReads load_a(buf, lane);
   constexpr int L = kWideLook;
   u32x4 ab[L + 1];
@@ -1091,23 +1096,21 @@ __device__ __forceinline__ void wide_score_mfma(const WideState& st, const lds_c
     // the buffer refilled here was consumed one step earlier
     if (kb + L < kWideKS) ab[(kb + L) % (L + 1)] = load_a(kb + L);
     const u32x4 a = ab[kb % (L + 1)];
-    if (kb == 0) mfma32_v_first(s0, a, st.qf[kb]);
-    else if (kb == 1) mfma32_v_first(s1, a, st.qf[kb]);
-    else if (kb & 1) mfma32_v(s1, a, st.qf[kb]);
-    else mfma32_v(s0, a, st.qf[kb]);
+    if (kb == 0) mfma32_v_first(sc, a, st.qf[kb]);
+    else mfma32_v(sc, a, st.qf[kb]);
   }
-  drain_scores32(s0, s1);
+  drain_scores32(sc);
 }
 
-// Softmax of one chunk, first part: the scores (both accumulator chains
-// added), masked past the split's end t1, and their max per head, with the
-// overflow bookkeeping.  tok0: the chunk's first token.
-__device__ __forceinline__ void wide_scores_max(WideState& st, const f32x16& s0, const f32x16& s1,
+// Softmax of one chunk, first part: the scores, masked past the split's end
+// t1, and their max per head, with the overflow bookkeeping.  tok0: the
+// chunk's first token.
+__device__ __forceinline__ void wide_scores_max(WideState& st, const f32x16& sc,
                                                 float (&v)[16], int lane, int tok0, int t1,
                                                 float cs) {
   const int hsel = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = s0[i] + s1[i];
+  for (int i = 0; i < 16; ++i) v[i] = sc[i];
   // lane: head 32w + (lane & 31), tokens tok0 + 8g + 4*hsel + j in v[4g + j]
   const int tb = tok0 + 4 * hsel;
   if (tok0 + kCT > t1) {                             // only a split's last chunk runs past t1
@@ -1303,18 +1306,18 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
       };
       if (nchunks > 0) {
         widen(0);
-        f32x16 s0, s1;
-        wide_score_mfma(st, slot(0), lane, s0, s1, [&](int) {});
+        f32x16 sc;
+        wide_score_mfma(st, slot(0), lane, sc, [&](int) {});
         float v[16];
-        wide_scores_max(st, s0, s1, v, lane, t0, t1, cs);
+        wide_scores_max(st, sc, v, lane, t0, t1, cs);
         wide_weights(st, v, pbuf(0), w, lane, cs);
       }
       for (int ci = 1; ci < nchunks; ++ci) {
         widen(ci);
-        f32x16 s0, s1;
-        wide_score_mfma(st, slot(ci), lane, s0, s1, [&](int) {});
+        f32x16 sc;
+        wide_score_mfma(st, slot(ci), lane, sc, [&](int) {});
         float v[16];
-        wide_scores_max(st, s0, s1, v, lane, t0 + ci * kCT, t1, cs);
+        wide_scores_max(st, sc, v, lane, t0 + ci * kCT, t1, cs);
         wide_values(st, slot(ci - 1), pbuf(ci - 1), vb, lane);
         wide_weights(st, v, pbuf(ci), w, lane, cs);
       }
@@ -1324,10 +1327,10 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
     if (nchunks > 0) {
       ld.refresh();
       const i32x4 rs = wide_rsrc(src, 2);
-      f32x16 s0, s1;
-      wide_score_mfma(st, slot(0), lane, s0, s1, [&](int k) { ld.issue(rs, slot(2), k); });
+      f32x16 sc;
+      wide_score_mfma(st, slot(0), lane, sc, [&](int k) { ld.issue(rs, slot(2), k); });
       float v[16];
-      wide_scores_max(st, s0, s1, v, lane, t0, t1, cs);
+      wide_scores_max(st, sc, v, lane, t0, t1, cs);
       wide_weights(st, v, pbuf(0), w, lane, cs);
     }
     for (int ci = 1; ci < nchunks; ++ci) {
@@ -1343,10 +1346,10 @@ __global__ __launch_bounds__(kWideNW * 64) void mla_wide_partial(Params p) {
       // issues the same loads, so the wait counts above hold)
       ld.refresh();
       const i32x4 rs = wide_rsrc(src, ci + 2);
-      f32x16 s0, s1;
-      wide_score_mfma(st, slot(ci), lane, s0, s1, [&](int k) { ld.issue(rs, slot(ci + 2), k); });
+      f32x16 sc;
+      wide_score_mfma(st, slot(ci), lane, sc, [&](int k) { ld.issue(rs, slot(ci + 2), k); });
       float v[16];
-      wide_scores_max(st, s0, s1, v, lane, t0 + ci * kCT, t1, cs);
+      wide_scores_max(st, sc, v, lane, t0 + ci * kCT, t1, cs);
       wide_values(st, slot(ci - 1), pbuf(ci - 1), vb, lane);
       wide_weights(st, v, pbuf(ci), w, lane, cs);
     }
