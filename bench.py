@@ -52,7 +52,8 @@ def kernel_family(inp) -> str:
     if inp.kind == "mla":
         return "mla"
     cols = inp.num_q_heads // inp.num_kv_heads * inp.q_len   # MFMA columns: (row, head) pairs
-    if inp.dtype == "bf16" and inp.head_dim == 128 and inp.block_size == 16 and 2 <= cols <= 16:
+    if (inp.dtype == "bf16" and inp.head_dim == 128 and inp.block_size in (16, 32)
+            and 2 <= cols <= 16):
         return "gqa"
     return "mha"
 

@@ -5,8 +5,9 @@
 // product O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16 (heads padded to
 // 16 columns).  One workgroup handles one (split, KV head, sequence): the
 // tile of a page is read from HBM once for all G heads.  Its NW waves take
-// pairs of pages round-robin (a pair is 32 tokens, the MFMA contraction
-// depth of the value product) and merge their running states in LDS at the
+// 32-token steps round-robin (the MFMA contraction depth of the value
+// product: a pair of 16-token pages, or one 32-token page) and merge their
+// running states in LDS at the
 // end, which yields the split's (o_s, lse_s) of Flash-Decoding's second step
 // (the "flash decoding ++" entry, its three-steps snippet).  NW is 4 (two
 // workgroups per CU), or 8 when the grid holds one workgroup per CU: a
@@ -35,9 +36,7 @@ namespace pa {
 namespace {
 
 constexpr int kD = 128;                 // head dim
-constexpr int kBS = 16;                 // tokens per page
 constexpr int kRowB = kD * 2;           // bytes per K row
-constexpr int kTile = kBS * kRowB;      // bytes per (page, head) tile, K and V alike
 constexpr int kOPad = kD + 4;           // LDS row stride of the merge buffer (floats)
 
 struct PairTile {
@@ -58,12 +57,12 @@ struct PairTile {
 // the same page) each hold half of what the other needs; widen() trades
 // those halves with v_permlane16_swap.
 constexpr int kRowB8 = kD;              // bytes per FP8 K row
-constexpr int kTile8 = kBS * kRowB8;    // bytes per FP8 (page, head) tile
 struct PairTile8 {
   u32x4 k[2][2];
   u32x4 v[4];
 };
 
+template <int BS>
 __device__ __forceinline__ void load_pair(PairTile8& t, const char* ka, const char* kb_,
                                           const char* va, const char* vb, int koff, int voff,
                                           bool ksel, bool vsel) {
@@ -74,7 +73,7 @@ __device__ __forceinline__ void load_pair(PairTile8& t, const char* ka, const ch
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) t.k[c][kb2] = ld128_stream(kp + c * 4 * kRowB8 + kb2 * 64);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) t.v[j] = ld128_stream(vp + j * 32 * kBS);
+  for (int j = 0; j < 4; ++j) t.v[j] = ld128_stream(vp + j * 32 * BS);
 }
 
 // Trade words between lanes l and l ^ 16: odd rows of `a` take the even
@@ -108,6 +107,7 @@ __device__ __forceinline__ void widen(const PairTile8& f, PairTile& t) {
   }
 }
 
+template <int BS>
 __device__ __forceinline__ void load_pair(PairTile& t, const char* ka, const char* kb_,
                                           const char* va, const char* vb, int koff, int voff,
                                           bool ksel, bool vsel) {
@@ -118,7 +118,7 @@ __device__ __forceinline__ void load_pair(PairTile& t, const char* ka, const cha
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) t.k[c][kb] = ld128_stream(kp + c * 4 * kRowB + kb * 64);
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) t.v[nb] = ld128_stream(vp + nb * 16 * 32);
+  for (int nb = 0; nb < 8; ++nb) t.v[nb] = ld128_stream(vp + nb * 16 * (2 * BS));
 }
 
 __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
@@ -205,11 +205,15 @@ __device__ __forceinline__ PairTile& bf16_tile(Tile& tin, PairTile& tw) {
   }
 }
 
-template <int NW, bool F8>
+// BS: tokens per page, 16 or 32.  A step consumes 32 tokens: two 16-token
+// pages, or one 32-token page as two halves of 16 (K rows 16 apart, V
+// tokens 16 apart within each dim's row), so the lane layouts are the same.
+template <int NW, bool F8, int BS>
 __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
   using Tile = typename std::conditional<F8, PairTile8, PairTile>::type;
-  constexpr int kT = F8 ? kTile8 : kTile;               // bytes per (page, head) tile
   constexpr int kR = F8 ? kRowB8 : kRowB;               // bytes per K row
+  constexpr int kT = BS * kR;                           // bytes per (page, head) tile
+  constexpr int kVR = F8 ? BS : 2 * BS;                 // bytes per V row (one dim)
   const int kvh = blockIdx.x;
   int b, s;
   if (p.sched) {
@@ -234,7 +238,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
   const int cj = n / G, cg = n - cj * G;
   const int ctx_col = ctx - ql + 1 + cj;
   const int ctx_lo = ctx - ql + 1;                   // the shortest any column sees
-  const int pages = (ctx + kBS - 1) / kBS;
+  const int pages = (ctx + BS - 1) / BS;
   const int nsplit = splits_of(pages, p.c);
   if (s >= (nsplit > 0 ? nsplit : 1)) return;
   const int p0 = s * p.c;
@@ -264,34 +268,43 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
   const bool ksel = (n >> 3) != 0;
   const int koff = (((n >> 2) & 1) * 8 + (n & 3)) * kR + quad * 16;
   const bool vsel = (quad >> 1) != 0;
-  const int voff = F8 ? (16 * (quad & 1) + n) * kBS : n * 32 + (quad & 1) * 16;
+  // the V bytes of the lane's 16-token page, or of its half of a 32-token one
+  const int vhalf = BS == 32 && vsel ? kVR / 2 : 0;
+  const int voff = (F8 ? (16 * (quad & 1) + n) * kVR : n * kVR + (quad & 1) * 16) + vhalf;
 
   f32x4 acc[8];
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = kNegInf, l = 0.f;
 
-  const int npairs = (p1 - p0 + 1) >> 1;
+  // 32-token steps: page pairs, or single 32-token pages
+  const int npairs = BS == 32 ? p1 - p0 : (p1 - p0 + 1) >> 1;
   int k = w;
   auto issue = [&](Tile& t, int kk) {
     if (kk >= npairs) {                              // past the split: read zeros (L2)
       const char* z = reinterpret_cast<const char*>(g_zero_tile);
-      load_pair(t, z, z, z, z, koff, voff, ksel, vsel);
+      load_pair<BS>(t, z, z, z, z, koff, voff, ksel, vsel);
       return;
     }
-    const int pa_ = p0 + 2 * kk;
-    const bool hasb = pa_ + 1 < p1;
-    const int ida = clampi(bt[pa_], 0, p.nblocks - 1);
-    const int idb = hasb ? clampi(bt[pa_ + 1], 0, p.nblocks - 1) : ida;
-    load_pair(t, kbase + ida * pstride, kbase + idb * pstride, vbase + ida * pstride,
-              vbase + idb * pstride, koff, voff, ksel, vsel);
+    if constexpr (BS == 32) {
+      const size_t off = (size_t)clampi(bt[p0 + kk], 0, p.nblocks - 1) * pstride;
+      load_pair<BS>(t, kbase + off, kbase + off + 16 * kR, vbase + off, vbase + off, koff, voff,
+                    ksel, vsel);
+    } else {
+      const int pa_ = p0 + 2 * kk;
+      const bool hasb = pa_ + 1 < p1;
+      const int ida = clampi(bt[pa_], 0, p.nblocks - 1);
+      const int idb = hasb ? clampi(bt[pa_ + 1], 0, p.nblocks - 1) : ida;
+      load_pair<BS>(t, kbase + ida * pstride, kbase + idb * pstride, vbase + ida * pstride,
+                    vbase + idb * pstride, koff, voff, ksel, vsel);
+    }
   };
   auto consume = [&](Tile& tin, int kk) {
-    const int pa_ = p0 + 2 * kk;
-    const bool hasb = pa_ + 1 < p1;
-    const bool partial = !hasb || (pa_ + 2) * kBS > ctx_lo;
-    const int mypage = vsel ? pa_ + 1 : pa_;
-    const int tok0 = (vsel && !hasb) ? -1 : mypage * kBS + (quad & 1) * 8;
+    // the step's first token and whether its second 16 tokens exist
+    const int tok_step = BS == 32 ? (p0 + kk) * 32 : (p0 + 2 * kk) * 16;
+    const bool hasb = BS == 32 || p0 + 2 * kk + 1 < p1;
+    const bool partial = !hasb || tok_step + 32 > ctx_lo;
+    const int tok0 = (vsel && !hasb) ? -1 : tok_step + (vsel ? 16 : 0) + (quad & 1) * 8;
     PairTile tw;
     PairTile& t = bf16_tile<F8>(tin, tw);
     if (partial)
@@ -365,25 +378,32 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
   }
 }
 
-template <int NW>
-void launch_waves(const Params& p, bool fp8kv, hipStream_t st) {
+template <int NW, int BS>
+void launch_waves_bs(const Params& p, bool fp8kv, hipStream_t st) {
   dim3 grid(p.Hkv, p.S, p.B);
   if (fp8kv)
-    hipLaunchKernelGGL((gqa_mfma_partial<NW, true>), grid, dim3(NW * 64), 0, st, p);
+    hipLaunchKernelGGL((gqa_mfma_partial<NW, true, BS>), grid, dim3(NW * 64), 0, st, p);
   else
-    hipLaunchKernelGGL((gqa_mfma_partial<NW, false>), grid, dim3(NW * 64), 0, st, p);
+    hipLaunchKernelGGL((gqa_mfma_partial<NW, false, BS>), grid, dim3(NW * 64), 0, st, p);
+}
+template <int NW>
+void launch_waves(const Params& p, bool fp8kv, hipStream_t st) {
+  if (p.bs == 32)
+    launch_waves_bs<NW, 32>(p, fp8kv, st);
+  else
+    launch_waves_bs<NW, 16>(p, fp8kv, st);
 }
 
 }  // namespace
 
 bool gqa_mfma_fp8_supported(int D, int bs, int G, int ql) {
   const int cols = G * ql;
-  return D == kD && bs == kBS && G >= 1 && cols >= 2 && cols <= 16;
+  return D == kD && (bs == 16 || bs == 32) && G >= 1 && cols >= 2 && cols <= 16;
 }
 
 bool gqa_mfma_supported(bool bf16, int D, int Dv, int bs, int G, int ql) {
   const int cols = G * ql;
-  return bf16 && D == kD && Dv == kD && bs == kBS && G >= 1 && cols >= 2 && cols <= 16;
+  return bf16 && D == kD && Dv == kD && (bs == 16 || bs == 32) && G >= 1 && cols >= 2 && cols <= 16;
 }
 
 hipError_t launch_gqa_mfma(const Params& p, bool fp8kv, hipStream_t st) {

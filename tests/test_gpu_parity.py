@@ -155,9 +155,15 @@ SMALL = {
                             context_lens=[1, 300, 17, 64, 65, 250, 3, 129, 200, 31, 32, 33,
                                           280, 90, 7, 160, 161, 15, 16, 100, 45, 222, 2, 199],
                             num_blocks=400),
-    # grouped heads on 32-token pages run on the VALU kernel
+    # grouped heads on 32-token pages: the matrix-core kernel takes each page as one 32-token
+    # step (its two 16-token halves), ragged tails inside a page and one-page contexts included
     "gqa_bf16_g4_bs32": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=8, num_kv_heads=2,
                              head_dim=128, block_size=32, context_lens=[40, 300], num_blocks=20),
+    "gqa_bf16_g8_bs32": dict(kind="mha", dtype="bf16", batch=5, num_q_heads=16, num_kv_heads=2,
+                             head_dim=128, block_size=32, context_lens=[1, 16, 17, 32, 1000],
+                             num_blocks=60),
+    "gqa_f32_g4_bs32": dict(kind="mha", dtype="f32", batch=2, num_q_heads=8, num_kv_heads=2,
+                            head_dim=128, block_size=32, context_lens=[33, 250], num_blocks=20),
 }
 
 
@@ -194,6 +200,9 @@ ROWS = {
     "rows_gqa_g2_q8": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=6, num_kv_heads=3,
                            head_dim=128, block_size=16, context_lens=[33, 95], num_blocks=20,
                            q_len=8),
+    "rows_gqa_g4_q4_bs32": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=8,
+                                num_kv_heads=2, head_dim=128, block_size=32,
+                                context_lens=[2, 33, 333], num_blocks=30, q_len=4),
     "rows_mla_h128_q2": dict(kind="mla", dtype="bf16", batch=2, num_q_heads=128, num_kv_heads=1,
                              head_dim=576, head_dim_v=512, block_size=64, context_lens=[65, 300],
                              num_blocks=12, scale=192 ** -0.5, q_len=2),
@@ -259,6 +268,12 @@ FP8 = {
     "fp8_rows_gqa_g4_q4": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=8, num_kv_heads=2,
                                head_dim=128, block_size=16, context_lens=[2, 17, 333],
                                num_blocks=60, q_len=4, **FP8_KV),
+    "fp8_gqa_g8_bs32": dict(kind="mha", dtype="bf16", batch=4, num_q_heads=16, num_kv_heads=2,
+                            head_dim=128, block_size=32, context_lens=[1, 31, 48, 900],
+                            num_blocks=60, **FP8_KV),
+    "fp8_rows_gqa_g4_q2_bs32": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=8,
+                                    num_kv_heads=2, head_dim=128, block_size=32,
+                                    context_lens=[1, 333], num_blocks=30, q_len=2, **FP8_KV),
     # pages of one, two and eleven (the last ragged) with a one-token sequence
     "fp8_mla_h128": dict(MLA_DIMS, batch=3, num_q_heads=128, context_lens=[1, 100, 700],
                          num_blocks=24, **FP8_LATENT),

@@ -44,10 +44,12 @@ def _draw(seed: int) -> tuple[dict, int]:
         ql = int(r.choice([q for q in (1, 2, 4, 8, 16) if G * q <= 16]))
         Hkv = int(r.integers(1, 4))
         fp8 = r.random() < 0.4
+        bs = int(r.choice([16, 32]))
         spec = dict(kind="mha", dtype="bf16", num_q_heads=G * Hkv, num_kv_heads=Hkv,
-                    head_dim=128, block_size=16)
+                    head_dim=128, block_size=bs)
         maxlen = 900
-    elif kind == "gqa_valu":                 # grouped heads on the VALU kernel: D 64 or bs 32
+    elif kind == "gqa_valu":                 # grouped heads with D 64 or fp32 on the VALU kernel
+                                             # (bf16 D 128 on 32-token pages: the MFMA kernel)
         G = int(r.choice([2, 4]))
         D, bs = [(64, 16), (128, 32), (64, 32)][int(r.integers(0, 3))]
         spec = dict(kind="mha", dtype=str(r.choice(["f32", "bf16"])), num_q_heads=2 * G,
