@@ -36,3 +36,22 @@ def test_committed_profiles_name_a_known_workload_and_family():
         text = open(os.path.join(bench.PROFILES, f"pmc_{name}.md")).read()
         assert re.search(r"kernel_source_sha256: [0-9a-f]{16}", text), name
         assert bench.kernel_family(make_config(name, values=False)) in bench.KERNEL_SOURCES
+
+
+def test_committed_profiles_match_the_kernel_sources():
+    """Every committed summary was measured on the kernel sources in the tree: its recorded
+    source hash is today's hash of the sources of the kernel its workload runs on."""
+    from workloads import make_config
+    pat = re.compile(r"^(trace|pmc|mfma)_(.+)\.md$")
+    seen = 0
+    for f in sorted(os.listdir(bench.PROFILES)):
+        m = pat.match(f)
+        if not m:
+            continue
+        family = bench.kernel_family(make_config(m.group(2), values=False))
+        text = open(os.path.join(bench.PROFILES, f)).read()
+        got = re.search(r"kernel_source_sha256: ([0-9a-f]{16})", text)
+        assert got, f
+        assert got.group(1) == bench.kernel_source_hash(family), (f, family)
+        seen += 1
+    assert seen >= 30
