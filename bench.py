@@ -52,7 +52,7 @@ def kernel_family(inp) -> str:
     if inp.kind == "mla":
         return "mla"
     cols = inp.num_q_heads // inp.num_kv_heads * inp.q_len   # MFMA columns: (row, head) pairs
-    if (inp.dtype == "bf16" and inp.head_dim == 128 and inp.block_size in (16, 32)
+    if (inp.dtype == "bf16" and inp.head_dim in (64, 128) and inp.block_size in (16, 32)
             and 2 <= cols <= 16):
         return "gqa"
     return "mha"

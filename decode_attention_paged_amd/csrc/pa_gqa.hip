@@ -35,16 +35,14 @@
 namespace pa {
 namespace {
 
-constexpr int kD = 128;                 // head dim
-constexpr int kRowB = kD * 2;           // bytes per K row
-constexpr int kOPad = kD + 4;           // LDS row stride of the merge buffer (floats)
-
+// D: head dim, 64 or 128 (D / 32 score k-steps, D / 16 value dim blocks).
+template <int D>
 struct PairTile {
-  u32x4 k[2][4];   // [chain][k-step]
-  u32x4 v[8];      // [dim block]
+  u32x4 k[2][D / 32];   // [chain][k-step]
+  u32x4 v[D / 16];      // [dim block]
 };
 
-// The same pair of pages with FP8 E4M3 caches (rows of 128 bytes), as
+// The same pair of pages with FP8 E4M3 caches (rows of D bytes), as
 // loaded.  The contraction order over dims is free as long as K and Q use
 // the same one, so a lane loads 16 contiguous dims of its K row at once:
 // k[c][kb2] holds dims (kb2*4 + quad)*16 .. +15, which become the A operands
@@ -56,14 +54,14 @@ struct PairTile {
 // 16*nb + n for every nb, so lanes l and l ^ 16 (rows quad and quad ^ 1 of
 // the same page) each hold half of what the other needs; widen() trades
 // those halves with v_permlane16_swap.
-constexpr int kRowB8 = kD;              // bytes per FP8 K row
+template <int D>
 struct PairTile8 {
-  u32x4 k[2][2];
-  u32x4 v[4];
+  u32x4 k[2][D / 64];
+  u32x4 v[D / 32];
 };
 
-template <int BS>
-__device__ __forceinline__ void load_pair(PairTile8& t, const char* ka, const char* kb_,
+template <int BS, int D>
+__device__ __forceinline__ void load_pair(PairTile8<D>& t, const char* ka, const char* kb_,
                                           const char* va, const char* vb, int koff, int voff,
                                           bool ksel, bool vsel) {
   const char* kp = (ksel ? kb_ : ka) + koff;
@@ -71,9 +69,9 @@ __device__ __forceinline__ void load_pair(PairTile8& t, const char* ka, const ch
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) t.k[c][kb2] = ld128_stream(kp + c * 4 * kRowB8 + kb2 * 64);
+    for (int kb2 = 0; kb2 < D / 64; ++kb2) t.k[c][kb2] = ld128_stream(kp + c * 4 * D + kb2 * 64);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) t.v[j] = ld128_stream(vp + j * 32 * BS);
+  for (int j = 0; j < D / 32; ++j) t.v[j] = ld128_stream(vp + j * 32 * BS);
 }
 
 // Trade words between lanes l and l ^ 16: odd rows of `a` take the even
@@ -85,11 +83,12 @@ __device__ __forceinline__ void swap_rows16(uint32_t& a, uint32_t& b) {
 }
 
 // Widen an FP8 pair tile to the bf16 operands consume_pair takes (exact).
-__device__ __forceinline__ void widen(const PairTile8& f, PairTile& t) {
+template <int D>
+__device__ __forceinline__ void widen(const PairTile8<D>& f, PairTile<D>& t) {
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < D / 32; ++kb) {
       const u32x4& w = f.k[c][kb >> 1];
       t.k[c][kb] = (kb & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
     }
@@ -98,7 +97,7 @@ __device__ __forceinline__ void widen(const PairTile8& f, PairTile& t) {
   // 0-7, then its own 8-15).  After the swap every lane has its 8 tokens of
   // both blocks: lo = block 2j, hi = block 2j + 1.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < D / 32; ++j) {
     uint32_t lo0 = f.v[j][0], lo1 = f.v[j][1], hi0 = f.v[j][2], hi1 = f.v[j][3];
     swap_rows16(lo0, hi0);
     swap_rows16(lo1, hi1);
@@ -107,8 +106,8 @@ __device__ __forceinline__ void widen(const PairTile8& f, PairTile& t) {
   }
 }
 
-template <int BS>
-__device__ __forceinline__ void load_pair(PairTile& t, const char* ka, const char* kb_,
+template <int BS, int D>
+__device__ __forceinline__ void load_pair(PairTile<D>& t, const char* ka, const char* kb_,
                                           const char* va, const char* vb, int koff, int voff,
                                           bool ksel, bool vsel) {
   const char* kp = (ksel ? kb_ : ka) + koff;
@@ -116,9 +115,9 @@ __device__ __forceinline__ void load_pair(PairTile& t, const char* ka, const cha
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) t.k[c][kb] = ld128_stream(kp + c * 4 * kRowB + kb * 64);
+    for (int kb = 0; kb < D / 32; ++kb) t.k[c][kb] = ld128_stream(kp + c * 4 * (2 * D) + kb * 64);
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) t.v[nb] = ld128_stream(vp + nb * 16 * (2 * BS));
+  for (int nb = 0; nb < D / 16; ++nb) t.v[nb] = ld128_stream(vp + nb * 16 * (2 * BS));
 }
 
 __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
@@ -126,8 +125,9 @@ __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <bool PARTIAL>
-__device__ __forceinline__ void consume_pair(PairTile& t, const u32x4 (&qf)[4], f32x4 (&acc)[8],
+template <bool PARTIAL, int D>
+__device__ __forceinline__ void consume_pair(PairTile<D>& t, const u32x4 (&qf)[D / 32],
+                                             f32x4 (&acc)[D / 16],
                                              float& m, float& l, float scale_log2, int tok0,
                                              int ctx_col, int ctx) {
   // tok0: logical index of this lane's first score token; the lane's tokens
@@ -136,7 +136,7 @@ __device__ __forceinline__ void consume_pair(PairTile& t, const u32x4 (&qf)[4], 
   // query row); V rows at or past ctx are zeroed.
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
+  for (int kb = 0; kb < D / 32; ++kb) {
     s0 = mfma(t.k[0][kb], qf[kb], s0);
     s1 = mfma(t.k[1][kb], qf[kb], s1);
   }
@@ -181,12 +181,12 @@ __device__ __forceinline__ void consume_pair(PairTile& t, const u32x4 (&qf)[4], 
       keep[e] = (v0 ? 0x0000ffffu : 0u) | (v1 ? 0xffff0000u : 0u);
     }
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
+    for (int nb = 0; nb < D / 16; ++nb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) t.v[nb][e] &= keep[e];
   }
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
+  for (int nb = 0; nb < D / 16; ++nb) {
     f32x4 a = acc[nb];
 #pragma unroll
     for (int r = 0; r < 4; ++r) a[r] *= alpha;
@@ -195,8 +195,8 @@ __device__ __forceinline__ void consume_pair(PairTile& t, const u32x4 (&qf)[4], 
 }
 
 // The bf16 operands of a loaded tile: the tile itself, or its FP8 codes widened into tw.
-template <bool F8, typename Tile>
-__device__ __forceinline__ PairTile& bf16_tile(Tile& tin, PairTile& tw) {
+template <bool F8, int D, typename Tile>
+__device__ __forceinline__ PairTile<D>& bf16_tile(Tile& tin, PairTile<D>& tw) {
   if constexpr (F8) {
     widen(tin, tw);
     return tw;
@@ -208,10 +208,12 @@ __device__ __forceinline__ PairTile& bf16_tile(Tile& tin, PairTile& tw) {
 // BS: tokens per page, 16 or 32.  A step consumes 32 tokens: two 16-token
 // pages, or one 32-token page as two halves of 16 (K rows 16 apart, V
 // tokens 16 apart within each dim's row), so the lane layouts are the same.
-template <int NW, bool F8, int BS>
+template <int NW, bool F8, int BS, int D>
 __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
-  using Tile = typename std::conditional<F8, PairTile8, PairTile>::type;
-  constexpr int kR = F8 ? kRowB8 : kRowB;               // bytes per K row
+  using Tile = typename std::conditional<F8, PairTile8<D>, PairTile<D>>::type;
+  constexpr int kKS = D / 32;                           // score k-steps
+  constexpr int kNB = D / 16;                           // value dim blocks
+  constexpr int kR = F8 ? D : 2 * D;                    // bytes per K row
   constexpr int kT = BS * kR;                           // bytes per (page, head) tile
   constexpr int kVR = F8 ? BS : 2 * BS;                 // bytes per V row (one dim)
   const int kvh = blockIdx.x;
@@ -245,12 +247,12 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
   const int p1 = min(pages, p0 + p.c);
 
   // Q^T as the B operand of the score MFMA: column n = (row cj, head kvh*G + cg)
-  u32x4 qf[4];
+  u32x4 qf[kKS];
   if (n < NC) {
     const char* qr =
-        static_cast<const char*>(p.q) + (((size_t)b * ql + cj) * p.Hq + kvh * G + cg) * kRowB;
+        static_cast<const char*>(p.q) + (((size_t)b * ql + cj) * p.Hq + kvh * G + cg) * (2 * D);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < kKS; ++kb) {
       // k-step kb: dims kb*32 + quad*8 (bf16 caches), or, in the FP8 tile's
       // order, (kb/2*4 + quad)*16 + (kb%2)*8
       const int qo = F8 ? (kb >> 1) * 128 + quad * 32 + (kb & 1) * 16 : kb * 64 + quad * 16;
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
     }
   } else {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) qf[kb] = u32x4{0u, 0u, 0u, 0u};
+    for (int kb = 0; kb < kKS; ++kb) qf[kb] = u32x4{0u, 0u, 0u, 0u};
   }
 
   const int* bt = p.block_table + (size_t)b * p.maxb;
@@ -272,9 +274,9 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
   const int vhalf = BS == 32 && vsel ? kVR / 2 : 0;
   const int voff = (F8 ? (16 * (quad & 1) + n) * kVR : n * kVR + (quad & 1) * 16) + vhalf;
 
-  f32x4 acc[8];
+  f32x4 acc[kNB];
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < kNB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = kNegInf, l = 0.f;
 
   // 32-token steps: page pairs, or single 32-token pages
@@ -305,8 +307,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
     const bool hasb = BS == 32 || p0 + 2 * kk + 1 < p1;
     const bool partial = !hasb || tok_step + 32 > ctx_lo;
     const int tok0 = (vsel && !hasb) ? -1 : tok_step + (vsel ? 16 : 0) + (quad & 1) * 8;
-    PairTile tw;
-    PairTile& t = bf16_tile<F8>(tin, tw);
+    PairTile<D> tw;
+    PairTile<D>& t = bf16_tile<F8, D>(tin, tw);
     if (partial)
       consume_pair<true>(t, qf, acc, m, l, p.scale_log2, tok0, ctx_col, ctx);
     else
@@ -331,20 +333,21 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
 
   // ---- merge the NW wave states per head and write the split result
   __shared__ float sm_m[NW][16], sm_l[NW][16];
+  constexpr int kOPad = D + 4;                          // LDS row stride of the merge buffer
   __shared__ float sm_o[NW][16][kOPad];
   if (quad == 0) {
     sm_m[w][n] = m;
     sm_l[w][n] = ltot;
   }
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb)
+  for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) sm_o[w][n][nb * 16 + quad * 4 + r] = acc[nb][r];
   __syncthreads();
 
   const bool direct = split_is_direct(p, nsplit);
-  for (int idx = threadIdx.x; idx < NC * kD; idx += NW * 64) {
-    const int hn = idx / kD, d = idx % kD;
+  for (int idx = threadIdx.x; idx < NC * D; idx += NW * 64) {
+    const int hn = idx / D, d = idx % D;
     const int rj = hn / G, rg = hn - rj * G;
     float M = kNegInf;
 #pragma unroll
@@ -364,7 +367,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
       store_out<true>(p, row, d, o);
       if (d == 0 && p.lse) p.lse[row] = lse;
     } else {
-      store_partial(p, p.o_part + (row * p.S + s) * kD + d, o);
+      store_partial(p, p.o_part + (row * p.S + s) * D + d, o);
       if (d == 0) store_partial(p, p.lse_part + row * p.S + s, lse);
     }
   }
@@ -378,32 +381,40 @@ __global__ __launch_bounds__(NW * 64) void gqa_mfma_partial(Params p) {
   }
 }
 
-template <int NW, int BS>
-void launch_waves_bs(const Params& p, bool fp8kv, hipStream_t st) {
+template <int NW, int BS, int D>
+void launch_shape(const Params& p, bool fp8kv, hipStream_t st) {
   dim3 grid(p.Hkv, p.S, p.B);
   if (fp8kv)
-    hipLaunchKernelGGL((gqa_mfma_partial<NW, true, BS>), grid, dim3(NW * 64), 0, st, p);
+    hipLaunchKernelGGL((gqa_mfma_partial<NW, true, BS, D>), grid, dim3(NW * 64), 0, st, p);
   else
-    hipLaunchKernelGGL((gqa_mfma_partial<NW, false, BS>), grid, dim3(NW * 64), 0, st, p);
+    hipLaunchKernelGGL((gqa_mfma_partial<NW, false, BS, D>), grid, dim3(NW * 64), 0, st, p);
+}
+template <int NW, int BS>
+void launch_dim(const Params& p, bool fp8kv, hipStream_t st) {
+  if (p.D == 64)
+    launch_shape<NW, BS, 64>(p, fp8kv, st);
+  else
+    launch_shape<NW, BS, 128>(p, fp8kv, st);
 }
 template <int NW>
 void launch_waves(const Params& p, bool fp8kv, hipStream_t st) {
   if (p.bs == 32)
-    launch_waves_bs<NW, 32>(p, fp8kv, st);
+    launch_dim<NW, 32>(p, fp8kv, st);
   else
-    launch_waves_bs<NW, 16>(p, fp8kv, st);
+    launch_dim<NW, 16>(p, fp8kv, st);
 }
 
 }  // namespace
 
 bool gqa_mfma_fp8_supported(int D, int bs, int G, int ql) {
   const int cols = G * ql;
-  return D == kD && (bs == 16 || bs == 32) && G >= 1 && cols >= 2 && cols <= 16;
+  return (D == 64 || D == 128) && (bs == 16 || bs == 32) && G >= 1 && cols >= 2 && cols <= 16;
 }
 
 bool gqa_mfma_supported(bool bf16, int D, int Dv, int bs, int G, int ql) {
   const int cols = G * ql;
-  return bf16 && D == kD && Dv == kD && (bs == 16 || bs == 32) && G >= 1 && cols >= 2 && cols <= 16;
+  return bf16 && (D == 64 || D == 128) && Dv == D && (bs == 16 || bs == 32) && G >= 1 &&
+         cols >= 2 && cols <= 16;
 }
 
 hipError_t launch_gqa_mfma(const Params& p, bool fp8kv, hipStream_t st) {

@@ -187,13 +187,14 @@ pa_status pa_workspace_init(const pa_shape* shape, int32_t num_splits, int32_t m
  * NULL only when S resolves to 1; its counters must be zero (see above).
  * Supported: PA_F32 with head_dim 64 or 128; PA_BF16 with head_dim 64 or 128;
  * head_dim_v == head_dim; block_size 16 or 32.  With q_len > 1: PA_BF16,
- * head_dim 128, block_size 16 or 32 and (num_q_heads / num_kv_heads) * q_len
- * <= 16 (each KV tile is then read once for all rows and heads of its group,
- * as for PA_BF16 grouped heads with one row); the splits are merged by a
- * reduction launch.  FP8 caches (kv_dtype PA_FP8_E4M3): PA_BF16 q, head_dim
- * 128, block_size 16 or 32, any q_len the bf16 path takes; codes are widened
- * to bfloat16 exactly, k_scale folds into the score scale and v_scale into
- * the outputs.
+ * head_dim 64 or 128, block_size 16 or 32 and (num_q_heads / num_kv_heads) *
+ * q_len <= 16 (each KV tile is then read once for all rows and heads of its
+ * group, as for PA_BF16 grouped heads with one row); the splits are merged by
+ * a reduction launch.  FP8 caches (kv_dtype PA_FP8_E4M3): PA_BF16 q,
+ * block_size 16 or 32, head_dim 128 with any q_len the bf16 path takes, or
+ * head_dim 64 with grouped heads or several rows; codes are widened to
+ * bfloat16 exactly, k_scale folds into the score scale and v_scale into the
+ * outputs.
  */
 pa_status pa_decode(const pa_shape* shape, const void* q, const void* k_cache,
                     const void* v_cache, const int32_t* block_table,

@@ -164,6 +164,12 @@ SMALL = {
                              num_blocks=60),
     "gqa_f32_g4_bs32": dict(kind="mha", dtype="f32", batch=2, num_q_heads=8, num_kv_heads=2,
                             head_dim=128, block_size=32, context_lens=[33, 250], num_blocks=20),
+    # 64-dim heads on the matrix-core kernel (two score k-steps, four value dim blocks)
+    "gqa_bf16_g4_d64": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=8, num_kv_heads=2,
+                            head_dim=64, block_size=16, context_lens=[1, 47, 400], num_blocks=40),
+    "gqa_bf16_g8_d64_bs32": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=16,
+                                 num_kv_heads=2, head_dim=64, block_size=32,
+                                 context_lens=[31, 700], num_blocks=30),
 }
 
 
@@ -203,6 +209,9 @@ ROWS = {
     "rows_gqa_g4_q4_bs32": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=8,
                                 num_kv_heads=2, head_dim=128, block_size=32,
                                 context_lens=[2, 33, 333], num_blocks=30, q_len=4),
+    "rows_gqa_g4_q2_d64": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=8,
+                               num_kv_heads=2, head_dim=64, block_size=16,
+                               context_lens=[1, 250], num_blocks=30, q_len=2),
     "rows_mla_h128_q2": dict(kind="mla", dtype="bf16", batch=2, num_q_heads=128, num_kv_heads=1,
                              head_dim=576, head_dim_v=512, block_size=64, context_lens=[65, 300],
                              num_blocks=12, scale=192 ** -0.5, q_len=2),
@@ -268,6 +277,9 @@ FP8 = {
     "fp8_rows_gqa_g4_q4": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=8, num_kv_heads=2,
                                head_dim=128, block_size=16, context_lens=[2, 17, 333],
                                num_blocks=60, q_len=4, **FP8_KV),
+    "fp8_gqa_g4_d64": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=8, num_kv_heads=2,
+                           head_dim=64, block_size=16, context_lens=[1, 17, 500], num_blocks=50,
+                           **FP8_KV),
     "fp8_gqa_g8_bs32": dict(kind="mha", dtype="bf16", batch=4, num_q_heads=16, num_kv_heads=2,
                             head_dim=128, block_size=32, context_lens=[1, 31, 48, 900],
                             num_blocks=60, **FP8_KV),

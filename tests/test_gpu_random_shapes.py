@@ -45,15 +45,15 @@ def _draw(seed: int) -> tuple[dict, int]:
         Hkv = int(r.integers(1, 4))
         fp8 = r.random() < 0.4
         bs = int(r.choice([16, 32]))
+        D = int(r.choice([64, 128]))
         spec = dict(kind="mha", dtype="bf16", num_q_heads=G * Hkv, num_kv_heads=Hkv,
-                    head_dim=128, block_size=bs)
+                    head_dim=D, block_size=bs)
         maxlen = 900
-    elif kind == "gqa_valu":                 # grouped heads with D 64 or fp32 on the VALU kernel
-                                             # (bf16 D 128 on 32-token pages: the MFMA kernel)
+    elif kind == "gqa_valu":                 # grouped heads in fp32: the VALU kernel
         G = int(r.choice([2, 4]))
         D, bs = [(64, 16), (128, 32), (64, 32)][int(r.integers(0, 3))]
-        spec = dict(kind="mha", dtype=str(r.choice(["f32", "bf16"])), num_q_heads=2 * G,
-                    num_kv_heads=2, head_dim=D, block_size=bs)
+        spec = dict(kind="mha", dtype="f32", num_q_heads=2 * G, num_kv_heads=2, head_dim=D,
+                    block_size=bs)
         ql, maxlen = 1, 600
     else:
         bs = 64 if kind == "mla_pages" else 1
