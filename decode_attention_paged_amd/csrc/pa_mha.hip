@@ -353,22 +353,26 @@ hipError_t launch_one(const Params& p, hipStream_t st) {
 
 }  // namespace
 
+// 256-dim heads: bfloat16 only (a float32 K row would need 64 lanes of 16 bytes)
 bool mha_valu_supported(bool bf16, int D, int bs) {
-  (void)bf16;
-  return (D == 64 || D == 128) && (bs == 16 || bs == 32);
+  return (D == 64 || D == 128 || (bf16 && D == 256)) && (bs == 16 || bs == 32);
 }
 
-bool mha_valu_fp8_supported(int D, int bs) { return D == 128 && (bs == 16 || bs == 32); }
+bool mha_valu_fp8_supported(int D, int bs) { return (D == 128 || D == 256) && (bs == 16 || bs == 32); }
 
 hipError_t launch_mha_valu(const Params& p, bool bf16, bool fp8kv, hipStream_t st) {
   const int D = p.D, bs = p.bs;
   if (fp8kv) {
     if (!bf16) return hipErrorInvalidValue;
+    if (D == 256 && bs == 16) return launch_one<true, 256, 16, true>(p, st);
+    if (D == 256 && bs == 32) return launch_one<true, 256, 32, true>(p, st);
     if (D == 128 && bs == 16) return launch_one<true, 128, 16, true>(p, st);
     if (D == 128 && bs == 32) return launch_one<true, 128, 32, true>(p, st);
     return hipErrorInvalidValue;
   }
   if (bf16) {
+    if (D == 256 && bs == 16) return launch_one<true, 256, 16>(p, st);
+    if (D == 256 && bs == 32) return launch_one<true, 256, 32>(p, st);
     if (D == 128 && bs == 16) return launch_one<true, 128, 16>(p, st);
     if (D == 128 && bs == 32) return launch_one<true, 128, 32>(p, st);
     if (D == 64 && bs == 16) return launch_one<true, 64, 16>(p, st);

@@ -185,14 +185,15 @@ pa_status pa_workspace_init(const pa_shape* shape, int32_t num_splits, int32_t m
  * when a reduction launch merges every unit in parallel instead (see
  * pa_decode_launches).  `lse` may be NULL.  `workspace` may be
  * NULL only when S resolves to 1; its counters must be zero (see above).
- * Supported: PA_F32 with head_dim 64 or 128; PA_BF16 with head_dim 64 or 128;
+ * Supported: PA_F32 with head_dim 64 or 128; PA_BF16 with head_dim 64, 128 or 256;
  * head_dim_v == head_dim; block_size 16 or 32.  With q_len > 1: PA_BF16,
  * head_dim 64 or 128, block_size 16 or 32 and (num_q_heads / num_kv_heads) *
  * q_len <= 16 (each KV tile is then read once for all rows and heads of its
  * group, as for PA_BF16 grouped heads with one row); the splits are merged by
  * a reduction launch.  FP8 caches (kv_dtype PA_FP8_E4M3): PA_BF16 q,
- * block_size 16 or 32, head_dim 128 with any q_len the bf16 path takes, or
- * head_dim 64 with grouped heads or several rows; codes are widened to
+ * block_size 16 or 32, head_dim 128 with any q_len the bf16 path takes,
+ * head_dim 256 with one row, or head_dim 64 with grouped heads or several
+ * rows; codes are widened to
  * bfloat16 exactly, k_scale folds into the score scale and v_scale into the
  * outputs.
  */

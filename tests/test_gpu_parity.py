@@ -164,6 +164,13 @@ SMALL = {
                              num_blocks=60),
     "gqa_f32_g4_bs32": dict(kind="mha", dtype="f32", batch=2, num_q_heads=8, num_kv_heads=2,
                             head_dim=128, block_size=32, context_lens=[33, 250], num_blocks=20),
+    # 256-dim heads (bf16) on the VALU kernel: plain, grouped and on 32-token pages
+    "mha_bf16_d256": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=2, num_kv_heads=2,
+                          head_dim=256, block_size=16, context_lens=[1, 200], num_blocks=20),
+    "gqa_bf16_g2_d256": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=4, num_kv_heads=2,
+                             head_dim=256, block_size=16, context_lens=[37, 300], num_blocks=30),
+    "mha_bf16_d256_bs32": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=2, num_kv_heads=2,
+                               head_dim=256, block_size=32, context_lens=[33, 150], num_blocks=12),
     # 64-dim heads on the matrix-core kernel (two score k-steps, four value dim blocks)
     "gqa_bf16_g4_d64": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=8, num_kv_heads=2,
                             head_dim=64, block_size=16, context_lens=[1, 47, 400], num_blocks=40),
@@ -277,6 +284,12 @@ FP8 = {
     "fp8_rows_gqa_g4_q4": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=8, num_kv_heads=2,
                                head_dim=128, block_size=16, context_lens=[2, 17, 333],
                                num_blocks=60, q_len=4, **FP8_KV),
+    "fp8_mha_d256": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=2, num_kv_heads=2,
+                         head_dim=256, block_size=16, context_lens=[15, 260], num_blocks=30,
+                         **FP8_KV),
+    "fp8_gqa_g2_d256_bs32": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=4,
+                                 num_kv_heads=2, head_dim=256, block_size=32,
+                                 context_lens=[1, 170], num_blocks=12, **FP8_KV),
     "fp8_gqa_g4_d64": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=8, num_kv_heads=2,
                            head_dim=64, block_size=16, context_lens=[1, 17, 500], num_blocks=50,
                            **FP8_KV),

@@ -32,10 +32,10 @@ def _draw(seed: int) -> tuple[dict, int]:
     fp8 = False
     if kind == "mha_valu":
         dtype = str(r.choice(["f32", "bf16"]))
-        D = int(r.choice([64, 128]))
+        D = int(r.choice([64, 128] if dtype == "f32" else [64, 128, 256]))
         bs = int(r.choice([16, 32]))
         H = int(r.integers(1, 9))
-        fp8 = dtype == "bf16" and D == 128 and bs == 16 and r.random() < 0.4
+        fp8 = dtype == "bf16" and D >= 128 and r.random() < 0.4
         spec = dict(kind="mha", dtype=dtype, num_q_heads=H, num_kv_heads=H, head_dim=D,
                     block_size=bs)
         ql, maxlen = 1, 700
