@@ -48,8 +48,9 @@ struct PairTile {
 // k[c][kb2] holds dims (kb2*4 + quad)*16 .. +15, which become the A operands
 // of k-steps 2*kb2 (first 8) and 2*kb2 + 1; the query operands follow the
 // same order.
-// A V row of one dim is 16 bytes (16 tokens).  Lane (n, quad) loads whole
-// rows: v[j] holds dim 16*(2j + (quad & 1)) + n, all 16 tokens of page
+// A V row of one dim is 16 bytes (16 tokens; on 32-token pages each
+// 16-token half of the 32-byte row).  Lane (n, quad) loads whole rows:
+// v[j] holds dim 16*(2j + (quad & 1)) + n, all 16 tokens of page (or half)
 // quad / 2.  The value operand needs tokens 8*(quad & 1) .. +7 of dims
 // 16*nb + n for every nb, so lanes l and l ^ 16 (rows quad and quad ^ 1 of
 // the same page) each hold half of what the other needs; widen() trades

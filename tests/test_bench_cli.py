@@ -55,3 +55,11 @@ def test_committed_profiles_match_the_kernel_sources():
         assert got.group(1) == bench.kernel_source_hash(family), (f, family)
         seen += 1
     assert seen >= 30
+
+
+def test_every_workload_has_full_size_parity():
+    """Each benchmark workload is also a full-size parity case."""
+    from workloads import CONFIG_ORDER
+    src = open(os.path.join(ROOT, "tests", "test_gpu_parity.py")).read()
+    full = re.search(r"FULL = \[(.*?)\]", src, re.S).group(1)
+    assert sorted(re.findall(r'"([a-z0-9_]+)"', full)) == sorted(CONFIG_ORDER)

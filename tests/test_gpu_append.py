@@ -28,6 +28,13 @@ CASES = {
     "gqa_fp8": dict(kind="mha", dtype="bf16", batch=4, num_q_heads=16, num_kv_heads=2,
                     head_dim=128, block_size=16, context_lens=[33, 1, 300, 16], num_blocks=40,
                     kv_dtype="fp8", k_scale=0.05, v_scale=0.3),
+    # 32-token pages with 64-dim heads (the grouped-query kernel decodes them), and 256-dim
+    # heads on 32-token pages (the VALU kernel)
+    "gqa_bf16_d64_bs32": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=16, num_kv_heads=4,
+                              head_dim=64, block_size=32, context_lens=[31, 32, 100],
+                              num_blocks=20),
+    "mha_bf16_d256_bs32": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=2, num_kv_heads=2,
+                               head_dim=256, block_size=32, context_lens=[63, 1], num_blocks=10),
     "mla_bf16": dict(kind="mla", dtype="bf16", batch=3, num_q_heads=16, num_kv_heads=1,
                      head_dim=576, head_dim_v=512, block_size=64, context_lens=[65, 64, 1],
                      num_blocks=12, scale=192 ** -0.5),

@@ -346,7 +346,8 @@ def test_fp8_kv(name):
 FULL = ["tiny_mha_f32", "llama_mha_bf16", "long_gqa_bf16", "ragged_gqa_bf16", "mla_bf16",
         "mla_topk_bf16", "mla_allentries_bf16", "llama_mha_q4_bf16", "long_gqa_q4_bf16",
         "mla_q2_bf16", "llama_mha_fp8", "long_gqa_fp8", "ragged_gqa_fp8", "mla_fp8",
-        "mla_topk_fp8", "serving_gqa_bf16"]
+        "mla_topk_fp8", "serving_gqa_bf16", "long_gqa_d64_bf16", "ragged_gqa_bs32_bf16",
+        "llama_mha_d256_bf16"]
 
 
 @pytest.mark.parametrize("name", FULL)

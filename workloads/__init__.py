@@ -383,12 +383,33 @@ CONFIGS = {
         k_scale=0.017, v_scale=0.019,
         meta=dict(desc="ragged GQA, FP8 E4M3 KV (bf16 q): 64 seqs, ctx log-U[128,32768], "
                        "64 q / 8 kv heads, D128, bs16")),
+    # Other head sizes and page sizes on the same kernels: grouped 64-dim heads at long
+    # context (a 32 q / 8 kv-head, 64-dim model), the ragged batch on 32-token pages, and
+    # 256-dim MHA heads (16 heads of 256).
+    "long_gqa_d64_bf16": dict(
+        kind="mha", dtype="bf16", batch=1, num_q_heads=32, num_kv_heads=8, head_dim=64,
+        block_size=16, context_lens=[131072], num_blocks=8192, scale=1.0 / 8.0, seed=3,
+        meta=dict(desc="long-context GQA bf16, 64-dim heads: B1, 32 q / 8 kv heads, D64, "
+                       "ctx 131072, bs16")),
+    "ragged_gqa_bs32_bf16": dict(
+        kind="mha", dtype="bf16", batch=64, num_q_heads=64, num_kv_heads=8, head_dim=128,
+        block_size=32, context_lens=_loguniform_ctx(128, 32768, 64), num_blocks=32768,
+        max_blocks_per_seq=1024, scale=1.0 / math.sqrt(128), seed=4,
+        meta=dict(desc="ragged GQA bf16 on 32-token pages: 64 seqs, ctx log-U[128,32768], "
+                       "64 q / 8 kv heads, D128, bs32")),
+    "llama_mha_d256_bf16": dict(
+        kind="mha", dtype="bf16", batch=16, num_q_heads=16, num_kv_heads=16, head_dim=256,
+        block_size=16, context_lens=_uniform_ctx(1024, 4096, 16), num_blocks=65536,
+        max_blocks_per_seq=256, scale=1.0 / 16.0, seed=2,
+        meta=dict(desc="MHA bf16, 256-dim heads: B16, 16 heads, D256, ctx U[1024,4096], bs16, "
+                       "65536-page pool")),
 }
 
 CONFIG_ORDER = ["tiny_mha_f32", "llama_mha_bf16", "long_gqa_bf16", "ragged_gqa_bf16", "mla_bf16",
                 "mla_topk_bf16", "mla_allentries_bf16", "llama_mha_q4_bf16", "long_gqa_q4_bf16",
                 "mla_q2_bf16", "llama_mha_fp8", "long_gqa_fp8", "ragged_gqa_fp8", "mla_fp8",
-                "mla_topk_fp8", "serving_gqa_bf16"]
+                "mla_topk_fp8", "serving_gqa_bf16", "long_gqa_d64_bf16", "ragged_gqa_bs32_bf16",
+                "llama_mha_d256_bf16"]
 
 
 def make_config(name: str, *, poison: bool = True, values: bool = True, seed: int | None = None,
