@@ -22,7 +22,7 @@ from test_gpu_parity import compare, run, say
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 96
+N_CASES = 192
 
 
 def _draw(seed: int) -> tuple[dict, int]:
