@@ -44,7 +44,7 @@ struct MhaCfg {
   static constexpr int DPI = 64 / LPD;     // dims per V load (1 KiB)
   static constexpr int VI = D / DPI;       // V loads per page = partial sums per lane
   static constexpr int TPL = BS / LPD;     // tokens per lane in a V load (16 / ES)
-  static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row width");
+  static_assert(LPR == 4 || LPR == 8 || LPR == 16 || LPR == 32, "row width");
   static_assert(!F8 || BF16, "FP8 caches take bf16 queries");
   static_assert(BS % RPI == 0 && VROWB % 16 == 0 && LPD <= 8 && D % DPI == 0, "tile shape");
   static_assert(TPL == 16 / ES, "a V load holds whole tokens");
@@ -53,7 +53,10 @@ struct MhaCfg {
 // Sum over the LPR lanes of one K row.
 template <int LPR>
 __device__ __forceinline__ float row_sum(float x) {
-  if constexpr (LPR == 8) {
+  if constexpr (LPR == 4) {
+    x += dpp<kDppQuadXor2>(x);
+    return x + dpp<kDppQuadXor1>(x);
+  } else if constexpr (LPR == 8) {
     return group_sum<8>(x);
   } else if constexpr (LPR == 16) {
     return group_sum<16>(x);
@@ -63,15 +66,19 @@ __device__ __forceinline__ float row_sum(float x) {
 }
 
 // Max / sum across the RPI row groups of a wave.
+// (rows of 4 lanes: the four row groups of a 16-lane DPP row are lanes 4
+// apart, combined by rotations of 4 and 8)
 template <int LPR>
 __device__ __forceinline__ float across_rows_max(float x) {
-  if constexpr (LPR == 8) x = fmaxf(x, dpp<kDppRowRor8>(x));
+  if constexpr (LPR == 4) x = fmaxf(x, dpp<kDppRowRor4>(x));
+  if constexpr (LPR <= 8) x = fmaxf(x, dpp<kDppRowRor8>(x));
   if constexpr (LPR <= 16) x = max_xor16(x);
   return max_xor32(x);
 }
 template <int LPR>
 __device__ __forceinline__ float across_rows_sum(float x) {
-  if constexpr (LPR == 8) x += dpp<kDppRowRor8>(x);
+  if constexpr (LPR == 4) x += dpp<kDppRowRor4>(x);
+  if constexpr (LPR <= 8) x += dpp<kDppRowRor8>(x);
   if constexpr (LPR <= 16) x = sum_xor16(x);
   return sum_xor32(x);
 }
@@ -358,12 +365,16 @@ bool mha_valu_supported(bool bf16, int D, int bs) {
   return (D == 64 || D == 128 || (bf16 && D == 256)) && (bs == 16 || bs == 32);
 }
 
-bool mha_valu_fp8_supported(int D, int bs) { return (D == 128 || D == 256) && (bs == 16 || bs == 32); }
+bool mha_valu_fp8_supported(int D, int bs) {
+  return (D == 64 || D == 128 || D == 256) && (bs == 16 || bs == 32);
+}
 
 hipError_t launch_mha_valu(const Params& p, bool bf16, bool fp8kv, hipStream_t st) {
   const int D = p.D, bs = p.bs;
   if (fp8kv) {
     if (!bf16) return hipErrorInvalidValue;
+    if (D == 64 && bs == 16) return launch_one<true, 64, 16, true>(p, st);
+    if (D == 64 && bs == 32) return launch_one<true, 64, 32, true>(p, st);
     if (D == 256 && bs == 16) return launch_one<true, 256, 16, true>(p, st);
     if (D == 256 && bs == 32) return launch_one<true, 256, 32, true>(p, st);
     if (D == 128 && bs == 16) return launch_one<true, 128, 16, true>(p, st);

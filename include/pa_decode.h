@@ -191,9 +191,8 @@ pa_status pa_workspace_init(const pa_shape* shape, int32_t num_splits, int32_t m
  * q_len <= 16 (each KV tile is then read once for all rows and heads of its
  * group, as for PA_BF16 grouped heads with one row); the splits are merged by
  * a reduction launch.  FP8 caches (kv_dtype PA_FP8_E4M3): PA_BF16 q,
- * block_size 16 or 32, head_dim 128 with any q_len the bf16 path takes,
- * head_dim 256 with one row, or head_dim 64 with grouped heads or several
- * rows; codes are widened to
+ * block_size 16 or 32, head_dim 64 or 128 with any q_len the bf16 path
+ * takes, or head_dim 256 with one row; codes are widened to
  * bfloat16 exactly, k_scale folds into the score scale and v_scale into the
  * outputs.
  */

@@ -119,8 +119,9 @@ def test_null_shape_and_pointers(lib):
     dict(max_context_len=(1 << 29) + 16, max_blocks_per_seq=(1 << 25) + 1),  # past 2^29 tokens
     dict(num_q_heads=1 << 16, num_kv_heads=1 << 16, batch=65535),             # rows past 2^31
     dict(kv_dtype=_lib.PA_FP8_E4M3, k_scale=0.1, v_scale=0.1, dtype=_lib.PA_F32),   # FP8: bf16 q
-    # FP8 with 64-dim heads: grouped heads or several rows only (matrix-core kernel)
-    dict(kv_dtype=_lib.PA_FP8_E4M3, k_scale=0.1, v_scale=0.1, head_dim=64, head_dim_v=64),
+    # FP8 with 256-dim heads: one query row only (the VALU kernel)
+    dict(kv_dtype=_lib.PA_FP8_E4M3, k_scale=0.1, v_scale=0.1, head_dim=256, head_dim_v=256,
+         q_len=2),
 ])
 
 def test_unsupported(lib, kw):

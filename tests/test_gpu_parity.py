@@ -258,9 +258,11 @@ def test_several_rows(name):
 # ----------------------------------------------------------------------------------------------
 
 FP8_KV = dict(kv_dtype="fp8", k_scale=0.037, v_scale=1.9)
-# One latent row holds keys and values: codes are N(0,1) / k_scale, so v_scale near k_scale
-# keeps the values (and outputs) near unit size, where the absolute bound applies.
-FP8_LATENT = dict(kv_dtype="fp8", k_scale=0.037, v_scale=0.045)
+# One latent row holds keys and values: codes are N(0,1) / k_scale, so v_scale below k_scale
+# keeps the values (and outputs) near unit size, where the absolute bound applies: a latent
+# output is rounded to bfloat16 twice (the split partial, then the output), up to 2^-8 |o|
+# each time, which stays within 2e-2 for |o| <= 2.5 (one-token contexts copy a value).
+FP8_LATENT = dict(kv_dtype="fp8", k_scale=0.037, v_scale=0.02)
 MLA_DIMS = dict(kind="mla", dtype="bf16", num_kv_heads=1, head_dim=576, head_dim_v=512,
                 block_size=64, scale=192 ** -0.5)
 FP8 = {
@@ -284,6 +286,13 @@ FP8 = {
     "fp8_rows_gqa_g4_q4": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=8, num_kv_heads=2,
                                head_dim=128, block_size=16, context_lens=[2, 17, 333],
                                num_blocks=60, q_len=4, **FP8_KV),
+    # 64-dim heads on the VALU kernel: a K row is 4 lanes of 16 codes
+    "fp8_mha_d64": dict(kind="mha", dtype="bf16", batch=3, num_q_heads=3, num_kv_heads=3,
+                        head_dim=64, block_size=16, context_lens=[1, 16, 333], num_blocks=40,
+                        **FP8_KV),
+    "fp8_mha_d64_bs32": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=2, num_kv_heads=2,
+                             head_dim=64, block_size=32, context_lens=[31, 200], num_blocks=12,
+                             **FP8_KV),
     "fp8_mha_d256": dict(kind="mha", dtype="bf16", batch=2, num_q_heads=2, num_kv_heads=2,
                          head_dim=256, block_size=16, context_lens=[15, 260], num_blocks=30,
                          **FP8_KV),
@@ -391,7 +400,7 @@ PROP_MLA = dict(kind="mla", dtype="bf16", batch=2, num_q_heads=32, num_kv_heads=
 # 128 heads on 64-token pages: the wide latent workgroup
 PROP_MLA128 = dict(PROP_MLA, num_q_heads=128)
 # the same on an FP8 latent cache
-PROP_MLA128_FP8 = dict(PROP_MLA128, kv_dtype="fp8", k_scale=0.037, v_scale=0.045)
+PROP_MLA128_FP8 = dict(PROP_MLA128, **FP8_LATENT)
 
 
 def _permuted(t, inp, seed):
