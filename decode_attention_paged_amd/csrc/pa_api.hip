@@ -17,6 +17,7 @@ constexpr long kFusedMergeBytes = 4 * 1024;   // largest per-unit partial set me
 constexpr double kSplitBytesValu = 128.0 * 1024.0;   // KV bytes per workgroup, VALU kernel
 constexpr double kSplitBytesMfma = 1024.0 * 1024.0;  // KV bytes per workgroup, MFMA kernel
 constexpr int kMinSplitsLong = 8;                    // splits of the longest sequence (MFMA kernel, full grid)
+constexpr double kShortUnitBytes = 4.0 * 1024 * 1024;  // longest unit (KV bytes) that is only halved
 constexpr int kSchedSplitsLong = 10;                 // the same when the units run longest first
 constexpr int kSchedSplitsMany = 3;                  // ... and the batch alone fills every slot twice
 constexpr double kManyUnitBytes = 512.0 * 1024.0;    // smallest split of such a batch (KV bytes)
@@ -176,10 +177,20 @@ int heuristic_splits(const pa_shape& s, int cus, bool mla) {
     int c = (int)(target_bytes / page_bytes);
     // A batch with a unit per CU or more runs its workgroups in rounds; the
     // units differ in length, and workgroups as long as a whole short-batch
-    // sequence leave a tail: the longest sequence gets at least kMinSplitsLong
-    // splits (Llama-style MHA with 4 query rows on the MFMA kernel: 8 splits,
-    // 110 us against 116 at 2).
-    if (k == Kernel::GqaMfma && units >= cus) {
+    // sequence leave a tail: the longest sequence of a batch with long units
+    // gets at least kMinSplitsLong splits.
+    const double long_unit_bytes = (double)P * page_bytes;   // the longest sequence's unit
+    if (k == Kernel::GqaMfma && units >= cus && units < 4L * cus &&
+        long_unit_bytes <= kShortUnitBytes) {
+      // The units alone fill the grid and none is long: every further split
+      // adds a workgroup's fixed cost and partials, so the longest sequence
+      // is only halved, against the tail of a ragged batch.  Measured (bf16,
+      // D128, bs16, decode call): 32 sequences x 8 KV heads at 8192 tokens,
+      // 175 us at 2 splits against 190 at 8 (163 unsplit); 64 x 8 of
+      // 1024-4096 tokens, 129 against 133 (141 unsplit); 128 x 4 of 512-2048,
+      // 73 against 80; Llama-style MHA with 4 rows, 116 against 122.
+      c = (P + 1) / 2;
+    } else if (k == Kernel::GqaMfma && units >= cus) {
       const int c_long = (P + kMinSplitsLong - 1) / kMinSplitsLong;
       if (c > c_long) c = c_long;
       // Several sequences with large units run longest first (uses_schedule),

@@ -433,7 +433,8 @@ def test_split_plan_for_batches_run_longest_first(lib):
     """With the units run longest first, the longest sequence gets 10 splits,
     or 3 when the batch's (sequence, KV head) units fill every workgroup slot
     (two per CU) twice over, and then no split reads less than 512 KiB (a
-    short longest sequence is not split at all)."""
+    short longest sequence is not split at all).  Units that fill the CUs but
+    hold at most 4 MiB each are only halved."""
     def S(**kw):
         base = dict(num_q_heads=64, num_kv_heads=8, max_context_len=32768,
                     max_blocks_per_seq=2048, num_blocks=65536)
@@ -453,6 +454,11 @@ def test_split_plan_for_batches_run_longest_first(lib):
     mha = dict(num_q_heads=32, num_kv_heads=32, max_context_len=4096, max_blocks_per_seq=256)
     assert S(batch=64, **mha)[0] == 4
     assert S(batch=16, **mha)[0] == 16
-    # fewer units than twice the slots: the 10-split rule (Llama-style 4-row MHA keeps 8)
+    # units that fill the CUs but are short (the longest at most 4 MiB of KV): halved only
     assert S(batch=16, num_q_heads=32, num_kv_heads=32, q_len=4, max_context_len=4096,
-             max_blocks_per_seq=256)[0] == 8
+             max_blocks_per_seq=256)[0] == 2               # Llama-style 4-row MHA, 2 MiB
+    assert S(batch=32, max_context_len=8192, max_blocks_per_seq=512)[0] == 2    # 256 units, 4 MiB
+    assert S(batch=128, num_q_heads=16, num_kv_heads=4, max_context_len=2048,
+             max_blocks_per_seq=128)[0] == 2              # 512 units, 1 MiB
+    # the same units past 4 MiB keep the long-unit plan (1 MiB splits: 8 here)
+    assert S(batch=32, max_context_len=16384, max_blocks_per_seq=1024)[0] == 8
