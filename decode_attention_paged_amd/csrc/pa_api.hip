@@ -161,7 +161,10 @@ int heuristic_splits(const pa_shape& s, int cus, bool mla) {
     } else {
       units = (long)s.batch * s.num_q_heads;
       heads_per_wg = 1;
-      target_bytes = kSplitBytesValu;
+      // heads wider than 128 dims: the same tokens per split (their kernel
+      // holds half the workgroups per CU; 256-dim heads, 16 x 16 of 1-4K
+      // tokens: 107.6 us at 16 splits against 109.8 at 32)
+      target_bytes = kSplitBytesValu * std::max(1.0, (s.head_dim + s.head_dim_v) / 256.0);
     }
     // FP8 caches hold half the bytes per token.  With at least one unit per
     // CU, splits keep the bf16 token count (the ragged batch: 186 against
